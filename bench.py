@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Throughput of the NVFP4 weight-only Gemma-4-26B-A4B MoE expert block on one
+MI355X.
+
+A step is one pass of the whole hot path -- moe_route, moe_bucket, the expert
+MLP (prep, gate/up, down) and moe_combine -- over one batch of seeded synthetic
+tokens, with inputs and weights already resident in HBM.  The default workload
+is one model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts,
+top-8, expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
+
+Timing: W warm-up steps, then K steps captured in one HIP graph and replayed
+once, bracketed by synchronisations (ms_per_step is wall clock / K).  Every
+stage call in the graph is bracketed by timing events recorded as graph nodes
+on the same stream, which gives the per-kernel durations used for the roofline
+of the dominant kernel (the gate/up GEMV/GEMM).  Consecutive steps read
+different, byte-identical copies of the expert weights so that each step
+streams its experts from HBM instead of the 256 MB last-level cache.
+
+Prints one JSON line (rank 0).
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
+STAGES = ("route", "bucket", "prep", "gate_up", "down", "combine")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
+                    help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
+                         "3: 30-layer decode sweep")
+    ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3 (1 or 8)")
+    ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    return ap.parse_args()
+
+
+class HipRuntime:
+    """The few HIP runtime calls torch does not expose on ROCm: timing events
+    recorded as external nodes of a captured graph, capture and launch of that
+    graph.  Uses the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        path = next((l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l),
+                    "libamdhip64.so")
+        h = ctypes.CDLL(path)
+        vp, P = ctypes.c_void_p, ctypes.POINTER
+        for name, args in {"hipEventCreate": [P(vp)], "hipEventRecordWithFlags": [vp, vp, ctypes.c_uint],
+                           "hipEventRecord": [vp, vp],
+                           "hipEventElapsedTime": [P(ctypes.c_float), vp, vp],
+                           "hipStreamBeginCapture": [vp, ctypes.c_int],
+                           "hipStreamEndCapture": [vp, P(vp)],
+                           "hipGraphInstantiate": [P(vp), vp, vp, ctypes.c_char_p, ctypes.c_size_t],
+                           "hipGraphLaunch": [vp, vp], "hipGetErrorString": [ctypes.c_int],
+                           "hipGraphCreate": [P(vp), ctypes.c_uint],
+                           "hipGraphAddEventRecordNode": [P(vp), vp, P(vp), ctypes.c_size_t, vp],
+                           "hipGraphAddChildGraphNode": [P(vp), vp, P(vp), ctypes.c_size_t, vp]}.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "hipGetErrorString" else ctypes.c_int
+        self.h = h
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {self.h.hipGetErrorString(rc).decode()}")
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        self._ok(self.h.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
+        return ev
+
+    def record(self, ev, stream, external):
+        if external:
+            self._ok(self.h.hipEventRecordWithFlags(ev, stream, 1), "hipEventRecordWithFlags")
+        else:
+            self._ok(self.h.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        self._ok(self.h.hipEventElapsedTime(ctypes.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def capture_graph(self, stream, fn):
+        """Stream-capture whatever fn() queues on `stream` into a graph."""
+        self._ok(self.h.hipStreamBeginCapture(stream, 2), "hipStreamBeginCapture")  # relaxed
+        graph = ctypes.c_void_p()
+        try:
+            fn()
+        finally:
+            rc = self.h.hipStreamEndCapture(stream, ctypes.byref(graph))
+        self._ok(rc, "hipStreamEndCapture")
+        return graph
+
+    def timed_chain(self, stream, calls, events):
+        """One graph: event[0], calls[0], event[1], calls[1], ... event[n] as a
+        chain of event-record nodes and child-graph nodes (each call captured
+        into its own child graph)."""
+        g = ctypes.c_void_p()
+        self._ok(self.h.hipGraphCreate(ctypes.byref(g), 0), "hipGraphCreate")
+        prev = None
+
+        def add_event(ev):
+            node = ctypes.c_void_p()
+            deps = (ctypes.c_void_p * 1)(prev) if prev is not None else None
+            self._ok(self.h.hipGraphAddEventRecordNode(ctypes.byref(node), g, deps,
+                                                       0 if prev is None else 1, ev),
+                     "hipGraphAddEventRecordNode")
+            return node
+
+        prev = add_event(events[0])
+        for call, ev in zip(calls, events[1:]):
+            child = self.capture_graph(stream, call)
+            node = ctypes.c_void_p()
+            deps = (ctypes.c_void_p * 1)(prev)
+            self._ok(self.h.hipGraphAddChildGraphNode(ctypes.byref(node), g, deps, 1, child),
+                     "hipGraphAddChildGraphNode")
+            prev = node
+            prev = add_event(ev)
+        exe = ctypes.c_void_p()
+        self._ok(self.h.hipGraphInstantiate(ctypes.byref(exe), g, None, None, 0),
+                 "hipGraphInstantiate")
+        return exe
+
+    def launch(self, exe, stream):
+        self._ok(self.h.hipGraphLaunch(exe, stream), "hipGraphLaunch")
+
+
+def expert_bytes_per_expert(H, I):
+    # packed nibbles + E4M3 scales + FP32 global, gate + up + down
+    return 3 * (H * I // 2 + H * I // 16 + 4)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
+              "multi-GPU path is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_synth as S
+    import nvfp4_weight_only_moe_amd as moe
+    from nvfp4_weight_only_moe_amd import workload as Wl
+
+    torch.cuda.set_device(0)
+    moe.lib()
+    wl = S.WORKLOADS[args.workload]
+    H, I, E, K = S.H, S.I, S.E, S.TOP_K
+    t_setup = time.perf_counter()
+
+    if args.workload == 3:
+        T = args.sweep_T
+        layers = [Wl.build_layer(l, zipf=False) for l in range(S.LAYERS)]
+        step_layers = [layers]                       # one step = the 30-layer sweep
+        replicas = 1                                 # 12.85 GB of distinct weights per sweep
+    else:
+        T = wl["T"][0]
+        base = Wl.build_layer(0, zipf=wl["zipf"])
+        touched = expert_bytes_per_expert(H, I) * min(E, T * K)
+        replicas = args.replicas or max(2, min(16, math.ceil(1.5 * 2 ** 30 / touched) + 1))
+        reps = Wl.replicate_experts(base, replicas)
+        step_layers = [[r] for r in reps]
+    x = Wl.to_device_bf16(S.activations(args.workload, T, outliers=wl["outliers"]))
+    buf = moe.MoeBuffers(T, H, I, E, K)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    def one_step(s, marks=None):
+        for layer in step_layers[s % len(step_layers)]:
+            moe.forward(layer, x, buf, marks=marks)
+
+    for s in range(args.warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+
+    # K steps, a timing event around every stage call.  With a graph the
+    # events are external event-record nodes of the graph itself.
+    n_layers = len(step_layers[0])
+    hip = HipRuntime()
+    stream = torch.cuda.Stream()
+    hs = ctypes.c_void_p(stream.cuda_stream)
+
+    def stage_calls(layer):
+        """The six stage calls of one block pass, each a closure on `stream`."""
+        from nvfp4_weight_only_moe_amd import _lib as C
+        return [
+            lambda: C.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w,
+                                buf.topk_w_raw, buf.logits, stream),
+            lambda: C.moe_bucket(buf.topk_idx, E, buf.expert_offsets, buf.sorted_pairs,
+                                 buf.pair_rank, buf.bucket_ws, stream),
+            lambda: C.nvfp4_expert_prep(x, buf.expert_offsets, E, I, K, buf.ws, stream),
+            lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
+                                           buf.sorted_pairs, T, K, H, buf.ws, stream),
+            lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K, buf.y_sorted,
+                                        buf.ws, stream),
+            lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream),
+        ]
+
+    calls = []
+    for s in range(args.steps):
+        for layer in step_layers[(args.warmup + s) % len(step_layers)]:
+            calls += stage_calls(layer)
+    bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
+
+    def run_eager():
+        hip.record(bounds[0], hs, False)
+        for call, e in zip(calls, bounds[1:]):
+            call()
+            hip.record(e, hs, False)
+
+    mode, graph_exec = "eager", None
+    torch.cuda.synchronize()
+    if not args.eager:
+        try:
+            graph_exec = hip.timed_chain(hs, calls, bounds)
+            mode = "hip_graph_with_event_nodes"
+        except Exception as exc:  # no event nodes: time eager launches
+            print(f"graph build failed ({exc}); timing eager launches", file=sys.stderr)
+            graph_exec = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph_exec is not None:
+        hip.launch(graph_exec, hs)
+    else:
+        run_eager()
+    stream.synchronize()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    stage_ms = {n: [] for n in STAGES}
+    gpu_step_ms = []
+    per_step = n_layers * len(STAGES)
+    for s in range(args.steps):
+        b = bounds[s * per_step:(s + 1) * per_step + 1]
+        for j in range(per_step):
+            stage_ms[STAGES[j % len(STAGES)]].append(hip.elapsed(b[j], b[j + 1]))
+        gpu_step_ms.append(hip.elapsed(b[0], b[-1]))
+    stage_avg_us = {n: 1e3 * float(np.mean(v)) for n, v in stage_ms.items()}
+
+    # work done per step (realised routing)
+    counts = np.diff(buf.expert_offsets.cpu().numpy())
+    U = int((counts > 0).sum())                  # active experts of the last layer run
+    P = T * K
+    if args.workload == 3:
+        U_layers = []
+        for layer in step_layers[0]:
+            moe.forward(layer, x, buf)
+            torch.cuda.synchronize()
+            U_layers.append(int((np.diff(buf.expert_offsets.cpu().numpy()) > 0).sum()))
+        U_total = sum(U_layers)
+    else:
+        U_layers, U_total = [U], U
+    per_exp = expert_bytes_per_expert(H, I)
+    gu_w_bytes = 2 * (H * I // 2 + H * I // 16 + 4)
+    step_s = ms_per_step / 1e3
+    gate_up_alg_bytes = gu_w_bytes * U + T * H * 2 + P * I * 2     # per launch (last layer)
+    gu_us = stage_avg_us["gate_up"]
+    achieved_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9
+    expert_flops = 2.0 * P * 3 * I * H * n_layers
+    out = {
+        "metric": "MoE layer tokens/s; decode NVFP4 weight GB/s; prefill TFLOP/s (1 MI355X)",
+        "value": T / step_s if args.workload != 3 else T / step_s,
+        "unit": "tokens/s" if args.workload != 3 else "tokens/s (30-layer sweep)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights (e2m1 x e4m3 x fp32) x bf16 activations; f16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded; bf16 N(0,0.02) experts quantised to NVFP4 on the GPU)",
+        "config": {"workload": wl["name"], "tokens": T, "hidden": H, "experts": E, "top_k": K,
+                   "moe_intermediate": I, "layers": n_layers, "weight_replicas": replicas,
+                   "timing": mode},
+        "detail": {
+            "gpu_ms_per_step_events": float(np.mean(gpu_step_ms)),
+            "stage_avg_us": stage_avg_us,
+            "active_experts": U_total,
+            "expert_weight_GBps": per_exp * U_total / step_s / 1e9,
+            "layer_alg_GBps": (per_exp * U_total + n_layers * ((E * H + H + E) * 2 + 2 * T * H * 2)) / step_s / 1e9,
+            "expert_TFLOPs": expert_flops / step_s / 1e12,
+            "max_over_mean_bucket": float(counts.max() / max(counts.mean(), 1e-9)),
+            "setup_s": t_setup,
+        },
+        "roofline": {
+            "kernel": "k_gateup (nvfp4_expert_gate_up)",
+            "bound": "hbm",
+            "achieved": achieved_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "alg_bytes_per_launch": gate_up_alg_bytes,
+            "avg_launch_us": gu_us,
+        },
+    }
+    if args.workload in (2, 4):
+        # prefill: the expert GEMMs are MFMA-bound; report both rooflines
+        gu_flops = 2.0 * P * 2 * I * H
+        out["roofline_mfma"] = {"bound": "mfma", "achieved": gu_flops / (gu_us * 1e-6) / 1e12,
+                                "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": gu_flops / (gu_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS}
+    if not args.no_cpu_baseline and args.workload != 3:
+        out["cpu_baseline"] = cpu_baseline(args, wl, T)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, wl, T):
+    """The fp64 oracle as it stands, single-threaded, on a bounded sample of
+    the same workload: the block for the first n tokens (expert weights
+    quantised by the oracle itself beforehand, untimed)."""
+    from threadpoolctl import threadpool_limits
+    import moe_synth as S
+    from oracle import formats as F
+    from oracle import moe as M
+    from oracle.quantize import quantize
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = min(T, args.cpu_sample_tokens)
+    p = S.router_params(0, zipf=wl["zipf"])
+    r = dict(w_router=F.bf16_bits_to_f64(p["w_router"]), scale=F.bf16_bits_to_f64(p["scale"]),
+             per_expert_scale=F.bf16_bits_to_f64(p["per_expert_scale"]), bias=p["bias"])
+    x = F.bf16_bits_to_f64(S.activations(args.workload, T, outliers=wl["outliers"]))[:n]
+    ids = M.route(x, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])["idx"]
+    todo = [(proj, int(e)) for e in np.unique(ids) for proj in (S.GATE, S.UP, S.DOWN)]
+
+    def q(item):
+        proj, e = item
+        return item, quantize(F.bf16_bits_to_f64(S.expert_weight(0, proj, e)))
+
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        packed = dict(ex.map(q, todo))                    # weight preparation, untimed
+    fn = {proj: (lambda e, proj=proj: F.dequantize(*packed[(proj, e)])) for proj in (S.GATE, S.UP, S.DOWN)}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        M.moe_block(x, x, r, fn[S.GATE], fn[S.UP], fn[S.DOWN], k=8)
+        dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of the {T} tokens of {wl['name']} through the fp64 oracle block "
+                      f"(route, bucket, NVFP4 decode of the {len(todo) // 3} touched experts, "
+                      f"expert MLPs, combine); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

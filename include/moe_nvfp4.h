@@ -1,0 +1,233 @@
+/*
+ * moe_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 weight-only MoE expert block.
+ *
+ * The block is the sparse branch of a Gemma-4-26B-A4B decoder layer
+ * ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture: block pseudocode and the
+ * router description): route the raw residual to 8 of 128 experts, run each
+ * routed token through its expert's GELU-tanh gated MLP (gate and up
+ * 2816 -> 704, down 704 -> 2816), and sum the expert outputs with the routing
+ * weights.  Expert weights are NVFP4: E2M1 elements in groups of 16 along the
+ * input dimension, one E4M3 scale per group, one FP32 scale per tensor
+ * ("Gemma-4-26B-A4B-NVFP4-mlx", Quantization recipe; "gemma-4-26B-A4B -
+ * NVFP4A16", Quantization details); activations are bf16 (W4A16).
+ *
+ * The hot path is four calls, in this order, on one stream:
+ *     moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine
+ *
+ * Conventions for every entry point
+ *   - Every pointer is a device pointer owned by the caller (for example
+ *     torch.Tensor.data_ptr()).  The library never allocates or frees device
+ *     memory and keeps no state between calls; calls are reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is queued
+ *     asynchronously in stream order; no call synchronises the host, copies
+ *     memory or calls hipMemset, so the sequence can be captured in a graph.
+ *   - bf16 and f16 values are passed as their uint16_t bit patterns.
+ *   - Host-detectable errors return a negative status and queue no work; no
+ *     call prints, aborts or exits.  NaN/Inf inputs propagate; they are not
+ *     validated.
+ *   - Integer outputs that the hot path produces are deterministic: the same
+ *     inputs give the same bytes on every run (no float atomics anywhere).
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL                */
+#define MOE_ERR_SHAPE (-2)       /* a size is out of range or inconsistent    */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than required   */
+#define MOE_ERR_UNSUPPORTED (-4) /* valid shape this build does not handle    */
+#define MOE_ERR_LAUNCH (-5)      /* a kernel launch failed (hipGetLastError)  */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 256 /* E                                   */
+#define MOE_MAX_TOPK 16     /* top_k                               */
+
+/*
+ * One stack of NVFP4 weights, one tensor per expert, canonical layout:
+ *   packed [E][N][K/2]  uint8: element k of row n is nibble (k & 1) of byte
+ *                       k/2 (low nibble = even k); nibble = E2M1 code,
+ *                       bit 3 sign, bits 0..2 index {0,.5,1,1.5,2,3,4,6}.
+ *   scales [E][N][K/16] uint8: OCP E4M3 (fn) code of the block scale of
+ *                       elements 16b..16b+15 of row n.
+ *   global [E]          float: per-tensor FP32 scale of expert e.
+ * Element value: E2M1(code) * E4M3(scale) * global[e].
+ * N is the output dimension, K the input ("inner") dimension, K % 32 == 0.
+ * Block scales must be finite and non-negative (the quantiser writes no others).
+ */
+typedef struct {
+  const uint8_t *packed;
+  const uint8_t *scales;
+  const float *global;
+  int32_t E, N, K;
+} nvfp4_tensor;
+
+/*
+ * moe_route -- the router ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture,
+ * router description): RMSNorm of the raw residual without a learned weight,
+ * times the learned per-channel `router_scale` and H^-0.5, linear to E
+ * logits, softmax over all E in fp32, top-k, renormalise the k probabilities
+ * to sum 1, multiply by per_expert_scale at the chosen ids.
+ *
+ *   x                [T][H] bf16   raw residual
+ *   w_router         [E][H] bf16   router projection
+ *   router_scale     [H]    bf16
+ *   per_expert_scale [E]    bf16
+ *   logit_bias       [E]    float  or NULL; added to the logits (a device to
+ *                                  skew expert popularity; zero on the pages)
+ *   eps                            RMSNorm epsilon (1e-6), inside the sqrt
+ *   topk_idx  out [T][top_k] int32 chosen expert ids, order unspecified;
+ *                                  ties on the logit go to the lower id
+ *   topk_w    out [T][top_k] float routing weights (renormalised x pes)
+ *   topk_w_raw out [T][top_k] float or NULL: renormalised weights before pes
+ *   logits    out [T][E] float     required: the logits (also the scratch
+ *                                  between the projection and the selection)
+ * Arithmetic: the logits accumulate in fp32 with no rounding of the
+ * normalised activation (the per-token 1/rms factor is applied to the dot
+ * product); softmax and renormalisation in fp32.
+ * Errors: MOE_ERR_NULL for a required NULL; MOE_ERR_SHAPE for T < 0, H <= 0,
+ * H % 32, E <= 0, top_k <= 0 or top_k > E; MOE_ERR_UNSUPPORTED for
+ * E > MOE_MAX_EXPERTS, E % 16 or top_k > MOE_MAX_TOPK.  T == 0 is a no-op.
+ */
+int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+              const uint16_t *per_expert_scale, const float *logit_bias, int32_t T, int32_t H,
+              int32_t E, int32_t top_k, float eps, int32_t *topk_idx, float *topk_w,
+              float *topk_w_raw, float *logits, void *stream);
+
+/*
+ * moe_bucket -- sort the T*top_k (token, slot) pairs by expert, the
+ * sort-by-expert step of a grouped GEMM ("Gemma 4 26B-A4B (MoE) - Core AI",
+ * Decode only: the batched sort-by-expert kernel for more than one token).
+ * Pair id p = t*top_k + j.  Order is (expert, t, j): a stable counting sort.
+ *
+ *   topk_idx        [T][top_k] int32  expert ids in [0, E)
+ *   expert_offsets  out [E+1] int32   bucket e is sorted_pairs[off[e] .. off[e+1])
+ *   sorted_pairs    out [T*top_k] int32 pair ids in sorted order
+ *   pair_rank       out [T*top_k] int32 position of pair p in sorted_pairs
+ *   workspace       >= moe_bucket_workspace_bytes(T, top_k, E) bytes; its
+ *                   first int32 is the device error word: the number of pairs
+ *                   whose id was outside [0, E).  Such pairs are placed after
+ *                   every bucket (positions >= off[E]) and go to no expert.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k <= 0, E <= 0),
+ * MOE_ERR_UNSUPPORTED (E > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOPK),
+ * MOE_ERR_WORKSPACE.
+ */
+int moe_bucket(const int32_t *topk_idx, int32_t T, int32_t top_k, int32_t E,
+               int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+               void *workspace, size_t ws_bytes, void *stream);
+size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
+
+/*
+ * nvfp4_expert_mlp -- every routed (token, expert) pair through its expert:
+ * A = gelu_tanh(X Wg^T) * (X Wu^T), Y = A Wd^T ("Gemma 4 26B-A4B (MoE) -
+ * Core AI", Architecture: GELU-gated experts in the tanh form; gate/up
+ * 2816 -> 704, down 704 -> 2816), with two-level NVFP4 weights
+ * (E2M1 x E4M3 block scale x FP32 tensor scale).
+ *
+ *   x_expert       [T][H] bf16   expert input (the pre-normed residual; may
+ *                                alias the router's x)
+ *   gate, up       nvfp4_tensor  N = I, K = H
+ *   down           nvfp4_tensor  N = H, K = I
+ *   expert_offsets [E+1], sorted_pairs [T*top_k]  from moe_bucket
+ *   y_sorted       out [T*top_k][H] bf16  expert output of the pair at each
+ *                                sorted position (routing weight not applied)
+ *   workspace      >= moe_workspace_bytes(T, top_k, E, H, I) bytes
+ * Arithmetic: E2M1 x E4M3 products are exact in f16; activations enter the
+ * MFMA as f16 after an exact per-row power-of-two rescale (so no bf16 value
+ * overflows; values more than 2^29 below the row's largest lose low bits);
+ * fp32 accumulation; the FP32 tensor scale and the power of two are applied
+ * to the fp32 sums; A is rounded to bf16 between the projections, Y to bf16.
+ * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, top_k <= 0, H or I <= 0,
+ * descriptor shapes not [E][I][H], [E][I][H], [E][H][I] with one E);
+ * MOE_ERR_UNSUPPORTED (H % 64, I % 64, E > MOE_MAX_EXPERTS,
+ * top_k > MOE_MAX_TOPK); MOE_ERR_WORKSPACE.
+ */
+int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate, const nvfp4_tensor *up,
+                     const nvfp4_tensor *down, const int32_t *expert_offsets,
+                     const int32_t *sorted_pairs, int32_t T, int32_t top_k, int32_t H, int32_t I,
+                     uint16_t *y_sorted, void *workspace, size_t ws_bytes, void *stream);
+size_t moe_workspace_bytes(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I);
+
+/*
+ * The three stages of nvfp4_expert_mlp as separate calls, for callers that
+ * want to time or interleave them; queued in this order on one stream with the
+ * same workspace they give the same bytes as nvfp4_expert_mlp.
+ *   nvfp4_expert_prep:    per-row power-of-two rescale of x_expert to f16, the
+ *                         (expert, row-block) tile list, clears the per-row
+ *                         max of A.  Reads expert_offsets.
+ *   nvfp4_expert_gate_up: A = gelu_tanh(X Wg^T) * (X Wu^T) for every sorted
+ *                         row, bf16, kept in the workspace.
+ *   nvfp4_expert_down:    y_sorted = A Wd^T.
+ * Arguments, layouts and errors as for nvfp4_expert_mlp.
+ */
+int nvfp4_expert_prep(const uint16_t *x_expert, const int32_t *expert_offsets, int32_t T,
+                      int32_t top_k, int32_t E, int32_t H, int32_t I, void *workspace,
+                      size_t ws_bytes, void *stream);
+int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor *up,
+                         const int32_t *expert_offsets, const int32_t *sorted_pairs, int32_t T,
+                         int32_t top_k, int32_t H, int32_t I, void *workspace, size_t ws_bytes,
+                         void *stream);
+int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets, int32_t T,
+                      int32_t top_k, int32_t H, int32_t I, uint16_t *y_sorted, void *workspace,
+                      size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- the weighted sum over a token's routed experts
+ * ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture: sum over k of w_k h2_k):
+ *   out[t] = sum_{j=0..top_k-1} topk_w[t][j] * y_sorted[pair_rank[t*top_k+j]]
+ * summed in the fixed order j = 0, 1, ... in fp32, rounded once to bf16.
+ *   y_sorted [T*top_k][H] bf16, topk_w [T][top_k] float, pair_rank [T*top_k]
+ *   out      out [T][H] bf16
+ * A pair whose rank is outside [0, T*top_k) contributes nothing.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k <= 0, H <= 0, H % 8).
+ */
+int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pair_rank, int32_t T,
+                int32_t top_k, int32_t H, uint16_t *out, void *stream);
+
+/*
+ * nvfp4_quantize -- weight preparation: the block quantiser of the
+ * "Gemma-4-26B-A4B-it-NVFP4" README (S_block = max|w|/6 over 16 contiguous
+ * inputs, q = clip(round(w / S_block), -6, 6)) in its two-level form.
+ * Per expert tensor W [N][K] (bf16):
+ *   g = fl32(max|W| / 2688)   (2688 = 6 * 448: largest E2M1 x largest E4M3)
+ *   block scale code = nearest E4M3 (ties to even, saturate at 448) of
+ *                      amax_block / (6 g), evaluated in IEEE double
+ *   element code     = nearest E2M1 (ties to even) of
+ *                      clip(w / (E4M3(code) * g), -6, 6) in double; a block
+ *                      scale of 0 gives code 0; a zero magnitude gives code 0.
+ *   w       [E][N][K] bf16 in;  K % 32 == 0
+ *   out     packed, scales, global as in nvfp4_tensor (non-const pointers)
+ * The result is bit-identical run to run.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E, N <= 0, K <= 0, K % 32).
+ */
+int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *packed,
+                   uint8_t *scales, float *global, void *stream);
+
+/*
+ * nvfp4_dequant_bf16 -- decode expert e of a stack to bf16 without the FP32
+ * tensor scale: out[n][k] = E2M1(code[n][k]) * E4M3(scale[n][k/16]), which
+ * is exact in bf16 ("Gemma-4-26B-A4B-NVFP4-mlx", Notes: E2M1 x per-16 E4M3
+ * block scale x per-tensor F32).  A check of the unpacking used by the
+ * expert kernels.
+ *   out [N][K] bf16
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (e outside [0, E), N or K <= 0, K % 32).
+ */
+int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream);
+
+/* Text of a status code (static storage). */
+const char *moe_status_str(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

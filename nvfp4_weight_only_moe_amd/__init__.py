@@ -1,0 +1,17 @@
+"""NVFP4 weight-only Gemma-4-26B-A4B MoE expert block for MI355X (gfx950).
+
+The product is the HIP library ``libmoe_nvfp4.so`` behind the C ABI in
+``include/moe_nvfp4.h``; this package is its thin Python binding (``_lib``),
+the four-call block sequence (``block``) and device-resident synthetic
+workloads (``workload``).
+"""
+from ._lib import (EXPORTED, MoeError, Nvfp4Weights, lib, moe_bucket, moe_bucket_workspace_bytes,
+                   moe_combine, moe_route, moe_workspace_bytes, nvfp4_dequant_bf16,
+                   nvfp4_expert_down, nvfp4_expert_gate_up, nvfp4_expert_mlp, nvfp4_expert_prep,
+                   nvfp4_quantize)
+from .block import MoeBuffers, MoeLayer, forward
+
+__all__ = ["EXPORTED", "MoeError", "Nvfp4Weights", "lib", "moe_bucket", "moe_bucket_workspace_bytes",
+           "moe_combine", "moe_route", "moe_workspace_bytes", "nvfp4_dequant_bf16",
+           "nvfp4_expert_mlp", "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
+           "nvfp4_quantize", "MoeBuffers", "MoeLayer", "forward"]

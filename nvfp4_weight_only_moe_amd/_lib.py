@@ -1,0 +1,233 @@
+"""ctypes binding of libmoe_nvfp4.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks their
+dtype, shape and contiguity, and passes raw pointers and the current HIP stream
+to the C entry point of the same name.  All computation happens in the HIP
+kernels; there is no fallback of any kind -- if the library is missing or a
+call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB as LIB_PATH
+
+MOE_OK = 0
+_ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
+           -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_LAUNCH"}
+
+EXPORTED = ("moe_route", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
+            "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
+            "moe_workspace_bytes", "moe_combine", "nvfp4_quantize", "nvfp4_dequant_bf16",
+            "moe_status_str", "moe_abi_version")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {status} ({_ERRORS.get(status, '?')}: "
+                         f"{lib().moe_status_str(status).decode()})")
+
+
+class Nvfp4TensorC(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib(path=None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it first (python __graft_entry__.py build "
+                           "or nvfp4_weight_only_moe_amd._build.build())")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    P = ctypes.POINTER(Nvfp4TensorC)
+    sig = {
+        "moe_route": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
+        "moe_bucket": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "moe_bucket_workspace_bytes": (sz, [i32, i32, i32]),
+        "nvfp4_expert_mlp": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
+        "nvfp4_expert_prep": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]),
+        "nvfp4_expert_gate_up": (ctypes.c_int, [P, P, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
+        "nvfp4_expert_down": (ctypes.c_int, [P, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
+        "moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "moe_combine": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "nvfp4_quantize": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp]),
+        "nvfp4_dequant_bf16": (ctypes.c_int, [P, i32, vp, vp]),
+        "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_abi_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+_B16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+class Nvfp4Weights:
+    """One NVFP4 stack: packed [E,N,K/2] u8, scales [E,N,K/16] u8, global [E] f32."""
+
+    def __init__(self, packed, scales, global_scale):
+        self.packed, self.scales, self.global_scale = packed, scales, global_scale
+        self.E, self.N, k2 = packed.shape
+        self.K = 2 * k2
+
+    @classmethod
+    def empty(cls, E, N, K, device="cuda"):
+        return cls(torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
+                   torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
+                   torch.empty((E,), dtype=torch.float32, device=device))
+
+    def c(self):
+        _ptr(self.packed, torch.uint8, (self.E, self.N, self.K // 2), "packed")
+        _ptr(self.scales, torch.uint8, (self.E, self.N, self.K // 16), "scales")
+        _ptr(self.global_scale, torch.float32, (self.E,), "global")
+        return Nvfp4TensorC(self.packed.data_ptr(), self.scales.data_ptr(),
+                            self.global_scale.data_ptr(), self.E, self.N, self.K)
+
+    def select(self, e0, e1):
+        """Experts e0..e1-1 (views, no copy)."""
+        return Nvfp4Weights(self.packed[e0:e1], self.scales[e0:e1], self.global_scale[e0:e1])
+
+
+def moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps,
+              topk_idx, topk_w, topk_w_raw, logits, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    st = lib().moe_route(_ptr(x, _B16, (T, H), "x"), _ptr(w_router, _B16, (E, H), "w_router"),
+                         _ptr(router_scale, _B16, (H,), "router_scale"),
+                         _ptr(per_expert_scale, _B16, (E,), "per_expert_scale"),
+                         _ptr(logit_bias, torch.float32, (E,), "logit_bias"), T, H, E, top_k,
+                         float(eps), _ptr(topk_idx, torch.int32, (T, top_k), "topk_idx"),
+                         _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
+                         _ptr(topk_w_raw, torch.float32, (T, top_k), "topk_w_raw"),
+                         _ptr(logits, torch.float32, (T, E), "logits"), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_bucket_workspace_bytes(T, top_k, E):
+    return int(lib().moe_bucket_workspace_bytes(T, top_k, E))
+
+
+def moe_bucket(topk_idx, E, expert_offsets, sorted_pairs, pair_rank, workspace, stream=None):
+    T, top_k = topk_idx.shape
+    st = lib().moe_bucket(_ptr(topk_idx, torch.int32, (T, top_k), "topk_idx"), T, top_k, E,
+                          _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+                          _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"),
+                          _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"),
+                          _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(stream))
+    _check("moe_bucket", st)
+
+
+def moe_workspace_bytes(T, top_k, E, H, I):
+    return int(lib().moe_workspace_bytes(T, top_k, E, H, I))
+
+
+def nvfp4_expert_mlp(x_expert, gate, up, down, expert_offsets, sorted_pairs, top_k, y_sorted,
+                     workspace, stream=None):
+    T, H = x_expert.shape
+    I = gate.N
+    cg, cu, cd = gate.c(), up.c(), down.c()
+    st = lib().nvfp4_expert_mlp(_ptr(x_expert, _B16, (T, H), "x_expert"), ctypes.byref(cg),
+                                ctypes.byref(cu), ctypes.byref(cd),
+                                _ptr(expert_offsets, torch.int32, (gate.E + 1,), "expert_offsets"),
+                                _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"), T,
+                                top_k, H, I, _ptr(y_sorted, _B16, (T * top_k, H), "y_sorted"),
+                                _ptr(workspace, None, None, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("nvfp4_expert_mlp", st)
+
+
+def nvfp4_expert_prep(x_expert, expert_offsets, E, I, top_k, workspace, stream=None):
+    T, H = x_expert.shape
+    st = lib().nvfp4_expert_prep(_ptr(x_expert, _B16, (T, H), "x_expert"),
+                                 _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"), T,
+                                 top_k, E, H, I, _ptr(workspace, None, None, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("nvfp4_expert_prep", st)
+
+
+def nvfp4_expert_gate_up(gate, up, expert_offsets, sorted_pairs, T, top_k, H, workspace,
+                         stream=None):
+    cg, cu = gate.c(), up.c()
+    st = lib().nvfp4_expert_gate_up(ctypes.byref(cg), ctypes.byref(cu),
+                                    _ptr(expert_offsets, torch.int32, (gate.E + 1,), "expert_offsets"),
+                                    _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"),
+                                    T, top_k, H, gate.N, _ptr(workspace, None, None, "workspace"),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("nvfp4_expert_gate_up", st)
+
+
+def nvfp4_expert_down(down, expert_offsets, T, top_k, y_sorted, workspace, stream=None):
+    cd = down.c()
+    st = lib().nvfp4_expert_down(ctypes.byref(cd),
+                                 _ptr(expert_offsets, torch.int32, (down.E + 1,), "expert_offsets"),
+                                 T, top_k, down.N, down.K,
+                                 _ptr(y_sorted, _B16, (T * top_k, down.N), "y_sorted"),
+                                 _ptr(workspace, None, None, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("nvfp4_expert_down", st)
+
+
+def moe_combine(y_sorted, topk_w, pair_rank, out, stream=None):
+    T, top_k = topk_w.shape
+    H = out.shape[1]
+    st = lib().moe_combine(_ptr(y_sorted, _B16, (T * top_k, H), "y_sorted"),
+                           _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
+                           _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"), T, top_k, H,
+                           _ptr(out, _B16, (T, H), "out"), _stream(stream))
+    _check("moe_combine", st)
+
+
+def nvfp4_quantize(w, out, stream=None):
+    """w [E, N, K] bf16 -> out (Nvfp4Weights of the same shape)."""
+    E, N, K = w.shape
+    st = lib().nvfp4_quantize(_ptr(w, _B16, (E, N, K), "w"), E, N, K,
+                              _ptr(out.packed, torch.uint8, (E, N, K // 2), "packed"),
+                              _ptr(out.scales, torch.uint8, (E, N, K // 16), "scales"),
+                              _ptr(out.global_scale, torch.float32, (E,), "global"), _stream(stream))
+    _check("nvfp4_quantize", st)
+
+
+def nvfp4_dequant_bf16(w, e, out, stream=None):
+    c = w.c()
+    st = lib().nvfp4_dequant_bf16(ctypes.byref(c), e, _ptr(out, _B16, (w.N, w.K), "out"),
+                                  _stream(stream))
+    _check("nvfp4_dequant_bf16", st)

@@ -1,0 +1,100 @@
+"""One MoE expert block as the sequence of the four C-ABI calls.
+
+``MoeLayer`` holds one layer's device weights, ``MoeBuffers`` the caller-owned
+outputs and workspaces for a token count, ``forward`` queues
+moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine on one stream.
+Nothing here computes: it only allocates device memory and passes pointers.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class MoeLayer:
+    w_router: torch.Tensor          # [E, H] bf16
+    router_scale: torch.Tensor      # [H] bf16
+    per_expert_scale: torch.Tensor  # [E] bf16
+    logit_bias: Optional[torch.Tensor]  # [E] f32 or None
+    gate: "_lib.Nvfp4Weights"       # [E, I, H]
+    up: "_lib.Nvfp4Weights"         # [E, I, H]
+    down: "_lib.Nvfp4Weights"       # [E, H, I]
+    top_k: int = 8
+    eps: float = 1e-6
+
+    @property
+    def E(self):
+        return self.w_router.shape[0]
+
+    @property
+    def H(self):
+        return self.w_router.shape[1]
+
+    @property
+    def I(self):
+        return self.gate.N
+
+    def with_experts(self, gate, up, down):
+        return MoeLayer(self.w_router, self.router_scale, self.per_expert_scale, self.logit_bias,
+                        gate, up, down, self.top_k, self.eps)
+
+
+class MoeBuffers:
+    """Every output and workspace of the four calls for T tokens."""
+
+    def __init__(self, T, H, I, E, top_k, device="cuda"):
+        kw = dict(device=device)
+        P = T * top_k
+        self.T, self.P = T, P
+        self.logits = torch.empty((T, E), dtype=torch.float32, **kw)
+        self.topk_idx = torch.empty((T, top_k), dtype=torch.int32, **kw)
+        self.topk_w = torch.empty((T, top_k), dtype=torch.float32, **kw)
+        self.topk_w_raw = torch.empty((T, top_k), dtype=torch.float32, **kw)
+        self.expert_offsets = torch.empty((E + 1,), dtype=torch.int32, **kw)
+        self.sorted_pairs = torch.empty((P,), dtype=torch.int32, **kw)
+        self.pair_rank = torch.empty((P,), dtype=torch.int32, **kw)
+        self.bucket_ws = torch.empty((_lib.moe_bucket_workspace_bytes(T, top_k, E),),
+                                     dtype=torch.uint8, **kw)
+        self.ws = torch.empty((_lib.moe_workspace_bytes(T, top_k, E, H, I),), dtype=torch.uint8, **kw)
+        self.y_sorted = torch.empty((P, H), dtype=torch.bfloat16, **kw)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, **kw)
+
+    def bucket_error_count(self):
+        """Pairs whose expert id was out of range in the last moe_bucket."""
+        return int(self.bucket_ws[:4].view(torch.int32)[0].item())
+
+
+def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, marks=None):
+    """Queue the whole block for x [T, H] bf16; the result lands in buf.out.
+
+    ``marks`` (optional) is a callable invoked with a stage name between the
+    calls ("route", "bucket", "prep", "gate_up", "down", "combine" after each);
+    with it the expert MLP runs as its three stage calls so that a caller can
+    record timing events around each stage."""
+    xe = x if x_expert is None else x_expert
+    mark = marks or (lambda name: None)
+    _lib.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale, layer.logit_bias,
+                   layer.top_k, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
+                   stream)
+    mark("route")
+    _lib.moe_bucket(buf.topk_idx, layer.E, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
+                    buf.bucket_ws, stream)
+    mark("bucket")
+    if marks is None:
+        _lib.nvfp4_expert_mlp(xe, layer.gate, layer.up, layer.down, buf.expert_offsets,
+                              buf.sorted_pairs, layer.top_k, buf.y_sorted, buf.ws, stream)
+    else:
+        _lib.nvfp4_expert_prep(xe, buf.expert_offsets, layer.E, layer.I, layer.top_k, buf.ws, stream)
+        mark("prep")
+        _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs,
+                                  buf.T, layer.top_k, layer.H, buf.ws, stream)
+        mark("gate_up")
+        _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,
+                               buf.ws, stream)
+        mark("down")
+    _lib.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream)
+    mark("combine")
+    return buf.out

@@ -1,0 +1,223 @@
+// moe_bucket: stable counting sort of the (token, slot) pairs by expert -- the
+// sort-by-expert step of a grouped GEMM ("Gemma 4 26B-A4B (MoE) - Core AI",
+// Decode only: batched sort-by-expert kernel for more than one token).
+//
+// Order is (expert, token, slot), i.e. by expert and then by pair id
+// p = t*top_k + j.  Pairs with an id outside [0, E) go to an extra bucket E
+// placed after all experts and are counted in the error word.
+//
+// Up to kChunk pairs: one workgroup does everything (LDS histogram, scan,
+// stable scatter).  Beyond that: (1) per-chunk LDS histograms, (2) one
+// workgroup turns them into expert offsets and per-chunk base positions,
+// (3) per-chunk stable scatter.  The in-chunk rank of a pair among pairs of the
+// same expert comes from a wave "multi-split": 9 ballots give each lane the
+// mask of lanes holding the same bucket; a popcount below the lane is its rank
+// in the wave, per-wave counts in LDS order the waves.  No atomics decide any
+// position, so the output is the same on every run.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBucketThreads = 256;
+constexpr int kBucketWaves = kBucketThreads / kWave;
+constexpr int kChunk = 4096;             // pairs per workgroup
+constexpr int kMaxB = MOE_MAX_EXPERTS + 1;  // buckets incl. the invalid one
+
+__device__ __forceinline__ int bucket_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
+
+// Stable scatter of the n bucket ids in s_b (pairs pbase .. pbase+n-1),
+// starting from the per-bucket positions in s_run (updated in place).
+__device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_run,
+                               int (*s_wcnt)[kMaxB], int32_t *sorted, int32_t *rank) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int base = 0; base < n; base += kBucketThreads) {
+    const int i = base + tid;
+    const bool valid = i < n;
+    const int b = valid ? s_b[i] : 0;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const bool on = (b >> bit) & 1;
+      const unsigned long long m = __ballot(on);
+      peers &= on ? m : ~m;
+    }
+    const int rank_w = __popcll(peers & lt);
+    if (valid && rank_w == 0) s_wcnt[wave][b] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = s_run[b];
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][b];
+      pos += rank_w;
+      const int p = pbase + i;
+      sorted[pos] = p;
+      rank[p] = pos;
+    }
+    __syncthreads();
+    for (int bb = tid; bb < nb; bb += kBucketThreads) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < kBucketWaves; ++w) {
+        s += s_wcnt[w][bb];
+        s_wcnt[w][bb] = 0;
+      }
+      s_run[bb] += s;
+    }
+    __syncthreads();
+  }
+}
+
+__device__ void zero_wcnt(int (*s_wcnt)[kMaxB], int nb) {
+  for (int i = threadIdx.x; i < kBucketWaves * nb; i += kBucketThreads) s_wcnt[i / nb][i % nb] = 0;
+}
+
+// Exclusive scan of cnt[0..nb) into out[0..nb) by the first wave (nb <= 257).
+__device__ void wave_exclusive_scan(const int *cnt, int *out, int nb) {
+  const int lane = threadIdx.x;
+  if (lane >= kWave) return;
+  int carry = 0;
+  for (int base = 0; base < nb; base += kWave) {
+    const int i = base + lane;
+    int v = i < nb ? cnt[i] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    if (i < nb) out[i] = carry + incl - v;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+}
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *__restrict__ idx,
+                                                                 int P, int E,
+                                                                 int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ sorted,
+                                                                 int32_t *__restrict__ rank,
+                                                                 int32_t *__restrict__ err) {
+  __shared__ int s_b[kChunk];
+  __shared__ int s_cnt[kMaxB], s_run[kMaxB];
+  __shared__ int s_wcnt[kBucketWaves][kMaxB];
+  const int tid = threadIdx.x, nb = E + 1;
+  for (int i = tid; i < nb; i += kBucketThreads) s_cnt[i] = 0;
+  zero_wcnt(s_wcnt, nb);
+  __syncthreads();
+  for (int p = tid; p < P; p += kBucketThreads) {
+    const int b = bucket_of(idx[p], E);
+    s_b[p] = b;
+    atomicAdd(&s_cnt[b], 1);
+  }
+  __syncthreads();
+  wave_exclusive_scan(s_cnt, s_run, nb);
+  __syncthreads();
+  for (int i = tid; i < nb; i += kBucketThreads) offsets[i] = s_run[i];
+  if (tid == 0) err[0] = s_cnt[E];
+  __syncthreads();
+  scatter_rounds(s_b, P, 0, nb, s_run, s_wcnt, sorted, rank);
+}
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket_hist(const int32_t *__restrict__ idx,
+                                                                int P, int E,
+                                                                int32_t *__restrict__ chunk_cnt) {
+  __shared__ int s_cnt[kMaxB];
+  const int tid = threadIdx.x, nb = E + 1, c = blockIdx.x;
+  for (int i = tid; i < nb; i += kBucketThreads) s_cnt[i] = 0;
+  __syncthreads();
+  const int p0 = c * kChunk, p1 = min(P, p0 + kChunk);
+  for (int p = p0 + tid; p < p1; p += kBucketThreads) atomicAdd(&s_cnt[bucket_of(idx[p], E)], 1);
+  __syncthreads();
+  for (int i = tid; i < nb; i += kBucketThreads) chunk_cnt[(size_t)c * nb + i] = s_cnt[i];
+}
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket_scan(const int32_t *__restrict__ chunk_cnt,
+                                                                int nchunks, int E,
+                                                                int32_t *__restrict__ chunk_base,
+                                                                int32_t *__restrict__ offsets,
+                                                                int32_t *__restrict__ err) {
+  __shared__ int s_tot[kMaxB], s_off[kMaxB];
+  const int tid = threadIdx.x, nb = E + 1;
+  for (int b = tid; b < nb; b += kBucketThreads) {
+    int s = 0;
+    for (int c = 0; c < nchunks; ++c) s += chunk_cnt[(size_t)c * nb + b];
+    s_tot[b] = s;
+  }
+  __syncthreads();
+  wave_exclusive_scan(s_tot, s_off, nb);
+  __syncthreads();
+  for (int b = tid; b < nb; b += kBucketThreads) {
+    offsets[b] = s_off[b];
+    int run = s_off[b];
+    for (int c = 0; c < nchunks; ++c) {
+      chunk_base[(size_t)c * nb + b] = run;
+      run += chunk_cnt[(size_t)c * nb + b];
+    }
+  }
+  if (tid == 0) err[0] = s_tot[E];
+}
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket_scatter(
+    const int32_t *__restrict__ idx, int P, int E, const int32_t *__restrict__ chunk_base,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ rank) {
+  __shared__ int s_b[kChunk];
+  __shared__ int s_run[kMaxB];
+  __shared__ int s_wcnt[kBucketWaves][kMaxB];
+  const int tid = threadIdx.x, nb = E + 1, c = blockIdx.x;
+  const int p0 = c * kChunk, n = min(P, p0 + kChunk) - p0;
+  for (int i = tid; i < nb; i += kBucketThreads) s_run[i] = chunk_base[(size_t)c * nb + i];
+  zero_wcnt(s_wcnt, nb);
+  for (int i = tid; i < n; i += kBucketThreads) s_b[i] = bucket_of(idx[p0 + i], E);
+  __syncthreads();
+  scatter_rounds(s_b, n, p0, nb, s_run, s_wcnt, sorted, rank);
+}
+
+size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_off) {
+  const size_t P = (size_t)T * top_k;
+  const size_t nchunks = (P + kChunk - 1) / kChunk;
+  const size_t nb = (size_t)E + 1;
+  *cnt_off = 256;
+  *base_off = *cnt_off + moe_align_up(nchunks * nb * 4, 256);
+  return *base_off + moe_align_up(nchunks * nb * 4, 256);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
+  if (T < 0 || top_k <= 0 || E <= 0) return 0;
+  size_t a, b;
+  return moe::bucket_ws_layout(T, top_k, E, &a, &b);
+}
+
+extern "C" int moe_bucket(const int32_t *topk_idx, int32_t T, int32_t top_k, int32_t E,
+                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+                          void *workspace, size_t ws_bytes, void *stream) {
+  using namespace moe;
+  if (!expert_offsets || !workspace || (T > 0 && (!topk_idx || !sorted_pairs || !pair_rank)))
+    return MOE_ERR_NULL;
+  if (T < 0 || top_k <= 0 || E <= 0) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
+  size_t cnt_off, base_off;
+  const size_t need = bucket_ws_layout(T, top_k, E, &cnt_off, &base_off);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int P = T * top_k;
+  int32_t *err = (int32_t *)workspace;
+  if (P <= kChunk) {
+    MOE_LAUNCH(k_bucket_small, dim3(1), dim3(kBucketThreads), 0, s, topk_idx, P, E,
+                       expert_offsets, sorted_pairs, pair_rank, err);
+    return MOE_OK;
+  }
+  const int nchunks = (P + kChunk - 1) / kChunk;
+  int32_t *chunk_cnt = (int32_t *)((char *)workspace + cnt_off);
+  int32_t *chunk_base = (int32_t *)((char *)workspace + base_off);
+  MOE_LAUNCH(k_bucket_hist, dim3(nchunks), dim3(kBucketThreads), 0, s, topk_idx, P, E,
+                     chunk_cnt);
+  MOE_LAUNCH(k_bucket_scan, dim3(1), dim3(kBucketThreads), 0, s, chunk_cnt, nchunks, E,
+                     chunk_base, expert_offsets, err);
+  MOE_LAUNCH(k_bucket_scatter, dim3(nchunks), dim3(kBucketThreads), 0, s, topk_idx, P, E,
+                     chunk_base, sorted_pairs, pair_rank);
+  return MOE_OK;
+}

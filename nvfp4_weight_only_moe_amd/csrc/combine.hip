@@ -1,0 +1,51 @@
+// moe_combine: weighted sum of a token's routed expert outputs
+// ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture: sum over k of w_k h2_k).
+// out[t] = sum_j w[t][j] * Y[rank(t, j)], fixed order j = 0, 1, ..., fp32
+// accumulation, one bf16 rounding.  One workgroup per token; each thread owns
+// 8 consecutive outputs (16-byte loads and stores).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
+                                                 const float *__restrict__ w,
+                                                 const int32_t *__restrict__ rank, int T, int K,
+                                                 int H, uint16_t *__restrict__ out) {
+  const int t = blockIdx.x;
+  const int P = T * K;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < K; ++j) {
+      const int r = rank[(size_t)t * K + j];
+      if (r < 0 || r >= P) continue;
+      const float wj = w[(size_t)t * K + j];
+      const u32x4 v = *(const u32x4 *)(y + (size_t)r * H + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wj, __uint_as_float(v[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+    *(u32x4 *)(out + (size_t)t * H + c) = o;
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pair_rank,
+                           int32_t T, int32_t top_k, int32_t H, uint16_t *out, void *stream) {
+  using namespace moe;
+  if (T > 0 && (!y_sorted || !topk_w || !pair_rank || !out)) return MOE_ERR_NULL;
+  if (T < 0 || top_k <= 0 || H <= 0 || H % 8) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  MOE_LAUNCH(k_combine, dim3(T), dim3(256), 0, (hipStream_t)stream, y_sorted, topk_w,
+                     pair_rank, T, top_k, H, out);
+  return MOE_OK;
+}

@@ -1,0 +1,185 @@
+// Weight preparation and checks: the NVFP4 block quantiser and the bf16
+// decode of one expert tensor, plus the status strings.
+//
+// Quantiser: "Gemma-4-26B-A4B-it-NVFP4" README, block-quantisation formulas:
+// S_block = max|w| / 6 over 16 contiguous inner-dimension elements,
+// q = clip(round(w / S_block), -6, 6), here in the two-level form (E4M3 block
+// scale x FP32 tensor scale, "Gemma-4-26B-A4B-NVFP4-mlx", Quantization recipe):
+//   g    = fl32(max|W| / (6 * 448))                  per expert tensor
+//   code = E4M3_rne_sat(amax_block / (6 g))          in IEEE double
+//   q    = E2M1_rne(clip(w / (E4M3(code) g), -6, 6)) in IEEE double
+// Three kernels: per-expert max|W| (integer atomicMax of float bits: exact and
+// order-independent), the per-block quantisation, and the write of g.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, int n, uint32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_absmax(const uint16_t *__restrict__ w, size_t per_e,
+                                                uint32_t *__restrict__ amax_bits) {
+  const int e = blockIdx.y;
+  const uint16_t *base = w + (size_t)e * per_e;
+  float m = 0.0f;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_e;
+       i += (size_t)gridDim.x * 256 * 8) {
+    const u32x4 v = *(const u32x4 *)(base + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m = fmaxf(m, fabsf(__uint_as_float(v[q] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(v[q] & 0xFFFF0000u)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(&amax_bits[e], __float_as_uint(m));
+}
+
+// nearest E4M3 code of r >= 0 (ties to even mantissa, saturate at 448)
+__device__ uint32_t e4m3_rne_sat(double r) {
+  if (!(r < 448.0)) return 0x7E;
+  if (r < 0.015625) {                        // below 2^-6: subnormal step 2^-9
+    return (uint32_t)rint(r * 512.0);          // 0..8; 8 is code 0x08 = 2^-6
+  }
+  int ex;
+  (void)frexp(r, &ex);                         // r = f 2^ex, f in [0.5, 1)
+  int E = ex - 1;                              // floor(log2 r), -6 .. 8
+  double q = rint(ldexp(r, 3 - E));            // 8 .. 16
+  if (q == 16.0) {
+    q = 8.0;
+    E += 1;
+  }
+  return (uint32_t)(((E + 7) << 3) | ((int)q - 8));
+}
+
+__device__ double e4m3_value(uint32_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+// nearest E2M1 magnitude code of a in [0, 6], ties to the even code
+__device__ uint32_t e2m1_rne(double a) {
+  return (uint32_t)(a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) +
+         (a > 5.0);
+}
+
+__global__ __launch_bounds__(256) void k_quant(const uint16_t *__restrict__ w, int N, int K,
+                                               const uint32_t *__restrict__ amax_bits,
+                                               uint8_t *__restrict__ packed,
+                                               uint8_t *__restrict__ scales) {
+  const int e = blockIdx.y;
+  const int nb = K / 16;
+  const size_t blk = (size_t)blockIdx.x * 256 + threadIdx.x;  // block index within expert
+  if (blk >= (size_t)N * nb) return;
+  const float g = (float)((double)__uint_as_float(amax_bits[e]) / 2688.0);
+  const size_t eoff = (size_t)e * N * K;
+  const uint16_t *src = w + eoff + blk * 16;
+  float v[16];
+  const u32x4 a = *(const u32x4 *)src, b = *(const u32x4 *)(src + 8);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(a[q] << 16);
+    v[2 * q + 1] = __uint_as_float(a[q] & 0xFFFF0000u);
+    v[8 + 2 * q] = __uint_as_float(b[q] << 16);
+    v[8 + 2 * q + 1] = __uint_as_float(b[q] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t code = 0;
+  double sb = 0.0;
+  if (g > 0.0f) {
+    code = e4m3_rne_sat((double)amax / (6.0 * (double)g));
+    sb = e4m3_value(code) * (double)g;
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t c = 0;
+    if (sb > 0.0) {
+      double q = (double)v[i] / sb;
+      q = fmin(6.0, fmax(-6.0, q));
+      const uint32_t mag = e2m1_rne(fabs(q));
+      c = mag | ((q < 0.0 && mag != 0) ? 8u : 0u);
+    }
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  *(u32x2 *)(packed + (size_t)e * N * (K / 2) + blk * 8) = u32x2{lo, hi};
+  scales[(size_t)e * N * nb + blk] = (uint8_t)code;
+}
+
+__global__ void k_write_global(const uint32_t *__restrict__ amax_bits, int E,
+                               float *__restrict__ global) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) global[e] = (float)((double)__uint_as_float(amax_bits[e]) / 2688.0);
+}
+
+// one thread per 8 elements: the expert kernels' decode, widened to bf16 (exact)
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ packed,
+                                                 const uint8_t *__restrict__ scales, int N, int K,
+                                                 uint16_t *__restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // dword index
+  if (i >= (size_t)N * K / 8) return;
+  const size_t n = i / (K / 8), k = (i % (K / 8)) * 8;
+  const uint32_t wv = *(const uint32_t *)(packed + n * (K / 2) + k / 2);
+  const BlockScale s = decode_block_scale(scales[n * (K / 16) + k / 16]);
+  const f16x8 h = dequant8(wv, s);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (uint32_t)f32_to_bf16((float)h[2 * q]) | ((uint32_t)f32_to_bf16((float)h[2 * q + 1]) << 16);
+  *(u32x4 *)(out + n * K + k) = o;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *packed,
+                              uint8_t *scales, float *global, void *stream) {
+  using namespace moe;
+  if (!w || !packed || !scales || !global) return MOE_ERR_NULL;
+  if (E <= 0 || N <= 0 || K <= 0 || K % 32) return MOE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  // the float output doubles as the per-expert max|W| (float bits) until the end
+  uint32_t *amax = (uint32_t *)global;
+  MOE_LAUNCH(k_fill_u32, dim3((E + 255) / 256), dim3(256), 0, s, amax, E, 0u);
+  const size_t per_e = (size_t)N * K;
+  const size_t gx0 = (per_e / 8 + 255) / 256;
+  const int gx = (int)(gx0 < 1024 ? gx0 : 1024);
+  MOE_LAUNCH(k_absmax, dim3(gx, E), dim3(256), 0, s, w, per_e, amax);
+  const size_t nblk = (size_t)N * (K / 16);
+  MOE_LAUNCH(k_quant, dim3((unsigned)((nblk + 255) / 256), E), dim3(256), 0, s, w, N, K,
+                     amax, packed, scales);
+  MOE_LAUNCH(k_write_global, dim3((E + 255) / 256), dim3(256), 0, s, amax, E, global);
+  return MOE_OK;
+}
+
+extern "C" int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream) {
+  using namespace moe;
+  if (!w || !out || !w->packed || !w->scales) return MOE_ERR_NULL;
+  if (w->N <= 0 || w->K <= 0 || w->K % 32 || e < 0 || e >= w->E) return MOE_ERR_SHAPE;
+  const size_t n8 = (size_t)w->N * w->K / 8;
+  const uint8_t *p = w->packed + (size_t)e * w->N * (w->K / 2);
+  const uint8_t *sc = w->scales + (size_t)e * w->N * (w->K / 16);
+  MOE_LAUNCH(k_dequant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, p, sc, w->N, w->K, out);
+  return MOE_OK;
+}
+
+extern "C" const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_WORKSPACE: return "workspace NULL or smaller than required";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int moe_abi_version(void) { return (1 << 16) | 0; }

@@ -1,0 +1,127 @@
+"""CPU checks of the C ABI: the built library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+codes before queueing any GPU work (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    from nvfp4_weight_only_moe_amd import _build, _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    return _lib.lib()
+
+
+def test_header_declares_the_hot_path():
+    names = _declared()
+    for n in ("moe_route", "moe_bucket", "nvfp4_expert_mlp", "moe_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from nvfp4_weight_only_moe_amd._lib import EXPORTED
+    names = _declared()
+    assert set(names) == set(EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.moe_status_str(st)
+    assert L.moe_abi_version() >> 16 == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+NULL = None
+
+
+def test_route_rejects(L):
+    args = [FAKE, FAKE, FAKE, FAKE, NULL, 4, 2816, 128, 8, 1e-6, FAKE, FAKE, NULL, FAKE, NULL]
+    a = list(args); a[0] = NULL
+    assert L.moe_route(*a) == -1                      # x NULL with T > 0
+    a = list(args); a[13] = NULL
+    assert L.moe_route(*a) == -1                      # logits required
+    a = list(args); a[6] = 2800
+    assert L.moe_route(*a) == -2                      # H % 32
+    a = list(args); a[8] = 129
+    assert L.moe_route(*a) == -2                      # top_k > E
+    a = list(args); a[7] = 120
+    assert L.moe_route(*a) == -4                      # E % 16
+    a = list(args); a[7], a[8] = 512, 8
+    assert L.moe_route(*a) == -4                      # E > 256
+    a = list(args); a[5] = -1
+    assert L.moe_route(*a) == -2
+
+
+def test_bucket_rejects(L):
+    ws = L.moe_bucket_workspace_bytes(64, 8, 128)
+    assert ws >= 256
+    assert L.moe_bucket(FAKE, 64, 8, 128, FAKE, FAKE, FAKE, FAKE, ws - 1, NULL) == -3
+    assert L.moe_bucket(FAKE, 64, 8, 128, FAKE, FAKE, FAKE, NULL, ws, NULL) == -1
+    assert L.moe_bucket(FAKE, 64, 17, 128, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -4
+    assert L.moe_bucket(FAKE, 64, 8, 300, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -4
+    assert L.moe_bucket(FAKE, -2, 8, 128, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -2
+
+
+def _tensor(E, N, K):
+    from nvfp4_weight_only_moe_amd._lib import Nvfp4TensorC
+    return Nvfp4TensorC(0x1000, 0x2000, 0x3000, E, N, K)
+
+
+def test_expert_mlp_rejects(L):
+    T, k, E, H, I = 64, 8, 128, 2816, 704
+    ws = L.moe_workspace_bytes(T, k, E, H, I)
+    g, u, d = _tensor(E, I, H), _tensor(E, I, H), _tensor(E, H, I)
+    ok = [FAKE, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), FAKE, FAKE, T, k, H, I, FAKE, FAKE, ws, NULL]
+    a = list(ok); a[12] = ws - 1
+    assert L.nvfp4_expert_mlp(*a) == -3
+    a = list(ok); a[11] = NULL
+    assert L.nvfp4_expert_mlp(*a) == -1
+    bad_d = _tensor(E, H, I + 64)
+    a = list(ok); a[3] = ctypes.byref(bad_d)
+    assert L.nvfp4_expert_mlp(*a) == -2
+    a = list(ok); a[9] = I + 32
+    g2, u2, d2 = _tensor(E, I + 32, H), _tensor(E, I + 32, H), _tensor(E, H, I + 32)
+    a[1], a[2], a[3] = ctypes.byref(g2), ctypes.byref(u2), ctypes.byref(d2)
+    a[12] = L.moe_workspace_bytes(T, k, E, H, I + 32)
+    assert L.nvfp4_expert_mlp(*a) == -4               # I % 64
+    nul = _tensor(E, I, H); nul.scales = None
+    a = list(ok); a[1] = ctypes.byref(nul)
+    assert L.nvfp4_expert_mlp(*a) == -1
+    # stage calls validate the same way
+    assert L.nvfp4_expert_prep(FAKE, FAKE, T, k, E, H, I, FAKE, ws - 1, NULL) == -3
+    assert L.nvfp4_expert_gate_up(ctypes.byref(g), ctypes.byref(d), FAKE, FAKE, T, k, H, I, FAKE, ws, NULL) == -2
+    assert L.nvfp4_expert_down(ctypes.byref(d), FAKE, T, k, H, I, NULL, FAKE, ws, NULL) == -1
+
+
+def test_combine_quantize_dequant_reject(L):
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 8, 2812, FAKE, NULL) == -2
+    assert L.moe_combine(NULL, FAKE, FAKE, 4, 8, 2816, FAKE, NULL) == -1
+    assert L.nvfp4_quantize(FAKE, 1, 16, 48, FAKE, FAKE, FAKE, NULL) == -2
+    assert L.nvfp4_quantize(FAKE, 1, 16, 64, FAKE, NULL, FAKE, NULL) == -1
+    t = _tensor(2, 16, 64)
+    assert L.nvfp4_dequant_bf16(ctypes.byref(t), 2, FAKE, NULL) == -2
+    assert L.nvfp4_dequant_bf16(ctypes.byref(t), 0, NULL, NULL) == -1
+
+
+def test_workspace_sizes_cover_buffers(L):
+    T, k, E, H, I = 16384, 8, 128, 2816, 704
+    P = T * k
+    ws = L.moe_workspace_bytes(T, k, E, H, I)
+    assert ws >= T * H * 2 + P * I * 2 + P * 4 + T * 4
+    assert L.moe_workspace_bytes(0, k, E, H, I) > 0
+    assert L.moe_bucket_workspace_bytes(T, k, E) >= 256

@@ -1,0 +1,279 @@
+"""GPU parity of each C-ABI call against the oracle on the same seeded inputs.
+
+Bit-exact: quantiser bytes, the bf16 decode, expert ids (outside near-ties),
+bucketing.  Floating point: routing weights within 4e-6; expert outputs and
+the combine within the bounds stated per test."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+from oracle import formats as F
+from oracle import moe as M
+from oracle.quantize import quantize, quantize_experts
+
+import nvfp4_weight_only_moe_amd as moe
+from nvfp4_weight_only_moe_amd import workload as W
+
+from parity_util import (REL_FROB_TOL, check_route, rel_frob, router_f64, row_rel)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()  # raises if the HIP library is missing
+    yield
+
+
+def _bits(a):
+    return W.to_device_bf16(a)
+
+
+def _np_bf16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- quantiser
+@pytest.mark.parametrize("shape", [(3, 48, 128), (2, 704, 2816), (2, 2816, 704)])
+def test_quantize_bit_exact(shape):
+    E, N, K = shape
+    rng = np.random.default_rng(N)
+    bits = S.f32_to_bf16_bits((rng.standard_normal(shape) * 0.02).astype(np.float32))
+    bits[0, :, 16:32] = 0                      # an all-zero block column
+    out = moe.Nvfp4Weights.empty(E, N, K)
+    moe.nvfp4_quantize(_bits(bits), out)
+    torch.cuda.synchronize()
+    p, s, g = quantize_experts(F.bf16_bits_to_f64(bits))
+    assert np.array_equal(out.packed.cpu().numpy(), p)
+    assert np.array_equal(out.scales.cpu().numpy(), s)
+    assert np.array_equal(out.global_scale.cpu().numpy().astype(np.float64), g)
+
+
+def test_quantize_edge_tensors():
+    # zero tensor, on-grid tensor (g = 1, scales 448), tiny values (subnormal
+    # E4M3 block scales) and exact E2M1 midpoints
+    K = 64
+    zero = np.zeros((1, 4, K), np.float32)
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(4, K)).astype(np.uint8)
+    codes[:, ::16] = 7
+    codes[codes == 8] = 0
+    grid = (F.e2m1_decode(codes) * 448.0).astype(np.float32)[None]
+    tiny = (rng.standard_normal((1, 4, K)) * 1e-3).astype(np.float32)
+    tiny[0, :, :16] *= 1e-5                    # blocks far below the tensor max
+    mids = np.tile(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2, np.float32), (4, K // 16))
+    mids = (mids * 448.0 * np.sign(rng.standard_normal((4, K)))).astype(np.float32)[None]
+    for arr in (zero, grid, tiny, mids):
+        bits = S.f32_to_bf16_bits(arr)
+        out = moe.Nvfp4Weights.empty(1, 4, K)
+        moe.nvfp4_quantize(_bits(bits), out)
+        torch.cuda.synchronize()
+        p, s, g = quantize(F.bf16_bits_to_f64(bits[0]))
+        assert np.array_equal(out.packed.cpu().numpy()[0], p)
+        assert np.array_equal(out.scales.cpu().numpy()[0], s)
+        assert float(out.global_scale.cpu().numpy()[0]) == g
+
+
+# ------------------------------------------------------------------- decode
+@pytest.mark.parametrize("N,K", [(32, 64), (704, 2816), (2816, 704)])
+def test_dequant_bf16_bit_exact(N, K):
+    rng = np.random.default_rng(K)
+    E = 2
+    packed = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(E, N, K // 16), dtype=np.uint8)  # every finite >= 0 code
+    scales[0, 0, :] = np.arange(K // 16) % 0x7F
+    w = moe.Nvfp4Weights(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(),
+                         torch.ones(E, dtype=torch.float32, device="cuda"))
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        moe.nvfp4_dequant_bf16(w, e, out)
+        torch.cuda.synchronize()
+        ref = F.dequantize_no_global(packed[e], scales[e])
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref)
+
+
+def test_dequant_every_scale_code_and_element():
+    # all 127 finite non-negative scale codes x all 16 element codes
+    K = 16 * 128
+    codes = np.tile(np.arange(16, dtype=np.uint8), 128)[None, :]
+    packed = F.pack_nibbles(codes)[None]
+    scales = np.concatenate([np.arange(0x7F), [0x38]]).astype(np.uint8)[None, None, :]
+    w = moe.Nvfp4Weights(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(),
+                         torch.ones(1, dtype=torch.float32, device="cuda"))
+    out = torch.empty((1, K), dtype=torch.bfloat16, device="cuda")
+    moe.nvfp4_dequant_bf16(w, 0, out)
+    torch.cuda.synchronize()
+    ref = F.dequantize_no_global(packed[0], scales[0])
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------- router
+def _route_gpu(x_bits, p, k, E):
+    T = x_bits.shape[0]
+    wr, sc, pes, bias = W.router_to_device(p)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    wr_raw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    moe.moe_route(_bits(x_bits), wr, sc, pes, bias, k, 1e-6, idx, w, wr_raw, lg)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), wr_raw.cpu().numpy(), lg.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,zipf,outliers", [(1, False, False), (4, False, False),
+                                             (64, False, False), (333, True, False),
+                                             (2048, True, True)])
+def test_route_model_shape(T, zipf, outliers):
+    p = S.router_params(0, zipf=zipf)
+    x = S.activations(90, T, outliers=outliers)
+    idx, w, w_raw, lg = _route_gpu(x, p, 8, 128)
+    r = router_f64(p)
+    ref = M.route(F.bf16_bits_to_f64(x), r["w_router"], r["scale"], r["per_expert_scale"], 8,
+                  r["bias"])
+    assert np.max(np.abs(lg - ref["logits"])) <= 2e-7
+    differ = check_route(idx, w, w_raw, ref, r["per_expert_scale"])
+    assert len(differ) <= max(1, T // 200)
+
+
+def test_route_small_odd_shapes():
+    for (t, h, e, k) in [(1, 32, 16, 1), (3, 96, 16, 2), (5, 64, 32, 4), (7, 2816, 256, 16)]:
+        c = S.small_case(t + e, t, h, 64, e, k, zipf=(t == 5))
+        idx, w, w_raw, lg = _route_gpu(c["x"], c["router"], k, e)
+        r = router_f64(c["router"])
+        ref = M.route(F.bf16_bits_to_f64(c["x"]), r["w_router"], r["scale"], r["per_expert_scale"],
+                      k, r["bias"])
+        assert np.max(np.abs(lg - ref["logits"])) <= 2e-7
+        check_route(idx, w, w_raw, ref, r["per_expert_scale"])
+
+
+def test_route_zero_row_and_ties():
+    # a zero row has all-zero logits: every expert ties, the lowest ids win
+    p = S.router_params(0)
+    x = np.zeros((2, 2816), np.uint16)
+    x[1] = S.activations(91, 1)[0]
+    idx, w, w_raw, lg = _route_gpu(x, p, 8, 128)
+    assert sorted(idx[0].tolist()) == list(range(8))
+    assert np.allclose(w_raw[0], 1 / 8, atol=1e-7)
+
+
+# ------------------------------------------------------------------- bucket
+def _bucket_gpu(idx, E):
+    T, k = idx.shape
+    ti = torch.from_numpy(idx.astype(np.int32)).cuda()
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pr = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_bucket_workspace_bytes(T, k, E), dtype=torch.uint8, device="cuda")
+    moe.moe_bucket(ti, E, off, sp, pr, ws)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sp.cpu().numpy(), pr.cpu().numpy(), int(ws[:4].view(torch.int32)[0])
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(0, 8, 128, 0), (1, 8, 128, 0), (4, 8, 128, 0), (64, 8, 128, 0),
+                                        (511, 8, 128, 0), (513, 8, 128, 1), (2048, 8, 128, 1),
+                                        (16384, 8, 128, 1), (37, 3, 5, 0), (100, 16, 256, 0)])
+def test_bucket_bit_exact(T, k, E, skew):
+    rng = np.random.default_rng(T * 31 + k)
+    if skew:
+        pr = 1.0 / np.arange(1, E + 1) ** 1.2
+        pr /= pr.sum()
+        idx = np.stack([rng.choice(E, k, replace=False, p=pr) for _ in range(T)]) if T else np.zeros((0, k), int)
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) if T else np.zeros((0, k), int)
+    off, sp, pr_, err = _bucket_gpu(idx, E)
+    ref = M.bucket(idx, E)
+    assert err == 0
+    assert np.array_equal(off, ref["offsets"])
+    assert np.array_equal(sp, ref["sorted_pairs"])
+    assert np.array_equal(pr_, ref["pair_rank"])
+
+
+@pytest.mark.parametrize("T", [5, 700])
+def test_bucket_invalid_ids_counted_and_parked(T):
+    k, E = 4, 16
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, size=(T, k))
+    bad = rng.random((T, k)) < 0.1
+    idx[bad] = np.where(rng.random(bad.sum()) < 0.5, -3, E + 7)
+    off, sp, pr, err = _bucket_gpu(idx, E)
+    assert err == int(bad.sum())
+    flat = idx.reshape(-1)
+    key = [(int(e) if 0 <= e < E else E, p) for p, e in enumerate(flat)]
+    order = [p for _, p in sorted(key)]
+    assert np.array_equal(sp, np.array(order))
+    assert np.array_equal(sp[pr], np.arange(T * k))
+    assert off[E] == T * k - err
+
+
+# ---------------------------------------------------------------- experts
+def _expert_case(T, k, E, H, I, seed):
+    c = S.small_case(seed, T, H, I, E, k)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    return c, idx
+
+
+@pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (5, 2, 8, 128, 64), (37, 4, 8, 192, 128),
+                                       (300, 2, 4, 256, 64)])
+def test_expert_mlp_small(T, k, E, H, I):
+    c, idx = _expert_case(T, k, E, H, I, seed=T)
+    layer = W.build_small_layer(c, k)
+    off, sp, pr, _ = _bucket_gpu(idx, E)
+    x = _bits(c["x"])
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    moe.nvfp4_expert_mlp(x, layer.gate, layer.up, layer.down, torch.from_numpy(off).cuda(),
+                         torch.from_numpy(sp).cuda(), k, y, ws)
+    torch.cuda.synchronize()
+    q = {n: quantize_experts(F.bf16_bits_to_f64(c[n])) for n in ("gate", "up", "down")}
+    fns = {n: M.nvfp4_weights(*q[n]) for n in q}
+    ref = M.experts(F.bf16_bits_to_f64(c["x"]), M.bucket(idx, E), k, fns["gate"], fns["up"], fns["down"])
+    got = y.float().cpu().numpy()
+    assert rel_frob(got, ref) <= 5e-3
+    assert np.max(row_rel(got, ref)) <= 1e-2
+
+
+def test_expert_mlp_large_activation_rows():
+    # rows spanning a wide range (1e-15 .. 1e15 in one batch; the intermediate
+    # A then spans 1e-30 .. 1e30, inside the bf16 range) stay finite and
+    # accurate thanks to the per-row power-of-two rescale
+    T, k, E, H, I = 6, 2, 4, 128, 64
+    c, idx = _expert_case(T, k, E, H, I, seed=77)
+    xf = S.bf16_bits_to_f32(c["x"]).copy()
+    xf[1] *= 1e15
+    xf[2] *= 1e-15
+    xf[3] *= 3e4
+    c["x"] = S.f32_to_bf16_bits(xf)
+    layer = W.build_small_layer(c, k)
+    off, sp, pr, _ = _bucket_gpu(idx, E)
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    moe.nvfp4_expert_mlp(_bits(c["x"]), layer.gate, layer.up, layer.down,
+                         torch.from_numpy(off).cuda(), torch.from_numpy(sp).cuda(), k, y, ws)
+    torch.cuda.synchronize()
+    q = {n: quantize_experts(F.bf16_bits_to_f64(c[n])) for n in ("gate", "up", "down")}
+    fns = {n: M.nvfp4_weights(*q[n]) for n in q}
+    ref = M.experts(F.bf16_bits_to_f64(c["x"]), M.bucket(idx, E), k, fns["gate"], fns["up"], fns["down"])
+    got = y.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.max(row_rel(got, ref)) <= 1e-2
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("T,k,H", [(1, 8, 2816), (9, 3, 64), (64, 8, 2816)])
+def test_combine(T, k, H):
+    rng = np.random.default_rng(T + k)
+    P = T * k
+    y = S.f32_to_bf16_bits(rng.standard_normal((P, H)).astype(np.float32))
+    w = rng.uniform(0.05, 1.5, (T, k)).astype(np.float32)
+    rank = rng.permutation(P).astype(np.int32)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(_bits(y), torch.from_numpy(w).cuda(), torch.from_numpy(rank).cuda(), out)
+    torch.cuda.synchronize()
+    ref = M.combine(F.bf16_bits_to_f64(y), w.astype(np.float64), rank, k)
+    got = out.float().cpu().numpy()
+    # one bf16 rounding of an fp32 sum: |err| <= 2^-8 |ref| + fp32 slack
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())

@@ -1,0 +1,172 @@
+"""Whole-block GPU parity against the fp64 oracle on the seeded model-shaped
+workloads (full size on the GPU; the oracle checks every token where it runs
+in seconds and a sample of tokens at prefill sizes), plus determinism, graph
+replay and small odd shapes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+from oracle import formats as F
+from oracle import moe as M
+from oracle.quantize import quantize_experts
+
+import nvfp4_weight_only_moe_amd as moe
+from nvfp4_weight_only_moe_amd import workload as W
+
+from parity_util import (REL_FROB_TOL, OracleExperts, check_route, rel_frob, router_f64, row_rel)
+
+pytestmark = pytest.mark.gpu
+
+_LAYER = {}
+
+
+@pytest.fixture(scope="module")
+def layer0():
+    assert torch.cuda.is_available()
+    moe.lib()
+    if "plain" not in _LAYER:
+        _LAYER["plain"] = W.build_layer(0, zipf=False)
+    return _LAYER["plain"]
+
+
+@pytest.fixture(scope="module")
+def layer0_zipf(layer0):
+    if "zipf" not in _LAYER:
+        p = S.router_params(0, zipf=True)
+        wr, sc, pes, bias = W.router_to_device(p)
+        _LAYER["zipf"] = moe.MoeLayer(wr, sc, pes, bias, layer0.gate, layer0.up, layer0.down, 8)
+    return _LAYER["zipf"]
+
+
+@pytest.fixture(scope="module")
+def oracle_experts():
+    return OracleExperts(0)
+
+
+def _run(layer, x_bits):
+    T = x_bits.shape[0]
+    buf = moe.MoeBuffers(T, layer.H, layer.I, layer.E, layer.top_k)
+    moe.forward(layer, W.to_device_bf16(x_bits), buf)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _check_block(buf, x_bits, router_p, oe, sample=None, tol=REL_FROB_TOL):
+    T = x_bits.shape[0]
+    r = router_f64(router_p)
+    xs = F.bf16_bits_to_f64(x_bits)
+    toks = np.arange(T) if sample is None else np.asarray(sample)
+    ref_r = M.route(xs[toks], r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])
+    gidx = buf.topk_idx.cpu().numpy()[toks]
+    check_route(gidx, buf.topk_w.cpu().numpy()[toks], buf.topk_w_raw.cpu().numpy()[toks], ref_r,
+                r["per_expert_scale"])
+    assert buf.bucket_error_count() == 0
+    oe.prefetch(np.unique(gidx))
+    # the oracle follows the GPU's choice on flagged near-ties (same set otherwise)
+    ref = M.moe_block(xs[toks], xs[toks], r, oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
+                      ids=gidx.astype(np.int64))["out"]
+    got = buf.out.float().cpu().numpy()[toks]
+    err = rel_frob(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err <= tol, err
+    return err, np.max(row_rel(got, ref))
+
+
+def test_layer_T4_all_tokens(layer0, oracle_experts):
+    x = S.activations(0, 4)
+    buf = _run(layer0, x)
+    err, worst_row = _check_block(buf, x, S.router_params(0), oracle_experts)
+    assert worst_row <= 1e-2
+    print(f"T=4 rel_frob={err:.3e} worst_row={worst_row:.3e}")
+
+
+def test_layer_T64_all_tokens(layer0, oracle_experts):
+    x = S.activations(1, 64)
+    buf = _run(layer0, x)
+    err, worst_row = _check_block(buf, x, S.router_params(0), oracle_experts)
+    assert worst_row <= 1e-2
+    print(f"T=64 rel_frob={err:.3e} worst_row={worst_row:.3e}")
+
+
+def test_layer_T2048_zipf_sampled(layer0_zipf, oracle_experts):
+    x = S.activations(2, 2048)
+    buf = _run(layer0_zipf, x)
+    counts = np.diff(buf.expert_offsets.cpu().numpy())
+    assert counts.sum() == 2048 * 8
+    assert counts.max() > 4 * counts.mean()   # the skew is there
+    sample = np.linspace(0, 2047, 12).astype(int)
+    err, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, sample)
+    print(f"T=2048 rel_frob(sample)={err:.3e} max/mean={counts.max() / counts.mean():.1f}")
+
+
+def test_layer_T16384_zipf_outliers_sampled(layer0_zipf, oracle_experts):
+    x = S.activations(4, 16384, outliers=True)
+    buf = _run(layer0_zipf, x)
+    out_rows = S.outlier_rows(4, 16384)
+    normal = np.setdiff1d(np.linspace(0, 16383, 10).astype(int), out_rows)
+    e1, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, out_rows[:5])
+    e2, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, normal)
+    print(f"T=16384 outlier rows rel_frob={e1:.3e} normal rows={e2:.3e}")
+
+
+def test_layer_deterministic(layer0):
+    x = S.activations(1, 64)
+    a = _run(layer0, x)
+    b = _run(layer0, x)
+    for name in ("topk_idx", "topk_w", "expert_offsets", "sorted_pairs", "pair_rank", "y_sorted", "out"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_graph_replay_matches_eager(layer0):
+    x = W.to_device_bf16(S.activations(1, 64))
+    eager = moe.MoeBuffers(64, layer0.H, layer0.I, layer0.E, 8)
+    moe.forward(layer0, x, eager)
+    buf = moe.MoeBuffers(64, layer0.H, layer0.I, layer0.E, 8)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(layer0, x, buf)          # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(layer0, x, buf)
+    for _ in range(3):
+        buf.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.out, eager.out)
+        assert torch.equal(buf.sorted_pairs, eager.sorted_pairs)
+
+
+@pytest.mark.parametrize("T,k,E,H,I,zipf", [(1, 2, 16, 128, 64, False), (3, 2, 16, 128, 64, False),
+                                            (5, 4, 32, 192, 128, True), (50, 8, 16, 256, 64, True)])
+def test_small_block_odd_shapes(T, k, E, H, I, zipf):
+    c = S.small_case(T * 7 + E, T, H, I, E, k, zipf)
+    layer = W.build_small_layer(c, k)
+    buf = moe.MoeBuffers(T, H, I, E, k)
+    moe.forward(layer, W.to_device_bf16(c["x"]), buf)
+    torch.cuda.synchronize()
+    r = router_f64(c["router"])
+    xs = F.bf16_bits_to_f64(c["x"])
+    ref_r = M.route(xs, r["w_router"], r["scale"], r["per_expert_scale"], k, r["bias"])
+    gidx = buf.topk_idx.cpu().numpy()
+    check_route(gidx, buf.topk_w.cpu().numpy(), buf.topk_w_raw.cpu().numpy(), ref_r,
+                r["per_expert_scale"])
+    q = {n: quantize_experts(F.bf16_bits_to_f64(c[n])) for n in ("gate", "up", "down")}
+    fns = {n: M.nvfp4_weights(*q[n]) for n in q}
+    ref = M.moe_block(xs, xs, r, fns["gate"], fns["up"], fns["down"], k=k, ids=gidx)["out"]
+    dense = M.moe_block_dense(xs, xs, r, fns["gate"], fns["up"], fns["down"], k=k)
+    got = buf.out.float().cpu().numpy()
+    assert rel_frob(got, ref) <= REL_FROB_TOL
+    if np.array_equal(np.sort(gidx, 1), np.sort(ref_r["idx"], 1)):
+        assert rel_frob(got, dense) <= REL_FROB_TOL
+
+
+def test_empty_batch_is_noop(layer0):
+    buf = moe.MoeBuffers(0, layer0.H, layer0.I, layer0.E, 8)
+    moe.forward(layer0, torch.empty((0, layer0.H), dtype=torch.bfloat16, device="cuda"), buf)
+    torch.cuda.synchronize()
+    assert buf.expert_offsets.cpu().numpy().tolist() == [0] * (layer0.E + 1)
