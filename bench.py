@@ -133,6 +133,9 @@ class HipRuntime:
                      "hipGraphAddChildGraphNode")
             prev = node
             prev = add_event(ev)
+        return self.instantiate(g)
+
+    def instantiate(self, g):
         exe = ctypes.c_void_p()
         self._ok(self.h.hipGraphInstantiate(ctypes.byref(exe), g, None, None, 0),
                  "hipGraphInstantiate")
@@ -245,6 +248,20 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # the same K steps as a plain graph of kernel nodes only (no event nodes)
+    plain_ms = None
+    if graph_exec is not None:
+        def all_calls():
+            for call in calls:
+                call()
+        plain = hip.instantiate(hip.capture_graph(hs, all_calls))
+        hip.launch(plain, hs)                  # one untimed replay
+        stream.synchronize()
+        ta = time.perf_counter()
+        hip.launch(plain, hs)
+        stream.synchronize()
+        plain_ms = (time.perf_counter() - ta) * 1e3 / args.steps
+
     stage_ms = {n: [] for n in STAGES}
     gpu_step_ms = []
     per_step = n_layers * len(STAGES)
@@ -293,6 +310,7 @@ def main():
                    "timing": mode},
         "detail": {
             "gpu_ms_per_step_events": float(np.mean(gpu_step_ms)),
+            "plain_graph_ms_per_step": plain_ms,
             "stage_avg_us": stage_avg_us,
             "active_experts": U_total,
             "expert_weight_GBps": per_exp * U_total / step_s / 1e9,

@@ -50,6 +50,10 @@ extern "C" {
 #define MOE_MAX_EXPERTS 256 /* E                                   */
 #define MOE_MAX_TOPK 16     /* top_k                               */
 
+/* Byte layouts of an nvfp4_tensor. */
+#define MOE_LAYOUT_CANONICAL 0 /* the row-major layout below (the pages' packed-U8 form) */
+#define MOE_LAYOUT_TILED 1     /* the same bytes permuted into 16-row x 128-K tiles      */
+
 /*
  * One stack of NVFP4 weights, one tensor per expert, canonical layout:
  *   packed [E][N][K/2]  uint8: element k of row n is nibble (k & 1) of byte
@@ -61,12 +65,25 @@ extern "C" {
  * Element value: E2M1(code) * E4M3(scale) * global[e].
  * N is the output dimension, K the input ("inner") dimension, K % 32 == 0.
  * Block scales must be finite and non-negative (the quantiser writes no others).
+ *
+ * MOE_LAYOUT_TILED (what the expert kernels read; made by nvfp4_repack):
+ * the same bytes, permuted so that one wave-wide 16-byte load per lane reads
+ * one contiguous kilobyte already in matrix-core operand order.  Per expert,
+ * rows are grouped in tiles of 16 (N % 16 == 0) and K in units of 128; the
+ * units of row tile t are stored one after the other from byte t*16*(K/2).
+ * Unit u of tile t holds, for lane l = 16*g + r (g = 0..3, r = 0..15), the 16
+ * canonical bytes of row 16t+r covering k = 128u + 32g .. 128u + 32g + 31 at
+ * byte 1024u + 16l (a last, partial unit holds only the lanes with k < K).
+ * Scales likewise: tile t starts at byte t*K, unit u at +128u, lane l at +2l
+ * holds the two scale bytes of row 16t+r for k = 128u + 32g .. +31.
+ * Sizes per expert are unchanged: N*K/2 and N*K/16 bytes.
  */
 typedef struct {
   const uint8_t *packed;
   const uint8_t *scales;
   const float *global;
   int32_t E, N, K;
+  int32_t layout; /* MOE_LAYOUT_CANONICAL or MOE_LAYOUT_TILED */
 } nvfp4_tensor;
 
 /*
@@ -133,8 +150,8 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  *
  *   x_expert       [T][H] bf16   expert input (the pre-normed residual; may
  *                                alias the router's x)
- *   gate, up       nvfp4_tensor  N = I, K = H
- *   down           nvfp4_tensor  N = H, K = I
+ *   gate, up       nvfp4_tensor  N = I, K = H, MOE_LAYOUT_TILED
+ *   down           nvfp4_tensor  N = H, K = I, MOE_LAYOUT_TILED
  *   expert_offsets [E+1], sorted_pairs [T*top_k]  from moe_bucket
  *   y_sorted       out [T*top_k][H] bf16  expert output of the pair at each
  *                                sorted position (routing weight not applied)
@@ -147,7 +164,8 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, top_k <= 0, H or I <= 0,
  * descriptor shapes not [E][I][H], [E][I][H], [E][H][I] with one E);
  * MOE_ERR_UNSUPPORTED (H % 64, I % 64, E > MOE_MAX_EXPERTS,
- * top_k > MOE_MAX_TOPK); MOE_ERR_WORKSPACE.
+ * top_k > MOE_MAX_TOPK, a descriptor not in MOE_LAYOUT_TILED);
+ * MOE_ERR_WORKSPACE.
  */
 int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate, const nvfp4_tensor *up,
                      const nvfp4_tensor *down, const int32_t *expert_offsets,
@@ -209,6 +227,16 @@ int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pa
  */
 int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *packed,
                    uint8_t *scales, float *global, void *stream);
+
+/*
+ * nvfp4_repack -- weight preparation: canonical -> MOE_LAYOUT_TILED (a pure
+ * permutation of bytes, see nvfp4_tensor).  src must be canonical; the
+ * outputs have src's sizes and must not overlap src.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E, N <= 0, N % 16, K <= 0, K % 32),
+ * MOE_ERR_UNSUPPORTED (src not canonical).
+ */
+int nvfp4_repack(const nvfp4_tensor *src, uint8_t *packed_tiled, uint8_t *scales_tiled,
+                 void *stream);
 
 /*
  * nvfp4_dequant_bf16 -- decode expert e of a stack to bf16 without the FP32

@@ -5,13 +5,14 @@ The product is the HIP library ``libmoe_nvfp4.so`` behind the C ABI in
 the four-call block sequence (``block``) and device-resident synthetic
 workloads (``workload``).
 """
-from ._lib import (EXPORTED, MoeError, Nvfp4Weights, lib, moe_bucket, moe_bucket_workspace_bytes,
+from ._lib import (EXPORTED, LAYOUT_CANONICAL, LAYOUT_TILED, MoeError, Nvfp4Weights, lib, moe_bucket, moe_bucket_workspace_bytes,
                    moe_combine, moe_route, moe_workspace_bytes, nvfp4_dequant_bf16,
                    nvfp4_expert_down, nvfp4_expert_gate_up, nvfp4_expert_mlp, nvfp4_expert_prep,
-                   nvfp4_quantize)
+                   nvfp4_quantize, nvfp4_repack)
 from .block import MoeBuffers, MoeLayer, forward
 
 __all__ = ["EXPORTED", "MoeError", "Nvfp4Weights", "lib", "moe_bucket", "moe_bucket_workspace_bytes",
            "moe_combine", "moe_route", "moe_workspace_bytes", "nvfp4_dequant_bf16",
            "nvfp4_expert_mlp", "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
-           "nvfp4_quantize", "MoeBuffers", "MoeLayer", "forward"]
+           "nvfp4_quantize", "nvfp4_repack", "LAYOUT_CANONICAL", "LAYOUT_TILED", "MoeBuffers",
+           "MoeLayer", "forward"]

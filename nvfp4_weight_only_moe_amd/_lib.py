@@ -19,8 +19,10 @@ _ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
 
 EXPORTED = ("moe_route", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
-            "moe_workspace_bytes", "moe_combine", "nvfp4_quantize", "nvfp4_dequant_bf16",
-            "moe_status_str", "moe_abi_version")
+            "moe_workspace_bytes", "moe_combine", "nvfp4_quantize", "nvfp4_repack",
+            "nvfp4_dequant_bf16", "moe_status_str", "moe_abi_version")
+
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -33,7 +35,7 @@ class MoeError(RuntimeError):
 class Nvfp4TensorC(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("global_", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("K", ctypes.c_int32)]
+                ("K", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -44,7 +46,7 @@ def lib(path=None):
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("MOE_NVFP4_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} not found: build it first (python __graft_entry__.py build "
                            "or nvfp4_weight_only_moe_amd._build.build())")
@@ -62,6 +64,7 @@ def lib(path=None):
         "moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "moe_combine": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp]),
+        "nvfp4_repack": (ctypes.c_int, [P, vp, vp, vp]),
         "nvfp4_dequant_bf16": (ctypes.c_int, [P, i32, vp, vp]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_abi_version": (ctypes.c_int, []),
@@ -101,29 +104,36 @@ _B16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
 class Nvfp4Weights:
-    """One NVFP4 stack: packed [E,N,K/2] u8, scales [E,N,K/16] u8, global [E] f32."""
+    """One NVFP4 stack: packed [E,N,K/2] u8, scales [E,N,K/16] u8, global [E] f32,
+    in the canonical or the tiled byte layout (same sizes)."""
 
-    def __init__(self, packed, scales, global_scale):
+    def __init__(self, packed, scales, global_scale, layout=LAYOUT_CANONICAL):
         self.packed, self.scales, self.global_scale = packed, scales, global_scale
         self.E, self.N, k2 = packed.shape
         self.K = 2 * k2
+        self.layout = layout
 
     @classmethod
-    def empty(cls, E, N, K, device="cuda"):
+    def empty(cls, E, N, K, device="cuda", layout=LAYOUT_CANONICAL):
         return cls(torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
                    torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
-                   torch.empty((E,), dtype=torch.float32, device=device))
+                   torch.empty((E,), dtype=torch.float32, device=device), layout)
 
     def c(self):
         _ptr(self.packed, torch.uint8, (self.E, self.N, self.K // 2), "packed")
         _ptr(self.scales, torch.uint8, (self.E, self.N, self.K // 16), "scales")
         _ptr(self.global_scale, torch.float32, (self.E,), "global")
         return Nvfp4TensorC(self.packed.data_ptr(), self.scales.data_ptr(),
-                            self.global_scale.data_ptr(), self.E, self.N, self.K)
+                            self.global_scale.data_ptr(), self.E, self.N, self.K, self.layout)
 
     def select(self, e0, e1):
         """Experts e0..e1-1 (views, no copy)."""
-        return Nvfp4Weights(self.packed[e0:e1], self.scales[e0:e1], self.global_scale[e0:e1])
+        return Nvfp4Weights(self.packed[e0:e1], self.scales[e0:e1], self.global_scale[e0:e1],
+                            self.layout)
+
+    def clone(self):
+        return Nvfp4Weights(self.packed.clone(), self.scales.clone(), self.global_scale.clone(),
+                            self.layout)
 
 
 def moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps,
@@ -224,6 +234,19 @@ def nvfp4_quantize(w, out, stream=None):
                               _ptr(out.scales, torch.uint8, (E, N, K // 16), "scales"),
                               _ptr(out.global_scale, torch.float32, (E,), "global"), _stream(stream))
     _check("nvfp4_quantize", st)
+
+
+def nvfp4_repack(w, stream=None):
+    """Canonical -> tiled copy of a stack (the layout the expert kernels read)."""
+    if w.layout != LAYOUT_CANONICAL:
+        raise ValueError("nvfp4_repack takes canonical weights")
+    out = Nvfp4Weights(torch.empty_like(w.packed), torch.empty_like(w.scales), w.global_scale,
+                       LAYOUT_TILED)
+    c = w.c()
+    st = lib().nvfp4_repack(ctypes.byref(c), _ptr(out.packed, torch.uint8, None, "packed"),
+                            _ptr(out.scales, torch.uint8, None, "scales"), _stream(stream))
+    _check("nvfp4_repack", st)
+    return out
 
 
 def nvfp4_dequant_bf16(w, e, out, stream=None):

@@ -14,17 +14,38 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
                                                  int H, uint16_t *__restrict__ out) {
   const int t = blockIdx.x;
   const int P = T * K;
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < K; ++j) {
-      const int r = rank[(size_t)t * K + j];
-      if (r < 0 || r >= P) continue;
-      const float wj = w[(size_t)t * K + j];
-      const u32x4 v = *(const u32x4 *)(y + (size_t)r * H + c);
+  // ranks and weights first, then every row load issued before any is used,
+  // so the loads of the K rows overlap instead of queueing one by one
+  int rk[MOE_MAX_TOPK];
+  float wk[MOE_MAX_TOPK];
+  uint32_t valid = 0;  // bit j: slot j has a rank inside [0, P)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wj, __uint_as_float(v[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wj, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    rk[j] = 0;
+    wk[j] = 0.0f;
+    if (j < K) {
+      const int rr = rank[(size_t)t * K + j];
+      if (rr >= 0 && rr < P) {
+        rk[j] = rr;
+        wk[j] = w[(size_t)t * K + j];
+        valid |= 1u << j;
+      }
+    }
+  }
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    u32x4 v[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if ((valid >> j) & 1u) v[j] = *(const u32x4 *)(y + (size_t)rk[j] * H + c);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if ((valid >> j) & 1u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wk[j], __uint_as_float(v[j][i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wk[j], __uint_as_float(v[j][i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
       }
     }
     u32x4 o;

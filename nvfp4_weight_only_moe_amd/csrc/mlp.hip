@@ -62,20 +62,20 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
 // ---------------------------------------------------------------- prep ----
 __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ x, int T, int H,
                                                    const int32_t *__restrict__ offsets, int E,
-                                                   int P, uint16_t *__restrict__ x16,
+                                                   int P, int bm, uint16_t *__restrict__ x16,
                                                    int32_t *__restrict__ x_exp,
                                                    int32_t *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles,
                                                    uint32_t *__restrict__ a_max) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (blockIdx.x == gridDim.x - 1) {
-    // tile list: expert e contributes ceil(M_e / kBM) tiles (wave 0 only)
+    // tile list: expert e contributes ceil(M_e / bm) tiles (wave 0 only)
     if (wave != 0) return;
     int carry = 0;
     for (int base = 0; base < E; base += kWave) {
       const int e = base + lane;
       const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
-      const int c = (m + kBM - 1) / kBM;
+      const int c = (m + bm - 1) / bm;
       int incl = c;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
       }
       for (int i = 0; i < c; ++i) {
         tiles[2 * (carry + incl - c + i)] = e;
-        tiles[2 * (carry + incl - c + i) + 1] = i * kBM;
+        tiles[2 * (carry + incl - c + i) + 1] = i * bm;
       }
       carry += __shfl(incl, kWave - 1, kWave);
     }
@@ -129,149 +129,229 @@ __device__ __forceinline__ float gelu_tanh(float g) {
   return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
 }
 
-// ------------------------------------------------------------- gate/up ----
-__global__ __launch_bounds__(kThreads) void k_gateup(
-    const uint16_t *__restrict__ x16, const int32_t *__restrict__ x_exp,
+// ------------------------------------------------- grouped expert GEMM ----
+// One kernel template for both projections.  A workgroup (4 waves) owns one
+// tile of kBM*MSUB sorted rows of one expert and a slice of output columns;
+// each wave owns NT row tiles (16 weight rows each) of that slice: for the
+// gated projection NT = 2 (16 gate rows and the same 16 up rows), for down
+// NT row tiles of consecutive outputs.
+//
+// K advances in units of 128.  Per unit, the activation tile [rows][128] is
+// staged once in LDS as f16 (double-buffered) and shared by the 4 waves; each
+// lane loads its 16 bytes of every weight row tile it owns (one contiguous
+// kilobyte per wave in the tiled layout), dequantises them in registers and
+// runs 4 x MSUB x NT MFMAs 16x16x32.  The weights of the next unit are loaded
+// while the current one is multiplied.
+constexpr int kUnitK = 128;
+constexpr int kLdsRow = kUnitK + 8;  // f16 per LDS row (padding spreads banks)
+#ifndef MOE_GEMM_PD
+#define MOE_GEMM_PD 1
+#endif
+constexpr int kPD = MOE_GEMM_PD;     // units in flight per lane (weights and activations)
+
+template <int MSUB, int NT, bool GATED>
+__global__ __launch_bounds__(kThreads) void k_expert_gemm(
+    const uint16_t *__restrict__ a_src,       // GATED: x16 [T][K] f16; else A [P][K] bf16
+    const int32_t *__restrict__ row_exp,      // GATED: x_exp [T];  else unused
+    uint32_t *__restrict__ a_max,             // GATED: row max of A (written); else read
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_pairs, int top_k,
-    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles, Nvfp4 gate, Nvfp4 up,
-    int H, int I, uint16_t *__restrict__ a_out, uint32_t *__restrict__ a_max) {
-  const int tile = blockIdx.y;
-  if (tile >= ntiles[0]) return;
-  const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
-  const int row0 = offsets[e] + m0;                       // first sorted row of the tile
-  const int mrows = min(kBM, offsets[e + 1] - row0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * kCols + wave * 16;
-
-  const size_t wrow = (size_t)e * I + n0 + r;
-  const uint8_t *pg = gate.packed + wrow * (H / 2);
-  const uint8_t *pu = up.packed + wrow * (H / 2);
-  const uint8_t *sg = gate.scales + wrow * (H / 16);
-  const uint8_t *su = up.scales + wrow * (H / 16);
-  const bool a_ok = r < mrows;
-  const uint16_t *pa = x16 + (size_t)(a_ok ? sorted_pairs[row0 + r] / top_k : 0) * H;
-
-  f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-  for (int kk = 0; kk < H; kk += 128) {
-    // H % 32 == 0: a lane's 32 K indices are all inside or all outside; lanes
-    // outside feed zeros (the MFMA itself always runs wave-wide)
-    const int k = kk + 32 * g;
-    const bool k_ok = k < H;
-    u32x4 wg = {0, 0, 0, 0}, wu = {0, 0, 0, 0};
-    uint32_t cg = 0, cu = 0;
-    if (k_ok) {
-      wg = *(const u32x4 *)(pg + k / 2);
-      wu = *(const u32x4 *)(pu + k / 2);
-      cg = *(const uint16_t *)(sg + k / 16);
-      cu = *(const uint16_t *)(su + k / 16);
-    }
-    f16x8 a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 v = {0, 0, 0, 0};
-      if (a_ok && k_ok) v = *(const u32x4 *)(pa + k + 8 * j);
-      a[j] = __builtin_bit_cast(f16x8, v);
-    }
-    const BlockScale bg0 = decode_block_scale(cg & 0xFF), bg1 = decode_block_scale(cg >> 8);
-    const BlockScale bu0 = decode_block_scale(cu & 0xFF), bu1 = decode_block_scale(cu >> 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      accg = mfma16x16x32(a[j], dequant8(wg[j], j < 2 ? bg0 : bg1), accg);
-      accu = mfma16x16x32(a[j], dequant8(wu[j], j < 2 ? bu0 : bu1), accu);
-    }
-  }
-  // epilogue: lane holds rows 4g+j, column n0 + r
-  const float gg = gate.global[e], gu = up.global[e];
-  float rmax[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = 4 * g + j;
-    rmax[j] = 0.0f;
-    if (m < mrows) {
-      const int tok = sorted_pairs[row0 + m] / top_k;
-      const float f = __builtin_ldexpf(1.0f, x_exp[tok] - 14);
-      const float G = accg[j] * (gg * f), U = accu[j] * (gu * f);
-      const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
-      a_out[(size_t)(row0 + m) * I + n0 + r] = ab;
-      rmax[j] = fabsf(bf16_to_f32(ab));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) rmax[j] = fmaxf(rmax[j], __shfl_xor(rmax[j], o, kWave));
-    const int m = 4 * g + j;
-    if (r == 0 && m < mrows) atomicMax(&a_max[row0 + m], __float_as_uint(rmax[j]));
-  }
-}
-
-// ---------------------------------------------------------------- down ----
-constexpr int kMaxI = 2048;  // largest expert intermediate size held in LDS
-
-__global__ __launch_bounds__(kThreads) void k_down(
-    const uint16_t *__restrict__ a_in, const uint32_t *__restrict__ a_max,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, Nvfp4 down, int I, int H, uint16_t *__restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_a[];  // [kBM][I + 8] f16
+    const int32_t *__restrict__ tiles, const int32_t *__restrict__ ntiles,
+    Nvfp4 w0, Nvfp4 w1,                       // GATED: gate, up; else w0 = down
+    int K, int N, uint16_t *__restrict__ out, int out_ld) {
+  constexpr int BM = kBM * MSUB;
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * kLdsRow];
+  __shared__ float s_rowscale[BM];
   const int tile = blockIdx.y;
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], m0 = tiles[2 * tile + 1];
   const int row0 = offsets[e] + m0;
-  const int mrows = min(kBM, offsets[e + 1] - row0);
-  const int ld = I + 8;
-  const int tid = threadIdx.x;
-  // stage A rows as f16, each row scaled by 2^(14 - exponent of its max)
-  for (int i = tid; i < kBM * (I / 8); i += kThreads) {
-    const int m = i / (I / 8), c = (i % (I / 8)) * 8;
-    u32x4 o = {0, 0, 0, 0};
-    if (m < mrows) {
-      const float f = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[row0 + m])));
-      const u32x4 v = *(const u32x4 *)(a_in + (size_t)(row0 + m) * I + c);
+  const int mrows = min(BM, offsets[e + 1] - row0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nunits = (K + kUnitK - 1) / kUnitK;
+
+  // ---- staging map: thread -> (row, 16-byte column) of the activation tile.
+  // Every load below is issued unconditionally from a valid address and the
+  // unwanted ones are zeroed with a select, so the loop body has no branches
+  // and the compiler can wait for exactly the load it needs (not for all).
+  const int st_col = (tid & 15) * 8;  // f16 element offset inside the unit
+  const uint16_t *st_src[MSUB];
+  bool st_ok[MSUB];
+  float st_scale[MSUB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f16 lo = (f16)(__uint_as_float(v[q] << 16) * f);
-        const f16 hi = (f16)(__uint_as_float(v[q] & 0xFFFF0000u) * f);
-        o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
+  for (int q = 0; q < MSUB; ++q) {
+    const int m = q * kBM + (tid >> 4);
+    st_ok[q] = m < mrows;
+    st_scale[q] = 1.0f;
+    const int mm = st_ok[q] ? m : 0;  // row 0 of the tile always exists
+    if (GATED) {
+      st_src[q] = a_src + (size_t)(sorted_pairs[row0 + mm] / top_k) * K;
+    } else {
+      st_src[q] = a_src + (size_t)(row0 + mm) * K;
+      st_scale[q] = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[row0 + mm])));
     }
-    *(u32x4 *)(s_a + m * ld + c) = o;
   }
+  // per-row factor applied to the fp32 sums: 2^(exponent - 14)
+  if (tid < BM) {
+    float f = 0.0f;
+    if (tid < mrows) {
+      const int ex = GATED ? row_exp[sorted_pairs[row0 + tid] / top_k]
+                           : row_exponent(__uint_as_float(a_max[row0 + tid]));
+      f = __builtin_ldexpf(1.0f, ex - 14);
+    }
+    s_rowscale[tid] = f;
+  }
+
+  auto load_a = [&](int u, u32x4 (&v)[MSUB]) {
+    const int k = u * kUnitK + st_col;
+    const bool kok = k < K;
+    const int kc = kok ? k : 0;
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q) {
+      const u32x4 t = *(const u32x4 *)(st_src[q] + kc);
+      const bool ok = kok && st_ok[q];
+      v[q] = u32x4{ok ? t[0] : 0u, ok ? t[1] : 0u, ok ? t[2] : 0u, ok ? t[3] : 0u};
+    }
+  };
+  auto store_a = [&](int buf, const u32x4 (&v)[MSUB]) {
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q) {
+      u32x4 o = v[q];
+      if (!GATED) {  // bf16 -> f16 with the row's power of two (exact)
+        const float f = st_scale[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16 lo = (f16)(__uint_as_float(v[q][i] << 16) * f);
+          const f16 hi = (f16)(__uint_as_float(v[q][i] & 0xFFFF0000u) * f);
+          o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+      }
+      *(u32x4 *)(&s_a[buf][(q * kBM + (tid >> 4)) * kLdsRow + st_col]) = o;
+    }
+  };
+
+  // ---- weight streams of this wave: NT row tiles.  Lane (r, g) of unit u
+  // is at +1024u (packed) / +128u (scales); lane (r, 0) of unit 0 always
+  // exists and stands in for lanes past the end of K.
+  const uint8_t *wp[NT];
+  const uint8_t *ws[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const Nvfp4 &w = (GATED && i == 1) ? w1 : w0;
+    const int nt = GATED ? (blockIdx.x * 4 + wave) : ((blockIdx.x * 4 + wave) * NT + i);
+    wp[i] = w.packed + (size_t)e * N * (K / 2) + (size_t)nt * 16 * (K / 2) + lane * 16;
+    ws[i] = w.scales + (size_t)e * N * (K / 16) + (size_t)nt * K + lane * 2;
+  }
+  auto load_w = [&](int u, u32x4 (&wv)[NT], uint32_t (&sv)[NT]) {
+    const bool ok = u < nunits && u * kUnitK + 32 * g < K;
+    const size_t po = ok ? (size_t)u * 1024 : 0, so = ok ? (size_t)u * 128 : 0;
+    const int pb = ok ? 0 : 256 * g, sb = ok ? 0 : 32 * g;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const u32x4 t = __builtin_nontemporal_load((const u32x4 *)(wp[i] + po - pb));
+      const uint32_t c = *(const uint16_t *)(ws[i] + so - sb);
+      wv[i] = u32x4{ok ? t[0] : 0u, ok ? t[1] : 0u, ok ? t[2] : 0u, ok ? t[3] : 0u};
+      sv[i] = ok ? c : 0u;
+    }
+  };
+
+  f32x4 acc[MSUB][NT];
+#pragma unroll
+  for (int q = 0; q < MSUB; ++q)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
+
+  // ---- pipeline.  Weights: unit u+kPD is loaded into the register slot
+  // that unit u just used.  Activations: unit u+kPD is loaded into a
+  // register slot before unit u is multiplied and reaches LDS (double
+  // buffer) at the end of iteration u+kPD-1.  Units past the end are zeros
+  // (the unit count is rounded up to a multiple of kPD).  One barrier per unit.
+  u32x4 wbuf[kPD][NT];
+  uint32_t sbuf[kPD][NT];
+  u32x4 av[kPD][MSUB];
+  load_a(0, av[0]);
+  store_a(0, av[0]);
+#pragma unroll
+  for (int d = 1; d < kPD; ++d) load_a(d, av[d]);
+#pragma unroll
+  for (int d = 0; d < kPD; ++d) load_w(d, wbuf[d], sbuf[d]);
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * kCols + wave * 16;
-  const size_t wrow = (size_t)e * H + n0 + r;
-  const uint8_t *pd = down.packed + wrow * (I / 2);
-  const uint8_t *sd = down.scales + wrow * (I / 16);
-  f32x4 acc = {0, 0, 0, 0};
-  for (int kk = 0; kk < I; kk += 128) {
-    // I % 32 == 0: a lane's 32 K indices are all inside or all outside; lanes
-    // outside feed zeros (the MFMA itself always runs wave-wide)
-    const int k = kk + 32 * g;
-    const bool k_ok = k < I;
-    u32x4 wd = {0, 0, 0, 0};
-    uint32_t cd = 0;
-    if (k_ok) {
-      wd = *(const u32x4 *)(pd + k / 2);
-      cd = *(const uint16_t *)(sd + k / 16);
-    }
-    const BlockScale b0 = decode_block_scale(cd & 0xFF), b1 = decode_block_scale(cd >> 8);
+  const int nu = (nunits + kPD - 1) / kPD * kPD;
+  for (int u0 = 0; u0 < nu; u0 += kPD) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 v = {0, 0, 0, 0};
-      if (k_ok) v = *(const u32x4 *)(s_a + r * ld + k + 8 * j);
-      acc = mfma16x16x32(__builtin_bit_cast(f16x8, v), dequant8(wd[j], j < 2 ? b0 : b1), acc);
+    for (int d = 0; d < kPD; ++d) {
+      const int u = u0 + d;
+      load_a(u + kPD, av[d]);
+      const uint16_t *abuf = s_a[u & 1];
+      BlockScale bs[NT][2];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        bs[i][0] = decode_block_scale(sbuf[d][i] & 0xFF);
+        bs[i][1] = decode_block_scale(sbuf[d][i] >> 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f16x8 b[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) b[i] = dequant8(wbuf[d][i][j], bs[i][j >> 1]);
+#pragma unroll
+        for (int q = 0; q < MSUB; ++q) {
+          const f16x8 a = __builtin_bit_cast(
+              f16x8, *(const u32x4 *)(abuf + (q * kBM + r) * kLdsRow + 32 * g + 8 * j));
+#pragma unroll
+          for (int i = 0; i < NT; ++i) acc[q][i] = mfma16x16x32(a, b[i], acc[q][i]);
+        }
+      }
+      load_w(u + kPD, wbuf[d], sbuf[d]);
+      store_a((u + 1) & 1, av[(d + 1) % kPD]);
+      __syncthreads();
     }
   }
-  const float gd = down.global[e];
+
+  // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
+  const int e_global = e;
+  if (GATED) {
+    const float gg = w0.global[e_global], gu = w1.global[e_global];
+    const int col = (blockIdx.x * 4 + wave) * 16 + r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = 4 * g + j;
-    if (m < mrows) {
-      const float f = __builtin_ldexpf(1.0f, row_exponent(__uint_as_float(a_max[row0 + m])) - 14);
-      y[(size_t)(row0 + m) * H + n0 + r] = f32_to_bf16(acc[j] * (gd * f));
+    for (int q = 0; q < MSUB; ++q) {
+      float rmax[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = q * kBM + 4 * g + jj;
+        rmax[jj] = 0.0f;
+        if (m < mrows) {
+          const float f = s_rowscale[m];
+          const float G = acc[q][0][jj] * (gg * f), U = acc[q][1][jj] * (gu * f);
+          const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
+          out[(size_t)(row0 + m) * out_ld + col] = ab;
+          rmax[jj] = fabsf(bf16_to_f32(ab));
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) rmax[jj] = fmaxf(rmax[jj], __shfl_xor(rmax[jj], o, kWave));
+        const int m = q * kBM + 4 * g + jj;
+        if (r == 0 && m < mrows)
+          atomicMax(&a_max[row0 + m], __float_as_uint(rmax[jj]));
+      }
+    }
+  } else {
+    const float gd = w0.global[e_global];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int col = ((blockIdx.x * 4 + wave) * NT + i) * 16 + r;
+#pragma unroll
+      for (int q = 0; q < MSUB; ++q)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int m = q * kBM + 4 * g + jj;
+          if (m < mrows)
+            out[(size_t)(row0 + m) * out_ld + col] = f32_to_bf16(acc[q][i][jj] * (gd * s_rowscale[m]));
+        }
     }
   }
 }
@@ -317,7 +397,7 @@ int check_common(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I, cons
                  size_t ws_bytes) {
   if (!workspace) return MOE_ERR_NULL;
   if (T < 0 || top_k <= 0 || H <= 0 || I <= 0 || E <= 0) return MOE_ERR_SHAPE;
-  if (H % kCols || I % kCols || I > kMaxI || E > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOPK)
+  if (H % kCols || I % kCols || E > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOPK)
     return MOE_ERR_UNSUPPORTED;
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   if (ws_bytes < ws_layout(T, top_k, E, H, I).total) return MOE_ERR_WORKSPACE;
@@ -325,6 +405,35 @@ int check_common(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I, cons
 }
 
 bool tensor_null(const nvfp4_tensor *t) { return !t || !t->packed || !t->scales || !t->global; }
+
+// rows per tile: 16 x MSUB, from the mean bucket size (host-known shapes only)
+int choose_msub(int T, int top_k, int E) {
+  const long long P = (long long)T * top_k;
+  const long long buckets = P < E ? P : E;
+  const long long avg = buckets > 0 ? P / buckets : 0;
+  if (avg < 24) return 1;
+  if (avg < 64) return 2;
+  return 4;
+}
+
+template <int MSUB>
+int launch_gate_up(const Ws &w, const int32_t *offsets, const int32_t *sorted_pairs, int top_k,
+                   Nvfp4 g, Nvfp4 u, int H, int I, hipStream_t s) {
+  MOE_LAUNCH((k_expert_gemm<MSUB, 2, true>), dim3(I / kCols, w.L.max_tiles), dim3(kThreads), 0, s,
+             (const uint16_t *)w.x16, (const int32_t *)w.x_exp, w.a_max, offsets, sorted_pairs,
+             top_k, (const int32_t *)w.tiles, (const int32_t *)w.ntiles, g, u, H, I, w.a, I);
+  return MOE_OK;
+}
+
+template <int MSUB, int NT>
+int launch_down(const Ws &w, const int32_t *offsets, int top_k, Nvfp4 d, int H, int I,
+                uint16_t *y, hipStream_t s) {
+  MOE_LAUNCH((k_expert_gemm<MSUB, NT, false>), dim3(H / (kCols * NT), w.L.max_tiles),
+             dim3(kThreads), 0, s, (const uint16_t *)w.a, (const int32_t *)nullptr, w.a_max,
+             offsets, (const int32_t *)nullptr, top_k, (const int32_t *)w.tiles,
+             (const int32_t *)w.ntiles, d, d, I, H, y, H);
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -335,9 +444,10 @@ extern "C" int nvfp4_expert_prep(const uint16_t *x_expert, const int32_t *expert
   int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
+  const int bm = kBM * choose_msub(T, top_k, E);
   MOE_LAUNCH(k_prep, dim3((T + 3) / 4 + 1), dim3(kThreads), 0, (hipStream_t)stream,
-                     x_expert, T, H, expert_offsets, E, T * top_k, w.x16, w.x_exp, w.tiles,
-                     w.ntiles, w.a_max);
+             x_expert, T, H, expert_offsets, E, T * top_k, bm, w.x16, w.x_exp, w.tiles,
+             w.ntiles, w.a_max);
   return MOE_OK;
 }
 
@@ -349,15 +459,18 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
     return MOE_ERR_NULL;
   const int E = gate->E;
   if (!tensor_ok(gate, E, I, H) || !tensor_ok(up, E, I, H)) return MOE_ERR_SHAPE;
+  if (gate->layout != MOE_LAYOUT_TILED || up->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
   int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
   Nvfp4 g{gate->packed, gate->scales, gate->global};
   Nvfp4 u{up->packed, up->scales, up->global};
-  MOE_LAUNCH(k_gateup, dim3(I / kCols, w.L.max_tiles), dim3(kThreads), 0,
-                     (hipStream_t)stream, w.x16, w.x_exp, expert_offsets, sorted_pairs, top_k,
-                     w.tiles, w.ntiles, g, u, H, I, w.a, w.a_max);
-  return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  switch (choose_msub(T, top_k, E)) {
+    case 1: return launch_gate_up<1>(w, expert_offsets, sorted_pairs, top_k, g, u, H, I, s);
+    case 2: return launch_gate_up<2>(w, expert_offsets, sorted_pairs, top_k, g, u, H, I, s);
+    default: return launch_gate_up<4>(w, expert_offsets, sorted_pairs, top_k, g, u, H, I, s);
+  }
 }
 
 extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets,
@@ -367,15 +480,21 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
   if (tensor_null(down) || !expert_offsets || (T > 0 && !y_sorted)) return MOE_ERR_NULL;
   const int E = down->E;
   if (!tensor_ok(down, E, H, I)) return MOE_ERR_SHAPE;
+  if (down->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
   int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
   Nvfp4 d{down->packed, down->scales, down->global};
-  const size_t lds = (size_t)kBM * (I + 8) * 2;
-  MOE_LAUNCH(k_down, dim3(H / kCols, w.L.max_tiles), dim3(kThreads), lds,
-                     (hipStream_t)stream, w.a, w.a_max, expert_offsets, w.tiles, w.ntiles, d, I,
-                     H, y_sorted);
-  return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool two = H % (2 * kCols) == 0;
+  switch (choose_msub(T, top_k, E)) {
+    case 1: return two ? launch_down<1, 2>(w, expert_offsets, top_k, d, H, I, y_sorted, s)
+                       : launch_down<1, 1>(w, expert_offsets, top_k, d, H, I, y_sorted, s);
+    case 2: return two ? launch_down<2, 2>(w, expert_offsets, top_k, d, H, I, y_sorted, s)
+                       : launch_down<2, 1>(w, expert_offsets, top_k, d, H, I, y_sorted, s);
+    default: return two ? launch_down<4, 2>(w, expert_offsets, top_k, d, H, I, y_sorted, s)
+                        : launch_down<4, 1>(w, expert_offsets, top_k, d, H, I, y_sorted, s);
+  }
 }
 
 extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate,
@@ -390,6 +509,9 @@ extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *ga
   const int E = gate->E;
   if (!tensor_ok(gate, E, I, H) || !tensor_ok(up, E, I, H) || !tensor_ok(down, E, H, I))
     return MOE_ERR_SHAPE;
+  if (gate->layout != MOE_LAYOUT_TILED || up->layout != MOE_LAYOUT_TILED ||
+      down->layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_UNSUPPORTED;
   int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   st = nvfp4_expert_prep(x_expert, expert_offsets, T, top_k, E, H, I, workspace, ws_bytes, stream);

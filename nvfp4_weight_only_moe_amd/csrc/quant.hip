@@ -118,15 +118,47 @@ __global__ void k_write_global(const uint32_t *__restrict__ amax_bits, int E,
   if (e < E) global[e] = (float)((double)__uint_as_float(amax_bits[e]) / 2688.0);
 }
 
+// Byte offsets of element (n, k) (k % 8 == 0) of one expert tensor in the
+// tiled layout: its packed dword and its scale byte.  Lane l = 16 g + r of
+// unit u of row tile t holds row 16t + r, k = 128u + 32g .. +31.
+__device__ __forceinline__ void tiled_offsets(size_t n, size_t k, int K, size_t *pw, size_t *ps) {
+  const size_t t = n / 16, r = n % 16, u = k / 128, g = (k % 128) / 32, w = (k % 32) / 8;
+  const size_t lane = 16 * g + r;
+  *pw = t * 16 * (size_t)(K / 2) + u * 1024 + lane * 16 + w * 4;
+  *ps = t * (size_t)K + u * 128 + lane * 2 + (k % 32) / 16;
+}
+
+// canonical -> tiled, one thread per 16-byte lane slot
+__global__ __launch_bounds__(256) void k_repack(const uint8_t *__restrict__ packed,
+                                                const uint8_t *__restrict__ scales, int N, int K,
+                                                size_t nslots, uint8_t *__restrict__ tp,
+                                                uint8_t *__restrict__ ts) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // (expert, row, 32-k slice)
+  if (i >= nslots) return;
+  const size_t per_e = (size_t)N * (K / 32);
+  const size_t e = i / per_e, rem = i % per_e;
+  const size_t n = rem / (K / 32), k = (rem % (K / 32)) * 32;
+  size_t pw, ps;
+  tiled_offsets(n, k, K, &pw, &ps);
+  const uint8_t *src = packed + e * N * (K / 2) + n * (K / 2) + k / 2;
+  *(u32x4 *)(tp + e * N * (K / 2) + pw) = *(const u32x4 *)src;
+  const uint8_t *ssrc = scales + e * N * (K / 16) + n * (K / 16) + k / 16;
+  uint8_t *sdst = ts + e * N * (K / 16) + ps;
+  sdst[0] = ssrc[0];
+  sdst[1] = ssrc[1];
+}
+
 // one thread per 8 elements: the expert kernels' decode, widened to bf16 (exact)
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ packed,
                                                  const uint8_t *__restrict__ scales, int N, int K,
-                                                 uint16_t *__restrict__ out) {
+                                                 int tiled, uint16_t *__restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // dword index
   if (i >= (size_t)N * K / 8) return;
   const size_t n = i / (K / 8), k = (i % (K / 8)) * 8;
-  const uint32_t wv = *(const uint32_t *)(packed + n * (K / 2) + k / 2);
-  const BlockScale s = decode_block_scale(scales[n * (K / 16) + k / 16]);
+  size_t pw = n * (K / 2) + k / 2, ps = n * (K / 16) + k / 16;
+  if (tiled) tiled_offsets(n, k, K, &pw, &ps);
+  const uint32_t wv = *(const uint32_t *)(packed + pw);
+  const BlockScale s = decode_block_scale(scales[ps]);
   const f16x8 h = dequant8(wv, s);
   u32x4 o;
 #pragma unroll
@@ -158,15 +190,29 @@ extern "C" int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K
   return MOE_OK;
 }
 
+extern "C" int nvfp4_repack(const nvfp4_tensor *src, uint8_t *packed_tiled, uint8_t *scales_tiled,
+                            void *stream) {
+  using namespace moe;
+  if (!src || !src->packed || !src->scales || !packed_tiled || !scales_tiled) return MOE_ERR_NULL;
+  if (src->E <= 0 || src->N <= 0 || src->N % 16 || src->K <= 0 || src->K % 32) return MOE_ERR_SHAPE;
+  if (src->layout != MOE_LAYOUT_CANONICAL) return MOE_ERR_UNSUPPORTED;
+  const size_t nslots = (size_t)src->E * src->N * (src->K / 32);
+  MOE_LAUNCH(k_repack, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+             src->packed, src->scales, src->N, src->K, nslots, packed_tiled, scales_tiled);
+  return MOE_OK;
+}
+
 extern "C" int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream) {
   using namespace moe;
   if (!w || !out || !w->packed || !w->scales) return MOE_ERR_NULL;
   if (w->N <= 0 || w->K <= 0 || w->K % 32 || e < 0 || e >= w->E) return MOE_ERR_SHAPE;
+  if (w->layout != MOE_LAYOUT_CANONICAL && w->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
+  if (w->layout == MOE_LAYOUT_TILED && w->N % 16) return MOE_ERR_SHAPE;
   const size_t n8 = (size_t)w->N * w->K / 8;
   const uint8_t *p = w->packed + (size_t)e * w->N * (w->K / 2);
   const uint8_t *sc = w->scales + (size_t)e * w->N * (w->K / 16);
-  MOE_LAUNCH(k_dequant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, p, sc, w->N, w->K, out);
+  MOE_LAUNCH(k_dequant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, (hipStream_t)stream, p,
+             sc, w->N, w->K, (int)(w->layout == MOE_LAYOUT_TILED), out);
   return MOE_OK;
 }
 

@@ -14,15 +14,16 @@ def to_device_bf16(bits, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def quantize_stack_on_gpu(bits_stack, device="cuda", chunk=32):
-    """[E, N, K] bf16 bits -> Nvfp4Weights, uploaded and quantised in chunks."""
+def quantize_stack_on_gpu(bits_stack, device="cuda", chunk=32, tiled=True):
+    """[E, N, K] bf16 bits -> Nvfp4Weights, uploaded and quantised in chunks,
+    then (by default) repacked into the tiled layout the expert kernels read."""
     E, N, K = bits_stack.shape
     out = _lib.Nvfp4Weights.empty(E, N, K, device)
     for e0 in range(0, E, chunk):
         e1 = min(E, e0 + chunk)
         w = to_device_bf16(bits_stack[e0:e1], device)
         _lib.nvfp4_quantize(w, out.select(e0, e1))
-    return out
+    return _lib.nvfp4_repack(out) if tiled else out
 
 
 def router_to_device(p, device="cuda"):
@@ -44,7 +45,8 @@ def build_layer(layer=0, zipf=False, device="cuda", seed=S.SEED, h=S.H, i=S.I, e
             e1 = min(e, e0 + experts_chunk)
             S.expert_weights(layer, proj, range(e0, e1), seed, h, i, out=buf[:e1 - e0])
             _lib.nvfp4_quantize(to_device_bf16(buf[:e1 - e0], device), out.select(e0, e1))
-        stacks.append(out)
+        stacks.append(_lib.nvfp4_repack(out))
+        del out
     torch.cuda.synchronize()
     return MoeLayer(wr, sc, pes, bias, stacks[0], stacks[1], stacks[2], k)
 
@@ -64,7 +66,6 @@ def replicate_experts(layer, n, device="cuda"):
     used to time HBM streaming rather than cache hits."""
     reps = [layer]
     for _ in range(n - 1):
-        cp = [(_lib.Nvfp4Weights(w.packed.clone(), w.scales.clone(), w.global_scale.clone()))
-              for w in (layer.gate, layer.up, layer.down)]
+        cp = [w.clone() for w in (layer.gate, layer.up, layer.down)]
         reps.append(layer.with_experts(*cp))
     return reps

@@ -77,9 +77,9 @@ def test_bucket_rejects(L):
     assert L.moe_bucket(FAKE, -2, 8, 128, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -2
 
 
-def _tensor(E, N, K):
+def _tensor(E, N, K, layout=1):
     from nvfp4_weight_only_moe_amd._lib import Nvfp4TensorC
-    return Nvfp4TensorC(0x1000, 0x2000, 0x3000, E, N, K)
+    return Nvfp4TensorC(0x1000, 0x2000, 0x3000, E, N, K, layout)
 
 
 def test_expert_mlp_rejects(L):
@@ -102,6 +102,9 @@ def test_expert_mlp_rejects(L):
     nul = _tensor(E, I, H); nul.scales = None
     a = list(ok); a[1] = ctypes.byref(nul)
     assert L.nvfp4_expert_mlp(*a) == -1
+    canon = _tensor(E, I, H, layout=0)                # the kernels read the tiled layout
+    a = list(ok); a[2] = ctypes.byref(canon)
+    assert L.nvfp4_expert_mlp(*a) == -4
     # stage calls validate the same way
     assert L.nvfp4_expert_prep(FAKE, FAKE, T, k, E, H, I, FAKE, ws - 1, NULL) == -3
     assert L.nvfp4_expert_gate_up(ctypes.byref(g), ctypes.byref(d), FAKE, FAKE, T, k, H, I, FAKE, ws, NULL) == -2
@@ -116,6 +119,14 @@ def test_combine_quantize_dequant_reject(L):
     t = _tensor(2, 16, 64)
     assert L.nvfp4_dequant_bf16(ctypes.byref(t), 2, FAKE, NULL) == -2
     assert L.nvfp4_dequant_bf16(ctypes.byref(t), 0, NULL, NULL) == -1
+    t7 = _tensor(2, 16, 64, layout=7)
+    assert L.nvfp4_dequant_bf16(ctypes.byref(t7), 0, FAKE, NULL) == -4
+    t24 = _tensor(2, 24, 64, layout=1)
+    assert L.nvfp4_dequant_bf16(ctypes.byref(t24), 0, FAKE, NULL) == -2   # tiled needs N % 16
+    c = _tensor(2, 16, 64, layout=0)
+    assert L.nvfp4_repack(ctypes.byref(c), NULL, FAKE, NULL) == -1
+    assert L.nvfp4_repack(ctypes.byref(_tensor(2, 16, 64, layout=1)), FAKE, FAKE, NULL) == -4
+    assert L.nvfp4_repack(ctypes.byref(_tensor(2, 20, 64, layout=0)), FAKE, FAKE, NULL) == -2
 
 
 def test_workspace_sizes_cover_buffers(L):

@@ -77,8 +77,42 @@ def test_quantize_edge_tensors():
 
 
 # ------------------------------------------------------------------- decode
+def _tiled_reference(packed, scales):
+    """numpy statement of the tiled layout (header: MOE_LAYOUT_TILED)."""
+    E, N, K2 = packed.shape
+    K = 2 * K2
+    tp = np.zeros_like(packed).reshape(E, -1)
+    ts = np.zeros_like(scales).reshape(E, -1)
+    for n in range(N):
+        t, r = divmod(n, 16)
+        for k in range(0, K, 32):
+            u, g = divmod(k, 128)
+            g //= 32
+            lane = 16 * g + r
+            o = t * 16 * (K // 2) + u * 1024 + lane * 16
+            tp[:, o:o + 16] = packed[:, n, k // 2:k // 2 + 16]
+            so = t * K + u * 128 + lane * 2
+            ts[:, so:so + 2] = scales[:, n, k // 16:k // 16 + 2]
+    return tp.reshape(packed.shape), ts.reshape(scales.shape)
+
+
+@pytest.mark.parametrize("N,K", [(16, 96), (48, 704), (32, 2816)])
+def test_repack_matches_layout_definition(N, K):
+    rng = np.random.default_rng(N + K)
+    packed = rng.integers(0, 256, size=(2, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(2, N, K // 16), dtype=np.uint8)
+    w = moe.Nvfp4Weights(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(),
+                         torch.ones(2, dtype=torch.float32, device="cuda"))
+    t = moe.nvfp4_repack(w)
+    torch.cuda.synchronize()
+    rp, rs = _tiled_reference(packed, scales)
+    assert np.array_equal(t.packed.cpu().numpy(), rp)
+    assert np.array_equal(t.scales.cpu().numpy(), rs)
+
+
 @pytest.mark.parametrize("N,K", [(32, 64), (704, 2816), (2816, 704)])
-def test_dequant_bf16_bit_exact(N, K):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_dequant_bf16_bit_exact(N, K, tiled):
     rng = np.random.default_rng(K)
     E = 2
     packed = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
@@ -86,6 +120,8 @@ def test_dequant_bf16_bit_exact(N, K):
     scales[0, 0, :] = np.arange(K // 16) % 0x7F
     w = moe.Nvfp4Weights(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(),
                          torch.ones(E, dtype=torch.float32, device="cuda"))
+    if tiled:
+        w = moe.nvfp4_repack(w)
     out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     for e in range(E):
         moe.nvfp4_dequant_bf16(w, e, out)
