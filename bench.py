@@ -9,12 +9,14 @@ is one model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts,
 top-8, expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
 
 Timing: W warm-up steps, then K steps captured in one HIP graph and replayed
-once, bracketed by synchronisations (ms_per_step is wall clock / K).  Every
-stage call in the graph is bracketed by timing events recorded as graph nodes
-on the same stream, which gives the per-kernel durations used for the roofline
-of the dominant kernel (the gate/up GEMV/GEMM).  Consecutive steps read
-different, byte-identical copies of the expert weights so that each step
-streams its experts from HBM instead of the 256 MB last-level cache.
+once, bracketed by synchronisations (ms_per_step is wall clock / K).  In the
+graph the activation prep of each step runs on a parallel branch beside the
+router and the bucketing (it does not depend on them).  The per-kernel
+durations used for the roofline of the dominant kernel (the gate/up GEMV/GEMM)
+come from a second graph of the same K steps in which every stage call is a
+child graph bracketed by timing-event nodes on the launch stream.  Consecutive
+steps read different, byte-identical copies of the expert weights so that each
+step streams its experts from HBM instead of the 256 MB last-level cache.
 
 Prints one JSON line (rank 0).
 """
@@ -47,7 +49,7 @@ def parse():
     ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3 (1 or 8)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     return ap.parse_args()
 
@@ -63,7 +65,7 @@ class HipRuntime:
         h = ctypes.CDLL(path)
         vp, P = ctypes.c_void_p, ctypes.POINTER
         for name, args in {"hipEventCreate": [P(vp)], "hipEventRecordWithFlags": [vp, vp, ctypes.c_uint],
-                           "hipEventRecord": [vp, vp],
+                           "hipEventRecord": [vp, vp], "hipStreamWaitEvent": [vp, vp, ctypes.c_uint],
                            "hipEventElapsedTime": [P(ctypes.c_float), vp, vp],
                            "hipStreamBeginCapture": [vp, ctypes.c_int],
                            "hipStreamEndCapture": [vp, P(vp)],
@@ -91,6 +93,9 @@ class HipRuntime:
             self._ok(self.h.hipEventRecordWithFlags(ev, stream, 1), "hipEventRecordWithFlags")
         else:
             self._ok(self.h.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def wait(self, stream, ev):
+        self._ok(self.h.hipStreamWaitEvent(stream, ev, 0), "hipStreamWaitEvent")
 
     def elapsed(self, a, b):
         ms = ctypes.c_float()
@@ -196,19 +201,19 @@ def main():
     # events are external event-record nodes of the graph itself.
     n_layers = len(step_layers[0])
     hip = HipRuntime()
-    stream = torch.cuda.Stream()
-    hs = ctypes.c_void_p(stream.cuda_stream)
+    stream, side = torch.cuda.Stream(), torch.cuda.Stream()
+    hs, hside = ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side.cuda_stream)
+    from nvfp4_weight_only_moe_amd import _lib as C
 
-    def stage_calls(layer):
-        """The six stage calls of one block pass, each a closure on `stream`."""
-        from nvfp4_weight_only_moe_amd import _lib as C
+    def stage_calls(layer, prep_stream=None):
+        """The six stage calls of one block pass, in STAGES order."""
         return [
             lambda: C.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
                                 layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w,
                                 buf.topk_w_raw, buf.logits, stream),
             lambda: C.moe_bucket(buf.topk_idx, E, buf.expert_offsets, buf.sorted_pairs,
                                  buf.pair_rank, buf.bucket_ws, stream),
-            lambda: C.nvfp4_expert_prep(x, buf.expert_offsets, E, I, K, buf.ws, stream),
+            lambda: C.nvfp4_expert_prep(x, E, I, K, buf.ws, prep_stream or stream),
             lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
                                            buf.sorted_pairs, T, K, H, buf.ws, stream),
             lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K, buf.y_sorted,
@@ -216,51 +221,71 @@ def main():
             lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream),
         ]
 
-    calls = []
-    for s in range(args.steps):
-        for layer in step_layers[(args.warmup + s) % len(step_layers)]:
-            calls += stage_calls(layer)
-    bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
+    step_plan = [step_layers[(args.warmup + s) % len(step_layers)] for s in range(args.steps)]
+    fork_join = [(hip.event(), hip.event()) for _ in range(args.steps * n_layers)]
 
-    def run_eager():
-        hip.record(bounds[0], hs, False)
-        for call, e in zip(calls, bounds[1:]):
-            call()
-            hip.record(e, hs, False)
+    def queue_steps():
+        """K steps; per layer the prep runs on `side`, forked after the
+        previous layer's combine and joined before the gate/up GEMM."""
+        n = 0
+        for layers in step_plan:
+            for layer in layers:
+                route, bucket, prep, gate_up, down, combine = stage_calls(layer, side)
+                fork, join = fork_join[n]
+                n += 1
+                hip.record(fork, hs, False)
+                hip.wait(hside, fork)
+                prep()
+                hip.record(join, hside, False)
+                route()
+                bucket()
+                hip.wait(hs, join)
+                gate_up()
+                down()
+                combine()
 
-    mode, graph_exec = "eager", None
+    # ---- timed region: the K steps as one graph, replayed once
+    mode, graph = "eager", None
     torch.cuda.synchronize()
     if not args.eager:
         try:
-            graph_exec = hip.timed_chain(hs, calls, bounds)
-            mode = "hip_graph_with_event_nodes"
-        except Exception as exc:  # no event nodes: time eager launches
+            graph = hip.instantiate(hip.capture_graph(hs, queue_steps))
+            mode = "hip_graph (prep on a parallel branch)"
+            hip.launch(graph, hs)            # one untimed replay
+            stream.synchronize()
+        except Exception as exc:
             print(f"graph build failed ({exc}); timing eager launches", file=sys.stderr)
-            graph_exec = None
+            graph = None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graph_exec is not None:
-        hip.launch(graph_exec, hs)
+    if graph is not None:
+        hip.launch(graph, hs)
     else:
-        run_eager()
+        queue_steps()
     stream.synchronize()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the same K steps as a plain graph of kernel nodes only (no event nodes)
-    plain_ms = None
-    if graph_exec is not None:
-        def all_calls():
-            for call in calls:
-                call()
-        plain = hip.instantiate(hip.capture_graph(hs, all_calls))
-        hip.launch(plain, hs)                  # one untimed replay
-        stream.synchronize()
-        ta = time.perf_counter()
-        hip.launch(plain, hs)
-        stream.synchronize()
-        plain_ms = (time.perf_counter() - ta) * 1e3 / args.steps
+    # ---- per-stage durations: the same K steps with every stage call a
+    # child graph between timing-event nodes (serial order, one stream)
+    calls = []
+    for layers in step_plan:
+        for layer in layers:
+            calls += stage_calls(layer)
+    bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
+    if not args.eager:
+        chain = hip.timed_chain(hs, calls, bounds)
+        hip.launch(chain, hs)
+        events_mode = "hip_graph_with_event_nodes"
+    else:
+        hip.record(bounds[0], hs, False)
+        for call, e in zip(calls, bounds[1:]):
+            call()
+            hip.record(e, hs, False)
+        events_mode = "eager_with_events"
+    stream.synchronize()
+    torch.cuda.synchronize()
 
     stage_ms = {n: [] for n in STAGES}
     gpu_step_ms = []
@@ -309,8 +334,8 @@ def main():
                    "moe_intermediate": I, "layers": n_layers, "weight_replicas": replicas,
                    "timing": mode},
         "detail": {
-            "gpu_ms_per_step_events": float(np.mean(gpu_step_ms)),
-            "plain_graph_ms_per_step": plain_ms,
+            "stage_timing": events_mode,
+            "gpu_ms_per_step_with_event_nodes": float(np.mean(gpu_step_ms)),
             "stage_avg_us": stage_avg_us,
             "active_experts": U_total,
             "expert_weight_GBps": per_exp * U_total / step_s / 1e9,

@@ -110,7 +110,7 @@ typedef struct {
  * normalised activation (the per-token 1/rms factor is applied to the dot
  * product); softmax and renormalisation in fp32.
  * Errors: MOE_ERR_NULL for a required NULL; MOE_ERR_SHAPE for T < 0, H <= 0,
- * H % 32, E <= 0, top_k <= 0 or top_k > E; MOE_ERR_UNSUPPORTED for
+ * H % 64, E <= 0, top_k <= 0 or top_k > E; MOE_ERR_UNSUPPORTED for
  * E > MOE_MAX_EXPERTS, E % 16 or top_k > MOE_MAX_TOPK.  T == 0 is a no-op.
  */
 int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -164,8 +164,8 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, top_k <= 0, H or I <= 0,
  * descriptor shapes not [E][I][H], [E][I][H], [E][H][I] with one E);
  * MOE_ERR_UNSUPPORTED (H % 64, I % 64, E > MOE_MAX_EXPERTS,
- * top_k > MOE_MAX_TOPK, a descriptor not in MOE_LAYOUT_TILED);
- * MOE_ERR_WORKSPACE.
+ * top_k > MOE_MAX_TOPK, a descriptor not in MOE_LAYOUT_TILED, one expert's
+ * packed tensor or the activation copies past 2 GiB); MOE_ERR_WORKSPACE.
  */
 int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate, const nvfp4_tensor *up,
                      const nvfp4_tensor *down, const int32_t *expert_offsets,
@@ -175,19 +175,23 @@ size_t moe_workspace_bytes(int32_t T, int32_t top_k, int32_t E, int32_t H, int32
 
 /*
  * The three stages of nvfp4_expert_mlp as separate calls, for callers that
- * want to time or interleave them; queued in this order on one stream with the
- * same workspace they give the same bytes as nvfp4_expert_mlp.
- *   nvfp4_expert_prep:    per-row power-of-two rescale of x_expert to f16, the
- *                         (expert, row-block) tile list, clears the per-row
- *                         max of A.  Reads expert_offsets.
+ * want to time or overlap them; queued in this order with the same workspace
+ * they give the same bytes as nvfp4_expert_mlp.
+ *   nvfp4_expert_prep:    per-token power-of-two rescale of x_expert to f16
+ *                         (for few rows per expert stored transposed), and
+ *                         clears the per-row max of A.  It does not read the
+ *                         routing, so it may run concurrently with moe_route
+ *                         and moe_bucket (on another stream or graph branch),
+ *                         as long as it completes before nvfp4_expert_gate_up.
  *   nvfp4_expert_gate_up: A = gelu_tanh(X Wg^T) * (X Wu^T) for every sorted
  *                         row, bf16, kept in the workspace.
  *   nvfp4_expert_down:    y_sorted = A Wd^T.
- * Arguments, layouts and errors as for nvfp4_expert_mlp.
+ * Arguments, layouts and errors as for nvfp4_expert_mlp.  The workspace
+ * layout depends on (T, top_k, E, H, I) only, so all three calls must be given
+ * the same values.
  */
-int nvfp4_expert_prep(const uint16_t *x_expert, const int32_t *expert_offsets, int32_t T,
-                      int32_t top_k, int32_t E, int32_t H, int32_t I, void *workspace,
-                      size_t ws_bytes, void *stream);
+int nvfp4_expert_prep(const uint16_t *x_expert, int32_t T, int32_t top_k, int32_t E, int32_t H,
+                      int32_t I, void *workspace, size_t ws_bytes, void *stream);
 int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor *up,
                          const int32_t *expert_offsets, const int32_t *sorted_pairs, int32_t T,
                          int32_t top_k, int32_t H, int32_t I, void *workspace, size_t ws_bytes,

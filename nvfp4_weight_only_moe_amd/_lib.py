@@ -58,7 +58,7 @@ def lib(path=None):
         "moe_bucket": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_bucket_workspace_bytes": (sz, [i32, i32, i32]),
         "nvfp4_expert_mlp": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
-        "nvfp4_expert_prep": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]),
+        "nvfp4_expert_prep": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_gate_up": (ctypes.c_int, [P, P, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_down": (ctypes.c_int, [P, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
         "moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -185,11 +185,12 @@ def nvfp4_expert_mlp(x_expert, gate, up, down, expert_offsets, sorted_pairs, top
     _check("nvfp4_expert_mlp", st)
 
 
-def nvfp4_expert_prep(x_expert, expert_offsets, E, I, top_k, workspace, stream=None):
+def nvfp4_expert_prep(x_expert, E, I, top_k, workspace, stream=None):
+    """Stage 1 of the expert MLP; independent of the routing (may run beside
+    moe_route / moe_bucket), must complete before nvfp4_expert_gate_up."""
     T, H = x_expert.shape
-    st = lib().nvfp4_expert_prep(_ptr(x_expert, _B16, (T, H), "x_expert"),
-                                 _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"), T,
-                                 top_k, E, H, I, _ptr(workspace, None, None, "workspace"),
+    st = lib().nvfp4_expert_prep(_ptr(x_expert, _B16, (T, H), "x_expert"), T, top_k, E, H, I,
+                                 _ptr(workspace, None, None, "workspace"),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("nvfp4_expert_prep", st)
 

@@ -87,7 +87,7 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
         _lib.nvfp4_expert_mlp(xe, layer.gate, layer.up, layer.down, buf.expert_offsets,
                               buf.sorted_pairs, layer.top_k, buf.y_sorted, buf.ws, stream)
     else:
-        _lib.nvfp4_expert_prep(xe, buf.expert_offsets, layer.E, layer.I, layer.top_k, buf.ws, stream)
+        _lib.nvfp4_expert_prep(xe, layer.E, layer.I, layer.top_k, buf.ws, stream)
         mark("prep")
         _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs,
                                   buf.T, layer.top_k, layer.H, buf.ws, stream)

@@ -29,39 +29,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// ---- NVFP4 block-scale decode --------------------------------------------
-// An E4M3 block scale s is split as s = 2^E * m with m in [1, 2) (sign on m):
-// the power of two rides in the hardware FP4 conversion (which uses only the
-// exponent of its f32 scale operand), m is applied with one packed f16
-// multiply.  E2M1 x 2^E and its product with m are exact in f16.
-struct BlockScale {
-  float pow2;   // 2^E as f32 (exponent bits only); 0 for a zero scale
-  f16x2 mant;   // (m, m) as f16
-};
+// ---- NVFP4 decode ----------------------------------------------------------
+// E2M1 x E4M3 products have at most 6 significant bits and lie in
+// [2^-10, 2688]: exact in f16.  So a block decodes as: hardware FP4 -> f16
+// conversion of the E2M1 codes (scale operand 1.0), times the E4M3 block scale
+// converted to f16 by the hardware FP8 conversion, in one packed f16 multiply.
 
-__device__ __forceinline__ BlockScale decode_block_scale(uint32_t code) {
-  float s = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);  // OCP E4M3 -> f32, exact
-  uint32_t b = __float_as_uint(s);
-  BlockScale r;
-  r.pow2 = __uint_as_float(b & 0x7F800000u);
-  uint16_t m16 = (uint16_t)(((b >> 16) & 0x8000u) | 0x3C00u | ((b & 0x007FFFFFu) >> 13));
-  f16 m = __builtin_bit_cast(f16, m16);
-  r.mant = f16x2{m, m};
-  return r;
+// Two E4M3 block-scale codes (bits 0..7 and 8..15) -> (s0, s1) in f16, exact.
+__device__ __forceinline__ f16x2 block_scales_f16(uint32_t two_codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_codes, 1.0f, false);
 }
 
-// 8 E2M1 codes (one dword, element 0 in the low nibble) times a block scale
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times block scale s
 // -> 8 f16 in MFMA operand order.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, const BlockScale &s) {
-  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 0);
-  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 1);
-  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 2);
-  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 3);
-  a *= s.mant;
-  b *= s.mant;
-  c *= s.mant;
-  d *= s.mant;
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ---- buffer loads ------------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): a load at a byte offset at
+// or beyond `bytes` returns zeros (hardware range check), which is how lanes
+// past the end of a tensor or tile read zeros without a select.
+constexpr uint32_t kOOB = 0x80000000u;  // an offset outside every buffer used here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// streamed once: non-temporal
+__device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 // C[16x16] += A[16x32] * B[32x16]; lane l holds A[l%16][8(l/16)+i],

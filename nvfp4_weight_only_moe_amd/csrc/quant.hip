@@ -158,8 +158,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ pac
   size_t pw = n * (K / 2) + k / 2, ps = n * (K / 16) + k / 16;
   if (tiled) tiled_offsets(n, k, K, &pw, &ps);
   const uint32_t wv = *(const uint32_t *)(packed + pw);
-  const BlockScale s = decode_block_scale(scales[ps]);
-  const f16x8 h = dequant8(wv, s);
+  const f16x8 h = dequant8(wv, block_scales_f16(scales[ps])[0]);
   u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q)

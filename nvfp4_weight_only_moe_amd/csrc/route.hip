@@ -62,138 +62,177 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---- few tokens: 16 experts per workgroup, 8 waves split K, MT x 16 tokens
-constexpr int kNarrowWaves = 8;
+// ---- few tokens (T <= 64): plain fp32 FMAs.  x*scale*W is a product of
+// three bf16 values, at most 24 significant bits: exact in fp32, so fma()
+// adds exact products with one rounding each, as the MFMA path does.  A
+// workgroup owns one expert; each wave keeps scale*W of the whole row in
+// registers (exact) and takes up to 16 tokens; every load is a coalesced
+// 16-byte-per-lane read along a row.
+constexpr int kFewMaxV = 8;  // 16-byte vectors per lane: H <= 64 * 8 * kFewMaxV
 
-template <int MT>
-__global__ __launch_bounds__(kNarrowWaves * 64) void k_route_logits_narrow(
+template <int NV>  // 16-byte vectors per lane: lane holds k = (v*64 + lane)*8 .. +7
+__global__ __launch_bounds__(256) void k_route_logits_few(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
     float eps, float *__restrict__ logits) {
-  __shared__ f32x4 s_acc[kNarrowWaves][MT][64];
-  __shared__ float s_ss[kNarrowWaves][MT * 16];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * 16;
-  const uint16_t *wrow = w + (size_t)(e0 + r) * H;
-  f32x4 acc[MT];
-  float ss[MT];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // scale*W of this lane's K elements (exact in fp32); lanes past H hold 0
+  float sw[NV * 8];
+  int koff[NV];
 #pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    acc[q] = f32x4{0, 0, 0, 0};
-    ss[q] = 0.0f;
-  }
-  // k-steps of 32 are dealt to the waves round-robin; each lane issues the
-  // loads of kBatch steps before using any of them
-  constexpr int kBatch = 4;
-  const int nsteps = H / 32;
-  for (int ks0 = wave; ks0 < nsteps; ks0 += kNarrowWaves * kBatch) {
-    u32x4 wv[kBatch], sv[kBatch], xv[kBatch][MT];
+  for (int v = 0; v < NV; ++v) {
+    const int k = (v * 64 + lane) * 8;
+    const bool ok = k < H;
+    koff[v] = ok ? k : 0;
+    const u32x4 wv = *(const u32x4 *)(w + (size_t)e * H + koff[v]);
+    const u32x4 sv = *(const u32x4 *)(scale + koff[v]);
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int ks = ks0 + b * kNarrowWaves;
-      const int k = ks * 32 + 8 * g;
-      wv[b] = sv[b] = u32x4{0, 0, 0, 0};
-      if (ks < nsteps) {
-        wv[b] = *(const u32x4 *)(wrow + k);
-        sv[b] = *(const u32x4 *)(scale + k);
-      }
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int t = q * 16 + r;
-        xv[b][q] = u32x4{0, 0, 0, 0};
-        if (ks < nsteps && t < T) xv[b][q] = *(const u32x4 *)(x + (size_t)t * H + k);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      if (ks0 + b * kNarrowWaves < nsteps) {  // uniform across the wave
-        bf16x8 bh, bl;
-        split_products(wv[b], sv[b], bh, bl);
-#pragma unroll
-        for (int q = 0; q < MT; ++q) {
-          ss[q] += sumsq8(xv[b][q]);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, xv[b][q]);
-          acc[q] = mfma_bf16(a, bh, acc[q]);
-          acc[q] = mfma_bf16(a, bl, acc[q]);
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = __uint_as_float(wv[i] << 16) * __uint_as_float(sv[i] << 16);
+      const float p1 = __uint_as_float(wv[i] & 0xFFFF0000u) * __uint_as_float(sv[i] & 0xFFFF0000u);
+      sw[v * 8 + 2 * i] = ok ? p0 : 0.0f;
+      sw[v * 8 + 2 * i + 1] = ok ? p1 : 0.0f;
     }
   }
-#pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    s_acc[wave][q][lane] = acc[q];
-    float v = ss[q];  // x^2 of token q*16 + r over this lane's k
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    if (g == 0) s_ss[wave][q * 16 + r] = v;
-  }
-  __syncthreads();
-  if (wave != 0) return;
   const float hs = 1.0f / sqrtf((float)H);
-  const float b = bias ? bias[e0 + r] : 0.0f;
+  const float b = bias ? bias[e] : 0.0f;
+  // workgroup (e, y) takes tokens 16y .. 16y+15, 4 per wave; the rows of the
+  // wave's tokens are all requested before any is used
+  constexpr int kTPW = 4;
+  const int t0 = blockIdx.y * 16 + wave * kTPW;
+  u32x4 xv[kTPW][NV];
 #pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    f32x4 tot = {0, 0, 0, 0};
-    for (int v = 0; v < kNarrowWaves; ++v) tot += s_acc[v][q][lane];
+  for (int q = 0; q < kTPW; ++q) {
+    const int t = min(t0 + q, T - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = q * 16 + 4 * g + j, t = m;
-      if (t < T) {
-        float sq = 0.0f;
-        for (int v = 0; v < kNarrowWaves; ++v) sq += s_ss[v][m];
-        const float inv = 1.0f / sqrtf(sq / (float)H + eps) * hs;
-        logits[(size_t)t * E + e0 + r] = tot[j] * inv + b;
+    for (int v = 0; v < NV; ++v) xv[q][v] = *(const u32x4 *)(x + (size_t)t * H + koff[v]);
+  }
+  float dot[kTPW], ss[kTPW];
+#pragma unroll
+  for (int q = 0; q < kTPW; ++q) {
+    dot[q] = ss[q] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const bool ok = (v * 64 + lane) * 8 < H;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = ok ? __uint_as_float(xv[q][v][i] << 16) : 0.0f;
+        const float hi = ok ? __uint_as_float(xv[q][v][i] & 0xFFFF0000u) : 0.0f;
+        dot[q] = fmaf(lo, sw[v * 8 + 2 * i], dot[q]);
+        dot[q] = fmaf(hi, sw[v * 8 + 2 * i + 1], dot[q]);
+        ss[q] = fmaf(lo, lo, ss[q]);
+        ss[q] = fmaf(hi, hi, ss[q]);
       }
     }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int q = 0; q < kTPW; ++q) {
+      dot[q] += __shfl_xor(dot[q], o, kWave);
+      ss[q] += __shfl_xor(ss[q], o, kWave);
+    }
+  if (lane < kTPW) {
+    float d = dot[0], q2 = ss[0];
+#pragma unroll
+    for (int q = 1; q < kTPW; ++q)
+      if (lane == q) {
+        d = dot[q];
+        q2 = ss[q];
+      }
+    const int t = t0 + lane;
+    if (t < T) logits[(size_t)t * E + e] = d * (1.0f / sqrtf(q2 / (float)H + eps) * hs) + b;
   }
 }
 
-// ---- many tokens: 64 tokens per workgroup, NF*16 experts per wave
-template <int NF>
+// ---- many tokens: 64 tokens x 128 experts per workgroup (16 x 128 per wave),
+// K in chunks of 64 staged in LDS by coalesced row loads.  The split is taken
+// on the activation side when staging: x*scale = hi + lo (both bf16, exact).
+constexpr int kWideKC = 64;
+constexpr int kWideTok = 64;
+constexpr int kWideExp = 128;
+constexpr int kWideLd = kWideKC + 8;  // bf16 per LDS row (padding spreads banks)
+
 __global__ __launch_bounds__(256) void k_route_logits_wide(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
     float eps, float *__restrict__ logits) {
-  __shared__ float s_inv[4][16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_xh[kWideTok * kWideLd];
+  __shared__ __attribute__((aligned(16))) uint16_t s_xl[kWideTok * kWideLd];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kWideExp * kWideLd];
+  __shared__ float s_ss[kWideTok];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * NF * 16;
-  const int t0 = blockIdx.y * 64 + wave * 16;
-  const int ta = t0 + r;
-  const bool a_ok = ta < T;
-  const uint16_t *xa = x + (size_t)(a_ok ? ta : 0) * H;
-  f32x4 acc[NF];
+  const int e0 = blockIdx.x * kWideExp;
+  const int t0 = blockIdx.y * kWideTok;
+  // staging map: 8 threads per row (8 x 16 B = one 64-element row chunk)
+  const int srow = tid >> 3, scol = (tid & 7) * 8;  // rows srow, srow+32 (x) / +32.. (w)
+  f32x4 acc[8];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0, 0, 0, 0};
-  float ss = 0.0f;
-  for (int kk = 0; kk < H; kk += 32) {
-    const int k = kk + 8 * g;
-    u32x4 xv = {0, 0, 0, 0};
-    if (a_ok) xv = *(const u32x4 *)(xa + k);
-    const u32x4 sv = *(const u32x4 *)(scale + k);
-    ss += sumsq8(xv);
-    bf16x8 ah, al;
-    split_products(xv, sv, ah, al);
+  for (int f = 0; f < 8; ++f) acc[f] = f32x4{0, 0, 0, 0};
+  float ss[2] = {0.0f, 0.0f};
+  for (int kc = 0; kc < H; kc += kWideKC) {
+    // loads (coalesced rows), then split, then LDS
+    const u32x4 sv = *(const u32x4 *)(scale + kc + scol);
+    u32x4 xv[2], wv[4];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4 *)(w + (size_t)(e0 + f * 16 + r) * H + k));
-      acc[f] = mfma_bf16(ah, b, acc[f]);
-      acc[f] = mfma_bf16(al, b, acc[f]);
+    for (int h = 0; h < 2; ++h) {
+      const int t = t0 + srow + 32 * h;
+      xv[h] = u32x4{0, 0, 0, 0};
+      if (t < T) xv[h] = *(const u32x4 *)(x + (size_t)t * H + kc + scol);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int ee = e0 + srow + 32 * h;
+      wv[h] = u32x4{0, 0, 0, 0};
+      if (ee < E) wv[h] = *(const u32x4 *)(w + (size_t)ee * H + kc + scol);
+    }
+    __syncthreads();  // previous chunk fully consumed
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ss[h] += sumsq8(xv[h]);
+      bf16x8 hi, lo;
+      split_products(xv[h], sv, hi, lo);
+      *(bf16x8 *)(s_xh + (srow + 32 * h) * kWideLd + scol) = hi;
+      *(bf16x8 *)(s_xl + (srow + 32 * h) * kWideLd + scol) = lo;
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) *(u32x4 *)(s_w + (srow + 32 * h) * kWideLd + scol) = wv[h];
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kWideKC; ks += 32) {
+      const int k = ks + 8 * g;
+      const bf16x8 ah = *(const bf16x8 *)(s_xh + (wave * 16 + r) * kWideLd + k);
+      const bf16x8 al = *(const bf16x8 *)(s_xl + (wave * 16 + r) * kWideLd + k);
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        const bf16x8 b = *(const bf16x8 *)(s_w + (f * 16 + r) * kWideLd + k);
+        acc[f] = mfma_bf16(ah, b, acc[f]);
+        acc[f] = mfma_bf16(al, b, acc[f]);
+      }
     }
   }
-  ss += __shfl_xor(ss, 16, kWave);
-  ss += __shfl_xor(ss, 32, kWave);
-  if (g == 0) s_inv[wave][r] = 1.0f / sqrtf(ss / (float)H + eps) * (1.0f / sqrtf((float)H));
-  __syncthreads();
+  // sum of squares per token: 8 threads per row
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
+  for (int h = 0; h < 2; ++h) {
+    float v = ss[h];
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave);
+    if ((tid & 7) == 0) s_ss[srow + 32 * h] = v;
+  }
+  __syncthreads();
+  const float hs = 1.0f / sqrtf((float)H);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
     const int e = e0 + f * 16 + r;
+    if (e >= E) continue;
     const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 4 * g + j;
-      if (t < T) logits[(size_t)t * E + e] = acc[f][j] * s_inv[wave][4 * g + j] + b;
+      const int m = wave * 16 + 4 * g + j, t = t0 + m;
+      if (t < T) logits[(size_t)t * E + e] = acc[f][j] * (1.0f / sqrtf(s_ss[m] / (float)H + eps) * hs) + b;
     }
   }
 }
@@ -289,28 +328,25 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
   using namespace moe;
   if (!w_router || !router_scale || !per_expert_scale) return MOE_ERR_NULL;
   if (T > 0 && (!x || !topk_idx || !topk_w || !logits)) return MOE_ERR_NULL;
-  if (T < 0 || H <= 0 || H % 32 || E <= 0 || top_k <= 0 || top_k > E) return MOE_ERR_SHAPE;
+  if (T < 0 || H <= 0 || H % 64 || E <= 0 || top_k <= 0 || top_k > E) return MOE_ERR_SHAPE;
   if (E > MOE_MAX_EXPERTS || E % 16 || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (T <= 64) {
-    const dim3 grid(E / 16), block(kNarrowWaves * 64);
-    const int mt = (T + 15) / 16;
-    if (mt == 1)
-      MOE_LAUNCH(k_route_logits_narrow<1>, grid, block, 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
-    else if (mt == 2)
-      MOE_LAUNCH(k_route_logits_narrow<2>, grid, block, 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
-    else
-      MOE_LAUNCH(k_route_logits_narrow<4>, grid, block, 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+  const int nv = (H + 511) / 512;
+  if (T <= 64 && nv <= kFewMaxV) {
+    switch (nv) {
+#define MOE_FEW(NV)                                                                          \
+  case NV:                                                                                   \
+    MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, router_scale, \
+               logit_bias, T, H, E, eps, logits);                                            \
+    break;
+      MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
+      default: MOE_FEW(8)
+#undef MOE_FEW
+    }
   } else {
-    // experts per workgroup: all of them (NF = E/16 up to 8) unless that
-    // leaves too few workgroups
-    const int tg = (T + 63) / 64;
-    const bool wide8 = (E % 128 == 0) && tg >= 128;
-    if (wide8)
-      MOE_LAUNCH(k_route_logits_wide<8>, dim3(E / 128, tg), dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
-    else
-      MOE_LAUNCH(k_route_logits_wide<1>, dim3(E / 16, tg), dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+    MOE_LAUNCH(k_route_logits_wide, dim3((E + kWideExp - 1) / kWideExp, (T + kWideTok - 1) / kWideTok),
+               dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
   }
   MOE_LAUNCH(k_route_select, dim3((T + 3) / 4), dim3(256), 0, s, logits, per_expert_scale,
                      T, E, top_k, topk_idx, topk_w, topk_w_raw);

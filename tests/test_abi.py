@@ -56,7 +56,7 @@ def test_route_rejects(L):
     a = list(args); a[13] = NULL
     assert L.moe_route(*a) == -1                      # logits required
     a = list(args); a[6] = 2800
-    assert L.moe_route(*a) == -2                      # H % 32
+    assert L.moe_route(*a) == -2                      # H % 64
     a = list(args); a[8] = 129
     assert L.moe_route(*a) == -2                      # top_k > E
     a = list(args); a[7] = 120
@@ -106,7 +106,10 @@ def test_expert_mlp_rejects(L):
     a = list(ok); a[2] = ctypes.byref(canon)
     assert L.nvfp4_expert_mlp(*a) == -4
     # stage calls validate the same way
-    assert L.nvfp4_expert_prep(FAKE, FAKE, T, k, E, H, I, FAKE, ws - 1, NULL) == -3
+    assert L.nvfp4_expert_prep(FAKE, T, k, E, H, I, FAKE, ws - 1, NULL) == -3
+    assert L.nvfp4_expert_prep(NULL, T, k, E, H, I, FAKE, ws, NULL) == -1
+    assert L.nvfp4_expert_prep(FAKE, T, k, E, H, I, NULL, ws, NULL) == -1
+    assert L.nvfp4_expert_prep(FAKE, T, k, E, H + 32, I, FAKE, ws, NULL) == -4
     assert L.nvfp4_expert_gate_up(ctypes.byref(g), ctypes.byref(d), FAKE, FAKE, T, k, H, I, FAKE, ws, NULL) == -2
     assert L.nvfp4_expert_down(ctypes.byref(d), FAKE, T, k, H, I, NULL, FAKE, ws, NULL) == -1
 

@@ -175,7 +175,8 @@ def test_route_model_shape(T, zipf, outliers):
 
 
 def test_route_small_odd_shapes():
-    for (t, h, e, k) in [(1, 32, 16, 1), (3, 96, 16, 2), (5, 64, 32, 4), (7, 2816, 256, 16)]:
+    for (t, h, e, k) in [(1, 64, 16, 1), (3, 192, 16, 2), (5, 64, 32, 4), (7, 2816, 256, 16),
+                         (65, 128, 32, 4), (100, 2816, 256, 8)]:
         c = S.small_case(t + e, t, h, 64, e, k, zipf=(t == 5))
         idx, w, w_raw, lg = _route_gpu(c["x"], c["router"], k, e)
         r = router_f64(c["router"])
@@ -252,8 +253,13 @@ def _expert_case(T, k, E, H, I, seed):
     return c, idx
 
 
-@pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (5, 2, 8, 128, 64), (37, 4, 8, 192, 128),
-                                       (300, 2, 4, 256, 64)])
+# Shapes chosen to reach every kernel variant: GEMV mode with 8-row tiles
+# (1 and 2 row groups, experts split over several tiles), GEMV mode with
+# 16-row tiles (1 to 4 row groups), and the LDS-tiled GEMM with 32- and
+# 64-row tiles; odd H / I multiples of 64 leave partial K units.
+@pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (5, 2, 8, 128, 64), (16, 2, 8, 128, 64),
+                                       (24, 4, 16, 256, 128), (37, 4, 8, 192, 128),
+                                       (100, 4, 8, 128, 64), (300, 2, 4, 256, 64)])
 def test_expert_mlp_small(T, k, E, H, I):
     c, idx = _expert_case(T, k, E, H, I, seed=T)
     layer = W.build_small_layer(c, k)
