@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter scaling reference)")
     return ap.parse_args()
 
 
@@ -157,6 +159,9 @@ def expert_bytes_per_expert(H, I):
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
               "multi-GPU path is a design note, not part of this build.", file=sys.stderr)
@@ -313,7 +318,8 @@ def main():
     per_exp = expert_bytes_per_expert(H, I)
     gu_w_bytes = 2 * (H * I // 2 + H * I // 16 + 4)
     step_s = ms_per_step / 1e3
-    gate_up_alg_bytes = gu_w_bytes * U + T * H * 2 + P * I * 2     # per launch (last layer)
+    U_mean = U_total / n_layers                 # active experts per gate/up launch
+    gate_up_alg_bytes = gu_w_bytes * U_mean + T * H * 2 + P * I * 2     # per launch
     gu_us = stage_avg_us["gate_up"]
     achieved_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9
     expert_flops = 2.0 * P * 3 * I * H * n_layers
@@ -344,27 +350,79 @@ def main():
             "max_over_mean_bucket": float(counts.max() / max(counts.mean(), 1e-9)),
             "setup_s": t_setup,
         },
-        "roofline": {
-            "kernel": "k_gateup (nvfp4_expert_gate_up)",
-            "bound": "hbm",
-            "achieved": achieved_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
-            "alg_bytes_per_launch": gate_up_alg_bytes,
-            "avg_launch_us": gu_us,
-        },
     }
+    # Roofline of the dominant kernel, the gate/up projection: the HBM one for
+    # decode (its algorithmic bytes: the active experts' gate and up tensors,
+    # the f16 activations and A written), the f16 MFMA one for prefill (its
+    # algorithmic flops 2 P 2 I H); the other one is reported beside it.
+    gu_kernel = gate_up_kernel_name(T, K, E)
+    hbm = {"kernel": gu_kernel, "bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
+           "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
+           "traffic": profiled_traffic(wl["name"], gu_kernel),
+           "alg_bytes_per_launch": gate_up_alg_bytes, "avg_launch_us": gu_us,
+           "units": f"{U_mean:g} active experts x {gu_w_bytes} B + {T} x {H} x 2 B + {P} x {I} x 2 B"}
+    gu_flops = 2.0 * P * 2 * I * H
+    tflops = gu_flops / (gu_us * 1e-6) / 1e12
+    mfma = {"kernel": gu_kernel, "bound": "mfma", "achieved": tflops, "peak": F16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / F16_MFMA_PEAK_TFLOPS, "traffic": None,
+            "alg_flops_per_launch": gu_flops, "avg_launch_us": gu_us}
     if args.workload in (2, 4):
-        # prefill: the expert GEMMs are MFMA-bound; report both rooflines
-        gu_flops = 2.0 * P * 2 * I * H
-        out["roofline_mfma"] = {"bound": "mfma", "achieved": gu_flops / (gu_us * 1e-6) / 1e12,
-                                "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": gu_flops / (gu_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS}
+        out["roofline"], out["roofline_hbm"] = mfma, hbm
+    else:
+        out["roofline"], out["roofline_mfma"] = hbm, mfma
     if not args.no_cpu_baseline and args.workload != 3:
         out["cpu_baseline"] = cpu_baseline(args, wl, T)
     print(json.dumps(out), flush=True)
+
+
+def gate_up_kernel_name(T, K, E):
+    """The kernel nvfp4_expert_gate_up launches for this shape (the dispatch
+    rule of the library: few rows per expert -> GEMV mode)."""
+    P = T * K
+    avg = P // max(1, min(P, E))
+    if avg < 24:
+        return f"k_expert_gemv<{8 if P <= 4 * E else 16}, 2, true>"
+    return f"k_expert_gemm<{2 if avg < 64 else 4}, 2, true>"
+
+
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or when the kernel
+    source has changed since the counters were taken (the summary records
+    the sha256 of the source file it was taken with)."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", f"hbm_traffic__{workload}.txt")
+    src = os.path.join(HERE, "nvfp4_weight_only_moe_amd", "csrc", "mlp.hip")
+    if not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != digest or rec.get("kernel") != kernel:
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_reference(mib):
+    """A plain device-to-device copy of `mib` MiB (three launches), the
+    reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to
+    bytes: each launch reads and writes exactly mib MiB."""
+    import torch
+    torch.cuda.set_device(0)
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(args, wl, T):

@@ -480,44 +480,55 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   for (int q = 0; q < NG; ++q)
 #pragma unroll
     for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
-  GemvUnit<NG, NW> buf[kGemvPD];
+  auto compute = [&](const GemvUnit<NG, NW> &c) {
+    f16x8 a[NG];
 #pragma unroll
-  for (int d = 0; d < kGemvPD; ++d) load(d, buf[d]);
-  const int nu = (nunits + kGemvPD - 1) / kGemvPD * kGemvPD;
-  for (int u0 = 0; u0 < nu; u0 += kGemvPD) {
+    for (int q = 0; q < NG; ++q) {
+      if (GATED) {
+        a[q] = __builtin_bit_cast(f16x8, c.a[q]);
+      } else {  // bf16 -> f16 with the row's power of two (exact)
 #pragma unroll
-    for (int d = 0; d < kGemvPD; ++d) {
-      GemvUnit<NG, NW> &c = buf[d];
-      f16x8 a[NG];
+        for (int t = 0; t < 4; ++t) {
+          a[q][2 * t] = (f16)(__uint_as_float(c.a[q][t] << 16) * a_scale[q]);
+          a[q][2 * t + 1] = (f16)(__uint_as_float(c.a[q][t] & 0xFFFF0000u) * a_scale[q]);
+        }
+      }
+    }
+    f16x2 bs[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(c.s[i]);
+    const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 b[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) b[i] = dequant8(c.w[i][j], bs[i][j >> 1]);
 #pragma unroll
       for (int q = 0; q < NG; ++q) {
-        if (GATED) {
-          a[q] = __builtin_bit_cast(f16x8, c.a[q]);
-        } else {  // bf16 -> f16 with the row's power of two (exact)
+        const f16x8 aj = h == j ? a[q] : zero;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a[q][2 * t] = (f16)(__uint_as_float(c.a[q][t] << 16) * a_scale[q]);
-            a[q][2 * t + 1] = (f16)(__uint_as_float(c.a[q][t] & 0xFFFF0000u) * a_scale[q]);
-          }
-        }
+        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(aj, b[i], acc[q][i]);
       }
-      f16x2 bs[NW];
+    }
+  };
+
+  // ---- K loop: kGemvPD + 1 register buffers.  The loads of unit u + kGemvPD
+  // are issued before unit u is multiplied (a scheduling barrier keeps them
+  // there), so kGemvPD units stay in flight while a wave computes.  The unit
+  // count is rounded up to a multiple of the buffer count; the extra units
+  // read zeros through the buffer range check and add nothing.
+  constexpr int NB = kGemvPD + 1;
+  GemvUnit<NG, NW> buf[NB];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(c.s[i]);
-      const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int d = 0; d < kGemvPD; ++d) load(d, buf[d]);
+  const int nu = (nunits + NB - 1) / NB * NB;
+  for (int u0 = 0; u0 < nu; u0 += NB) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f16x8 b[NW];
-#pragma unroll
-        for (int i = 0; i < NW; ++i) b[i] = dequant8(c.w[i][j], bs[i][j >> 1]);
-#pragma unroll
-        for (int q = 0; q < NG; ++q) {
-          const f16x8 aj = h == j ? a[q] : zero;
-#pragma unroll
-          for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(aj, b[i], acc[q][i]);
-        }
-      }
-      load(u0 + d + kGemvPD, c);
+    for (int d = 0; d < NB; ++d) {
+      load(u0 + d + kGemvPD, buf[(d + kGemvPD) % NB]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
