@@ -48,17 +48,17 @@ struct Nvfp4 {
 };
 
 struct WsLayout {
-  size_t x_exp, a_max, x16, a, total;
+  size_t tiles, x_exp, a_max, x16, a, total;
   int max_tiles;
 };
 
-// rows per tile: 16 x MSUB, from the mean bucket size (host-known shapes only)
+// rows per tile: 16 x MSUB, from the mean bucket size (host-known shapes
+// only).  MSUB = 1 selects GEMV mode.
 int choose_msub(int T, int top_k, int E) {
   const long long P = (long long)T * top_k;
   const long long buckets = P < E ? P : E;
   const long long avg = buckets > 0 ? P / buckets : 0;
   if (avg < 24) return 1;
-  if (avg < 64) return 2;
   return 4;
 }
 
@@ -73,14 +73,16 @@ int tile_rows(int T, int top_k, int E) {
   return gemv_mode(T, top_k, E) ? gemv_rows(T, top_k, E) : kBM * choose_msub(T, top_k, E);
 }
 
-// Workspace: token exponents [T], per-row max of A [P], the f16 activations
-// [T][H], A [P][I] bf16.
+// Workspace: the GEMV-mode tile list [max_tiles] int4, token exponents [T],
+// per-row max of A [P], the f16 activations [T][H], A [P][I] bf16.
 WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
   WsLayout L;
   const size_t P = (size_t)T * top_k;
   const int bm = tile_rows(T, top_k, E);
   L.max_tiles = (int)((P + bm - 1) / bm + (size_t)(E < (int)P ? E : (int)P));
-  L.x_exp = 0;
+  const bool gemv = gemv_mode(T, top_k, E);
+  L.tiles = 0;
+  L.x_exp = L.tiles + (gemv ? moe_align_up((size_t)L.max_tiles * 16, 256) : 0);
   L.a_max = L.x_exp + moe_align_up((size_t)T * 4, 256);
   L.x16 = L.a_max + moe_align_up(P * 4, 256);
   L.a = L.x16 + moe_align_up((size_t)T * H * 2, 256);
@@ -90,40 +92,6 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
 }
 
 // ---------------------------------------------------------------- prep ----
-// Tile `tile` of the list "expert e contributes ceil(M_e / bm) tiles": one
-// wave-wide inclusive scan over the bucket sizes; the same answer in every
-// lane.  False past the last tile.
-__device__ bool find_tile(const int32_t *__restrict__ offsets, int E, int bm, int tile, int &e,
-                          int &m0) {
-  const int lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < E; base += kWave) {
-    const int ee = base + lane;
-    const int c = ee < E ? (offsets[ee + 1] - offsets[ee] + bm - 1) / bm : 0;
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += u;
-    }
-    // wave-uniform (scalar) values only in the control flow below, so that
-    // e and m0 stay scalar after the loop
-    const int total = carry + __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
-    if (tile < total) {
-      const bool hit = tile >= carry + incl - c && tile < carry + incl;
-      const unsigned long long mask = __ballot(hit);
-      const int src = __ffsll((long long)mask) - 1;
-      // the same in every lane: made scalar, so that the buffer resources
-      // built from e are uniform (no per-lane descriptor loop)
-      e = base + __builtin_amdgcn_readfirstlane(src);
-      m0 = __builtin_amdgcn_readfirstlane((tile - carry - __shfl(incl - c, src, kWave)) * bm);
-      return true;
-    }
-    carry = total;
-  }
-  return false;
-}
-
 // One wave per token: row maximum -> exponent -> f16 row scaled by
 // 2^(14 - exponent), row-major [T][H]; the other threads clear the per-row
 // maximum of A.
@@ -168,88 +136,149 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 }
 
 // ------------------------------------------------- grouped expert GEMM ----
-// One kernel template for both projections.  A workgroup (4 waves) owns one
-// tile of kBM*MSUB sorted rows of one expert and a slice of output columns;
-// each wave owns NT row tiles (16 weight rows each) of that slice: for the
-// gated projection NT = 2 (16 gate rows and the same 16 up rows), for down
-// NT row tiles of consecutive outputs.
+// Tiled mode (prefill).  A workgroup (4 waves) owns one block of 16*MSUB
+// sorted rows of one expert and 4*NP*16 output columns; each wave owns NP row
+// tiles of 16 outputs (gated: NP gate tiles and the same NP up tiles).
 //
-// K advances in units of 128.  Per unit, the activation tile [rows][128] is
+// K advances in units of 128.  Per unit the activation block [rows][128] is
 // staged once in LDS as f16 (double-buffered) and shared by the 4 waves; each
 // lane loads its 16 bytes of every weight row tile it owns (one contiguous
 // kilobyte per wave in the tiled layout), dequantises them in registers and
-// runs 4 x MSUB x NT MFMAs 16x16x32.  The weights of the next unit are loaded
-// while the current one is multiplied.
+// runs MSUB x NW x 4 MFMAs 16x16x32, so one LDS fragment feeds NW MFMAs and
+// one dequantised weight fragment feeds MSUB.  The weights of unit u+1 are
+// in flight while unit u is multiplied; the activations of unit u+2 while
+// unit u+1 is staged.  16-row blocks past the end of a partial block skip
+// their MFMAs (a workgroup-uniform branch).
+//
+// Order of the workgroups: a 1-D grid, a multiple of the 8 XCDs.  Hardware
+// hands workgroup b to XCD b % 8; b is mapped to the logical index
+// (b % 8) * (grid / 8) + b / 8 so that each XCD walks one contiguous range of
+// the logical order (expert, column block, row block).  The row blocks that
+// reuse a column block's weights then run side by side on one XCD and hit
+// its L2 instead of HBM.
 constexpr int kUnitK = 128;
-constexpr int kLdsRow = kUnitK + 8;  // f16 per LDS row (padding spreads banks)
-#ifndef MOE_GEMM_PD
-#define MOE_GEMM_PD 1
-#endif
-constexpr int kPD = MOE_GEMM_PD;     // units in flight per lane (weights and activations)
+constexpr int kXcds = 8;
 
-template <int MSUB, int NT, bool GATED>
-__global__ __launch_bounds__(kThreads) void k_expert_gemm(
-    const uint16_t *__restrict__ a_src,       // GATED: x16 [T][K] f16; else A [P][K] bf16
-    const int32_t *__restrict__ row_exp,      // GATED: x_exp [T];  else unused
-    uint32_t *__restrict__ a_max,             // GATED: row max of A (written); else read
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_pairs, int top_k,
-    int E, Nvfp4 w0, Nvfp4 w1,                // GATED: gate, up; else w0 = down
-    int K, int N, uint16_t *__restrict__ out, int out_ld) {
+// Logical block `L` of the order (expert e, column block cb, row block m):
+// expert e holds ceil(M_e / bm) * ncb consecutive blocks.  One wave-wide scan
+// (scalar results).  False past the last block.
+__device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int ncb, int L,
+                           int &e, int &m0, int &cb) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int base = 0; base < E; base += kWave) {
+    const int ee = base + lane;
+    const int c = ee < E ? (offsets[ee + 1] - offsets[ee] + bm - 1) / bm * ncb : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    const int total = carry + __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+    if (L < total) {
+      const bool hit = L >= carry + incl - c && L < carry + incl;
+      const unsigned long long mask = __ballot(hit);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)mask) - 1);
+      e = base + src;
+      const int rem = L - carry - __builtin_amdgcn_readfirstlane(__shfl(incl - c, src, kWave));
+      const int nblk = __builtin_amdgcn_readfirstlane(__shfl(c, src, kWave)) / ncb;
+      cb = rem / nblk;
+      m0 = (rem - cb * nblk) * bm;
+      return true;
+    }
+    carry = total;
+  }
+  return false;
+}
+
+// LDS layout of the activation block: [rows][128] f16, no padding; the
+// 16-byte chunk c of row m sits at chunk position c ^ (m & 15), so the 16
+// rows read by one MFMA fragment load (same c) hit 16 different bank groups.
+__device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m & 15)); }
+
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// DIRECT: the activations are f16 in memory (gate/up): buffer loads write
+// them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
+// through registers and are converted to f16 with the row's power of two.
+template <int MSUB, int NP, bool GATED>
+__device__ __forceinline__ void gemm_run(
+    const uint16_t *__restrict__ a_src, const int32_t *__restrict__ x_exp,
+    uint32_t *__restrict__ a_max, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_pairs, int top_k, int E, int ncb, uint32_t a_bytes,
+    const Nvfp4 &w0, const Nvfp4 &w1, int K, int N, uint16_t *__restrict__ out) {
+  constexpr bool DIRECT = GATED;
   constexpr int BM = kBM * MSUB;
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * kLdsRow];
+  constexpr int NW = GATED ? 2 * NP : NP;  // weight row tiles streamed by a wave
+  constexpr int NBUF = DIRECT ? 3 : 2;  // LDS activation buffers
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[NBUF][BM * kUnitK];
   __shared__ float s_rowscale[BM];
-  int e, m0;
-  if (!find_tile(offsets, E, BM, blockIdx.y, e, m0)) return;  // uniform over the workgroup
+  const int per_xcd = gridDim.x / kXcds;
+  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  int e, m0, cb;
+  if (!find_block(offsets, E, BM, ncb, L, e, m0, cb)) return;  // uniform over the workgroup
   const int row0 = offsets[e] + m0;
   const int mrows = min(BM, offsets[e + 1] - row0);
+  const int nq = (mrows + kBM - 1) / kBM;  // 16-row blocks holding rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (K + kUnitK - 1) / kUnitK;
+  const int nt0 = (cb * 4 + wave) * NP;          // first output row tile of this wave
+  const bool wave_on = nt0 * 16 < N;             // waves past the last column stage only
 
-  // ---- staging map: thread -> (row, 16-byte column) of the activation tile.
-  // Every load below is issued unconditionally from a valid address and the
-  // unwanted ones are zeroed with a select, so the loop body has no branches
-  // and the compiler can wait for exactly the load it needs (not for all).
-  const int st_col = (tid & 15) * 8;  // f16 element offset inside the unit
-  const uint16_t *st_src[MSUB];
-  bool st_ok[MSUB];
+  // ---- staging map.  DIRECT: load q of wave w fills rows 16q + 4w + lane/16,
+  // LDS chunk positions lane%16 (one contiguous kilobyte per load); the lane
+  // fetches the K chunk that belongs at that position.  Otherwise: thread ->
+  // (row 16q + tid/16, K chunk tid%16).  Rows past the block, and chunks past
+  // K, read hardware zeros (offset out of range).
+  const int st_row = DIRECT ? 4 * wave + (lane >> 4) : (tid >> 4);  // row within each 16
+  const int st_c = DIRECT ? ((lane & 15) ^ st_row) : (tid & 15);      // K chunk of this lane
+  uint32_t st_off[MSUB];
   float st_scale[MSUB];
 #pragma unroll
   for (int q = 0; q < MSUB; ++q) {
-    const int m = q * kBM + (tid >> 4);
-    st_ok[q] = m < mrows;
+    const int m = q * kBM + st_row;
+    const bool ok = m < mrows;
+    const int prow = ok ? row0 + m : row0;
+    const int arow = GATED ? sorted_pairs[prow] / top_k : prow;
+    st_off[q] = ok ? (uint32_t)arow * (uint32_t)K * 2 + (uint32_t)st_c * 16 : kOOB;
     st_scale[q] = 1.0f;
-    const int mm = st_ok[q] ? m : 0;  // row 0 of the tile always exists
-    if (GATED) {
-      st_src[q] = a_src + (size_t)(sorted_pairs[row0 + mm] / top_k) * K;
-    } else {
-      st_src[q] = a_src + (size_t)(row0 + mm) * K;
-      st_scale[q] = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[row0 + mm])));
-    }
+    if (!GATED) st_scale[q] = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[prow])));
   }
   // per-row factor applied to the fp32 sums: 2^(exponent - 14)
   if (tid < BM) {
     float f = 0.0f;
     if (tid < mrows) {
-      const int ex = GATED ? row_exp[sorted_pairs[row0 + tid] / top_k]
+      const int ex = GATED ? x_exp[sorted_pairs[row0 + tid] / top_k]
                            : row_exponent(__uint_as_float(a_max[row0 + tid]));
       f = __builtin_ldexpf(1.0f, ex - 14);
     }
     s_rowscale[tid] = f;
   }
-
-  auto load_a = [&](int u, u32x4 (&v)[MSUB]) {
-    const int k = u * kUnitK + st_col;
-    const bool kok = k < K;
-    const int kc = kok ? k : 0;
-#pragma unroll
-    for (int q = 0; q < MSUB; ++q) {
-      const u32x4 t = *(const u32x4 *)(st_src[q] + kc);
-      const bool ok = kok && st_ok[q];
-      v[q] = u32x4{ok ? t[0] : 0u, ok ? t[1] : 0u, ok ? t[2] : 0u, ok ? t[3] : 0u};
-    }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_src, a_bytes);
+  auto a_offset = [&](int u, int q) -> uint32_t {
+    const bool kok = u < nunits && u * kUnitK + st_c * 8 < K;
+    return kok ? st_off[q] + (uint32_t)u * kUnitK * 2 : kOOB;  // kOOB + 256u stays out of range
   };
-  auto store_a = [&](int buf, const u32x4 (&v)[MSUB]) {
+  // DIRECT staging of unit u into buffer b
+  auto load_a_lds = [&](int u, int b) {
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void *)&s_a[b][(q * kBM + 4 * wave) * kUnitK], 16,
+          a_offset(u, q), 0, 0, 0);
+  };
+  // register staging
+  auto load_a = [&](int u, u32x4 (&v)[MSUB]) {
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q) v[q] = bload16(ra, a_offset(u, q));
+  };
+  auto store_a = [&](int b, const u32x4 (&v)[MSUB]) {
 #pragma unroll
     for (int q = 0; q < MSUB; ++q) {
       u32x4 o = v[q];
@@ -263,154 +292,195 @@ __global__ __launch_bounds__(kThreads) void k_expert_gemm(
                  ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
       }
-      *(u32x4 *)(&s_a[buf][(q * kBM + (tid >> 4)) * kLdsRow + st_col]) = o;
+      *(u32x4 *)(&s_a[b][lds_chunk(q * kBM + st_row, st_c) * 8]) = o;
     }
   };
 
-  // ---- weight streams of this wave: NT row tiles, read through buffer
-  // resources over expert e's tensor: lane (r, g) of unit u is at byte
-  // 1024u + 16 lane of its row tile (scales: 128u + 2 lane); lanes past the
-  // end of K (and units past the end) read hardware zeros.
-  __amdgpu_buffer_rsrc_t rw[NT], rs[NT];
-  uint32_t vw[NT], vs[NT];
+  // ---- weight streams of this wave (buffer resources over expert e's
+  // tensors; lanes past K, units past the end and waves past N read zeros)
+  __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
+  uint32_t vw[NW], vs[NW];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const Nvfp4 &w = (GATED && i == 1) ? w1 : w0;
-    const int nt = GATED ? (blockIdx.x * 4 + wave) : ((blockIdx.x * 4 + wave) * NT + i);
+  for (int i = 0; i < NW; ++i) {
+    const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
+    const int nt = nt0 + (GATED ? i % NP : i);
     rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
     rs[i] = make_rsrc(w.scales + (size_t)e * N * (K / 16), (uint32_t)((size_t)N * (K / 16)));
-    vw[i] = (uint32_t)nt * 16 * (K / 2) + lane * 16;
-    vs[i] = (uint32_t)nt * K + lane * 2;
+    vw[i] = wave_on ? (uint32_t)nt * 16 * (K / 2) + lane * 16 : kOOB;
+    vs[i] = wave_on ? (uint32_t)nt * K + lane * 2 : kOOB;
   }
-  auto load_w = [&](int u, u32x4 (&wv)[NT], uint32_t (&sv)[NT]) {
+  auto load_w = [&](int u, u32x4 (&wv)[NW], uint32_t (&sv)[NW]) {
     const bool ok = u < nunits && u * kUnitK + 32 * g < K;
-    const uint32_t ow = ok ? (uint32_t)u * 1024 : kOOB, os = ok ? (uint32_t)u * 128 : kOOB;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      wv[i] = bload16_nt(rw[i], vw[i] + ow);
-      sv[i] = bload2(rs[i], vs[i] + os);
+    for (int i = 0; i < NW; ++i) {
+      wv[i] = bload16_nt(rw[i], ok ? vw[i] + (uint32_t)u * 1024 : kOOB);
+      sv[i] = bload2(rs[i], ok ? vs[i] + (uint32_t)u * 128 : kOOB);
     }
   };
 
-  f32x4 acc[MSUB][NT];
+  f32x4 acc[MSUB][NW];
 #pragma unroll
   for (int q = 0; q < MSUB; ++q)
 #pragma unroll
-    for (int i = 0; i < NT; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
+    for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
 
-  // ---- pipeline.  Weights: unit u+kPD is loaded into the register slot
-  // that unit u just used.  Activations: unit u+kPD is loaded into a
-  // register slot before unit u is multiplied and reaches LDS (double
-  // buffer) at the end of iteration u+kPD-1.  Units past the end are zeros
-  // (the unit count is rounded up to a multiple of kPD).  One barrier per unit.
-  u32x4 wbuf[kPD][NT];
-  uint32_t sbuf[kPD][NT];
-  u32x4 av[kPD][MSUB];
-  load_a(0, av[0]);
-  store_a(0, av[0]);
+  auto compute = [&](const uint16_t *abuf, const u32x4 (&wv)[NW], const uint32_t (&sv)[NW]) {
+    f16x2 bs[NW];
 #pragma unroll
-  for (int d = 1; d < kPD; ++d) load_a(d, av[d]);
+    for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(sv[i]);
 #pragma unroll
-  for (int d = 0; d < kPD; ++d) load_w(d, wbuf[d], sbuf[d]);
-  __syncthreads();
-
-  const int nu = (nunits + kPD - 1) / kPD * kPD;
-  for (int u0 = 0; u0 < nu; u0 += kPD) {
+    for (int j = 0; j < 4; ++j) {
+      f16x8 b[NW];
 #pragma unroll
-    for (int d = 0; d < kPD; ++d) {
-      const int u = u0 + d;
-      load_a(u + kPD, av[d]);
-      const uint16_t *abuf = s_a[u & 1];
-      f16x2 bs[NT];
+      for (int i = 0; i < NW; ++i) b[i] = dequant8(wv[i][j], bs[i][j >> 1]);
 #pragma unroll
-      for (int i = 0; i < NT; ++i) bs[i] = block_scales_f16(sbuf[d][i]);
+      for (int q = 0; q < MSUB; ++q) {
+        const f16x8 a = __builtin_bit_cast(
+            f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f16x8 b[NT];
-#pragma unroll
-        for (int i = 0; i < NT; ++i) b[i] = dequant8(wbuf[d][i][j], bs[i][j >> 1]);
-#pragma unroll
-        for (int q = 0; q < MSUB; ++q) {
-          const f16x8 a = __builtin_bit_cast(
-              f16x8, *(const u32x4 *)(abuf + (q * kBM + r) * kLdsRow + 32 * g + 8 * j));
-#pragma unroll
-          for (int i = 0; i < NT; ++i) acc[q][i] = mfma16x16x32(a, b[i], acc[q][i]);
-        }
+        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a, b[i], acc[q][i]);
       }
-      load_w(u + kPD, wbuf[d], sbuf[d]);
-      store_a((u + 1) & 1, av[(d + 1) % kPD]);
-      __syncthreads();
+      // one K step at a time: bounded fragment live ranges
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
 
-  // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
-  const int e_global = e;
-  if (GATED) {
-    const float gg = w0.global[e_global], gu = w1.global[e_global];
-    const int col = (blockIdx.x * 4 + wave) * 16 + r;
+  // ---- pipeline, one barrier per unit; unrolled by two so that register
+  // buffers have static indices (an odd unit count runs one unit of zeros).
+  // Weights: double-buffered in registers, unit u+1 issued before unit u is
+  // multiplied.  Activations are fetched two units ahead.  DIRECT: a ring of
+  // three LDS buffers, unit u+2 issued before unit u is multiplied and
+  // waited for one unit later; otherwise two register sets, unit u+3 loaded
+  // when unit u+1 has been converted into the LDS double buffer.
+  u32x4 wv[2][NW];
+  uint32_t sv[2][NW];
+  const int nu = (nunits + 1) & ~1;
+  if (DIRECT) {
+    load_a_lds(0, 0);
+    load_a_lds(1, 1);
+    load_w(0, wv[0], sv[0]);
+    MOE_WAIT_VMCNT(MSUB + 2 * NW);  // unit 0 of the activations has landed
+    __syncthreads();
+    int ring = 0;  // LDS buffer of unit u
+    for (int u0 = 0; u0 < nu; u0 += 2) {
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q) {
-      float rmax[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m = q * kBM + 4 * g + jj;
-        rmax[jj] = 0.0f;
-        if (m < mrows) {
-          const float f = s_rowscale[m];
-          const float G = acc[q][0][jj] * (gg * f), U = acc[q][1][jj] * (gu * f);
-          const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
-          out[(size_t)(row0 + m) * out_ld + col] = ab;
-          rmax[jj] = fabsf(bf16_to_f32(ab));
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) rmax[jj] = fmaxf(rmax[jj], __shfl_xor(rmax[jj], o, kWave));
-        const int m = q * kBM + 4 * g + jj;
-        if (r == 0 && m < mrows)
-          atomicMax(&a_max[row0 + m], __float_as_uint(rmax[jj]));
+      for (int d = 0; d < 2; ++d) {
+        const int u = u0 + d;
+        const int next2 = ring == 0 ? 2 : ring - 1;  // (u + 2) % 3
+        load_a_lds(u + 2, next2);
+        load_w(u + 1, wv[d ^ 1], sv[d ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s_a[ring], wv[d], sv[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_WAIT_VMCNT(MSUB + 2 * NW);  // unit u+1 of the activations has landed
+        __syncthreads();
+        ring = ring == 2 ? 0 : ring + 1;
       }
     }
   } else {
-    const float gd = w0.global[e_global];
+    u32x4 av[2][MSUB];
+    load_a(0, av[0]);
+    load_w(0, wv[0], sv[0]);
+    load_a(1, av[1]);
+    store_a(0, av[0]);
+    load_a(2, av[0]);
+    __syncthreads();
+    for (int u0 = 0; u0 < nu; u0 += 2) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int col = ((blockIdx.x * 4 + wave) * NT + i) * 16 + r;
-#pragma unroll
-      for (int q = 0; q < MSUB; ++q)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int m = q * kBM + 4 * g + jj;
-          if (m < mrows)
-            out[(size_t)(row0 + m) * out_ld + col] = f32_to_bf16(acc[q][i][jj] * (gd * s_rowscale[m]));
-        }
+      for (int d = 0; d < 2; ++d) {
+        const int u = u0 + d;
+        load_w(u + 1, wv[d ^ 1], sv[d ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s_a[d], wv[d], sv[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(d ^ 1, av[d ^ 1]);
+        load_a(u + 3, av[d ^ 1]);
+        __syncthreads();
+      }
     }
   }
+  if (!wave_on) return;  // no barrier follows
+
+  // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
+  if (GATED) {
+    const float gg = w0.global[e], gu = w1.global[e];
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = q * kBM + 4 * g + jj;
+        const bool ok = m < mrows;
+        const float f = s_rowscale[m];
+        float rmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const float G = acc[q][i][jj] * (gg * f), U = acc[q][NP + i][jj] * (gu * f);
+          const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
+          if (ok) out[(size_t)(row0 + m) * N + (nt0 + i) * 16 + r] = ab;
+          rmax = fmaxf(rmax, ok ? fabsf(bf16_to_f32(ab)) : 0.0f);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, kWave));
+        if (r == 0 && ok) atomicMax(&a_max[row0 + m], __float_as_uint(rmax));
+      }
+    }
+  } else {
+    const float gd = w0.global[e];
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = q * kBM + 4 * g + jj;
+        if (m < mrows) {
+          const float f = gd * s_rowscale[m];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const int n = (nt0 + i) * 16 + r;
+            if (n < N) out[(size_t)(row0 + m) * N + n] = f32_to_bf16(acc[q][i][jj] * f);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MSUB, int NP, bool GATED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_expert_gemm(
+    const uint16_t *__restrict__ a_src,  // GATED: x16 [T][K] f16; else A [P][K] bf16
+    const int32_t *__restrict__ x_exp,   // GATED: exponent of each token
+    uint32_t *__restrict__ a_max,        // GATED: row max of A (written); else read
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_pairs, int top_k,
+    int E, int ncb, uint32_t a_bytes,
+    Nvfp4 w0, Nvfp4 w1,                  // GATED: gate, up; else w0 = down
+    int K, int N, uint16_t *__restrict__ out) {
+  gemm_run<MSUB, NP, GATED>(a_src, x_exp, a_max, offsets, sorted_pairs, top_k, E, ncb, a_bytes, w0,
+                            w1, K, N, out);
 }
 
 // ------------------------------------------------------- GEMV mode ----
 // Few rows per expert (decode).  Every wave is an independent stream: no LDS
 // staging and no barrier in the K loop.  A wave owns NW weight row tiles
 // (gated: NP gate tiles and the same NP up tiles; down: NP tiles) of one
-// tile of up to 4 * NGMAX sorted rows of one expert, processed as groups of 4
-// rows.
+// tile of up to ROWS sorted rows of one expert.
 //
-// Four rows fill one 16x16x32 MFMA block-diagonally, so that one 16-byte
-// load per lane brings 4 rows x 128 K of activations per K unit: lane
-// (r, g) loads row 4q + r%4 of group q, K = 128u + 32g + 8h .. +7 with
-// h = r/4, and feeds it to MFMA h only (zeros to the other three).  MFMA j
-// multiplies by dword j of the lane's weight bytes (K = 128u + 32g + 8j), so
-// accumulator row 4h + m holds row m's dot product over the K chunks with
-// j = h; the four partial rows of a row are summed once after the K loop.
-// Units up to kGemvPD ahead are in flight.
-constexpr int kGemvPD = 2;
-constexpr int kGateNP = 2;  // gate/up row-tile pairs per wave
-constexpr int kDownNP = 4;  // down row tiles per wave
+// Packing of R = 4, 8 or 16 rows into one 16x16x32 MFMA output block: the
+// 16 accumulator rows are 16/R groups of R rows.  Lane (r, g) serves row
+// r % R of group h = r / R and loads NL = R/4 adjacent 16-byte chunks of it,
+// K = 128u + 32g + 8(h NL + s), s < NL; it feeds chunk s to MFMA
+// j = h NL + s and zeros to the others.  MFMA j multiplies by dword j of the
+// lane's weight bytes (K = 128u + 32g + 8j), so group h accumulates the K
+// chunks j in [h NL, h NL + NL) of its rows; the groups are summed once after
+// the K loop.  Every tile costs 4 MFMAs per weight row tile and K unit, and
+// R/4 activation loads per lane.  Units up to kGemvPD ahead are in flight.
+constexpr int kGemvPD = 1;
+constexpr int kGateNP = 1;  // gate/up row-tile pairs per wave
+constexpr int kDownNP = 2;  // down row tiles per wave
 
-template <int NG, int NW>
+template <int NL, int NW>
 struct GemvUnit {
-  u32x4 a[NG];
+  u32x4 a[NL];
   u32x4 w[NW];
   uint32_t s[NW];
 };
@@ -425,28 +495,24 @@ struct GemvArgs {
   uint16_t *out;           // GATED: A [P][N] bf16; else Y [P][N] bf16
 };
 
-template <int NG, int NP, bool GATED>
+template <int R, int NP, bool GATED>
 __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, const Nvfp4 &w1,
                                          int e, int row0, int mrows, int nt0) {
   constexpr int NW = GATED ? 2 * NP : NP;
+  constexpr int NL = R / 4;  // activation chunks per lane and unit
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4, h = r >> 2, m4 = r & 3;
+  const int r = lane & 15, g = lane >> 4, h = r / R, m = r % R;
   const int K = p.K, N = p.N;
   const int nunits = (K + kUnitK - 1) / kUnitK;
 
-  // activation rows of this lane (one per group) and their offsets
-  uint32_t va[NG];
-  float a_scale[NG];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    const int m = 4 * q + m4;
-    const bool ok = m < mrows;
-    const int prow = ok ? row0 + m : row0;
-    const int arow = GATED ? p.sorted_pairs[prow] / p.top_k : prow;
-    va[q] = ok ? (uint32_t)arow * (uint32_t)K * 2 + (uint32_t)(32 * g + 8 * h) * 2 : kOOB;
-    a_scale[q] = 1.0f;
-    if (!GATED) a_scale[q] = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(p.a_max[prow])));
-  }
+  // activation row of this lane
+  const bool row_ok = m < mrows;
+  const int prow = row_ok ? row0 + m : row0;
+  const int arow = GATED ? p.sorted_pairs[prow] / p.top_k : prow;
+  const uint32_t va = row_ok ? (uint32_t)arow * (uint32_t)K * 2 + (uint32_t)(32 * g + 8 * h * NL) * 2
+                             : kOOB;
+  float a_scale = 1.0f;
+  if (!GATED) a_scale = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(p.a_max[prow])));
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_src, p.a_bytes);
 
   // weight streams: expert e's tensors through buffer resources; offsets past
@@ -462,12 +528,13 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     vw[i] = (uint32_t)nt * 16 * (K / 2) + lane * 16;
     vs[i] = (uint32_t)nt * K + lane * 2;
   }
-  auto load = [&](int u, GemvUnit<NG, NW> &d) {
+  auto load = [&](int u, GemvUnit<NL, NW> &d) {
     const bool kok = u < nunits && u * kUnitK + 32 * g < K;
     const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 128 : kOOB;
-    // va[q] is kOOB for rows past the tile; kOOB + 256u stays out of range
+    // va is kOOB for rows past the tile; kOOB + 256u + 16s stays out of range
+    const uint32_t oa = kok ? va + (uint32_t)u * kUnitK * 2 : kOOB;
 #pragma unroll
-    for (int q = 0; q < NG; ++q) d.a[q] = bload16(ra, kok ? va[q] + (uint32_t)u * kUnitK * 2 : kOOB);
+    for (int sl = 0; sl < NL; ++sl) d.a[sl] = bload16(ra, oa + 16 * sl);
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       d.w[i] = bload16_nt(rw[i], vw[i] + ow);
@@ -475,22 +542,20 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     }
   };
 
-  f32x4 acc[NG][NW];
+  f32x4 acc[NW];
 #pragma unroll
-  for (int q = 0; q < NG; ++q)
+  for (int i = 0; i < NW; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  auto compute = [&](const GemvUnit<NL, NW> &c) {
+    f16x8 a[NL];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
-  auto compute = [&](const GemvUnit<NG, NW> &c) {
-    f16x8 a[NG];
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
+    for (int sl = 0; sl < NL; ++sl) {
       if (GATED) {
-        a[q] = __builtin_bit_cast(f16x8, c.a[q]);
+        a[sl] = __builtin_bit_cast(f16x8, c.a[sl]);
       } else {  // bf16 -> f16 with the row's power of two (exact)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          a[q][2 * t] = (f16)(__uint_as_float(c.a[q][t] << 16) * a_scale[q]);
-          a[q][2 * t + 1] = (f16)(__uint_as_float(c.a[q][t] & 0xFFFF0000u) * a_scale[q]);
+          a[sl][2 * t] = (f16)(__uint_as_float(c.a[sl][t] << 16) * a_scale);
+          a[sl][2 * t + 1] = (f16)(__uint_as_float(c.a[sl][t] & 0xFFFF0000u) * a_scale);
         }
       }
     }
@@ -500,15 +565,10 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x8 b[NW];
+      // this lane's operand for MFMA j: its chunk j - h NL when that is in range
+      const f16x8 aj = NL == 4 ? a[j % NL] : (j / NL == h ? a[j % NL] : zero);
 #pragma unroll
-      for (int i = 0; i < NW; ++i) b[i] = dequant8(c.w[i][j], bs[i][j >> 1]);
-#pragma unroll
-      for (int q = 0; q < NG; ++q) {
-        const f16x8 aj = h == j ? a[q] : zero;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(aj, b[i], acc[q][i]);
-      }
+      for (int i = 0; i < NW; ++i) acc[i] = mfma16x16x32(aj, dequant8(c.w[i][j], bs[i][j >> 1]), acc[i]);
     }
   };
 
@@ -518,7 +578,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   // count is rounded up to a multiple of the buffer count; the extra units
   // read zeros through the buffer range check and add nothing.
   constexpr int NB = kGemvPD + 1;
-  GemvUnit<NG, NW> buf[NB];
+  GemvUnit<NL, NW> buf[NB];
 #pragma unroll
   for (int d = 0; d < kGemvPD; ++d) load(d, buf[d]);
   const int nu = (nunits + NB - 1) / NB * NB;
@@ -532,85 +592,107 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     }
   }
 
-  // ---- sum the four partial rows: lane (n, g) holds accumulator rows
-  // 4g + jj, i.e. partial h = g of row jj; after the butterfly every lane
-  // holds the full sums and lane (n, g) keeps row 4q + g.
-  float v[NG][NW];
+  // ---- sum the row groups: lane (n, g) holds accumulator rows 4g + jj =
+  // group (4g + jj) / R, row (4g + jj) % R; after the butterfly over the
+  // groups, lanes with 4g + jj < R hold the full sums of row 4g + jj.
 #pragma unroll
-  for (int q = 0; q < NG; ++q)
+  for (int i = 0; i < NW; ++i)
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      float s4[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float t = acc[q][i][jj];
-        t += __shfl_xor(t, 16, kWave);
-        t += __shfl_xor(t, 32, kWave);
-        s4[jj] = t;
-      }
-      v[q][i] = g == 0 ? s4[0] : g == 1 ? s4[1] : g == 2 ? s4[2] : s4[3];
+    for (int jj = 0; jj < 4; ++jj) {
+      float t = acc[i][jj];
+      if (R <= 8) t += __shfl_xor(t, 32, kWave);
+      if (R <= 4) t += __shfl_xor(t, 16, kWave);
+      acc[i][jj] = t;
     }
 
   if (GATED) {
     const float gg = w0.global[e], gu = w1.global[e];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const int m = 4 * q + g;
-      const bool ok = m < mrows;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int mr = 4 * g + jj;  // row of this lane's sums (valid when mr < R)
+      const bool ok = mr < R && mr < mrows;
       float f = 0.0f;
-      if (ok) f = __builtin_ldexpf(1.0f, p.x_exp[p.sorted_pairs[row0 + m] / p.top_k] - 14);
+      if (ok) f = __builtin_ldexpf(1.0f, p.x_exp[p.sorted_pairs[row0 + mr] / p.top_k] - 14);
       float rmax = 0.0f;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const float G = v[q][i] * (gg * f), U = v[q][NP + i] * (gu * f);
+        const float G = acc[i][jj] * (gg * f), U = acc[NP + i][jj] * (gu * f);
         const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
-        if (ok) p.out[(size_t)(row0 + m) * N + (nt0 + i) * 16 + r] = ab;
+        if (ok) p.out[(size_t)(row0 + mr) * N + (nt0 + i) * 16 + r] = ab;
         rmax = fmaxf(rmax, ok ? fabsf(bf16_to_f32(ab)) : 0.0f);
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, kWave));
-      if (r == 0 && ok) atomicMax(&p.a_max[row0 + m], __float_as_uint(rmax));
+      if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], __float_as_uint(rmax));
     }
   } else {
     const float gd = w0.global[e];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const int m = 4 * q + g;
-      if (m < mrows) {
+    for (int jj = 0; jj < 4; ++jj) {
+      const int mr = 4 * g + jj;
+      if (mr < R && mr < mrows) {
         const float f =
-            gd * __builtin_ldexpf(1.0f, row_exponent(__uint_as_float(p.a_max[row0 + m])) - 14);
+            gd * __builtin_ldexpf(1.0f, row_exponent(__uint_as_float(p.a_max[row0 + mr])) - 14);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const int n = (nt0 + i) * 16 + r;
-          if (n < N) p.out[(size_t)(row0 + m) * N + n] = f32_to_bf16(v[q][i] * f);
+          if (n < N) p.out[(size_t)(row0 + mr) * N + n] = f32_to_bf16(acc[i][jj] * f);
         }
       }
     }
   }
 }
 
+// The GEMV-mode tile list: tile i = (expert, first sorted row, rows) for
+// "expert e contributes ceil(M_e / rows) tiles of rows rows", in expert order;
+// entries up to max_tiles past the last tile get expert -1.  One workgroup:
+// per-expert counts, a scan in LDS, then each thread writes its experts'
+// tiles.  Computed once per launch so that every GEMV workgroup finds its
+// tile with a single scalar load.
+constexpr int kTileThreads = 256;
+__global__ __launch_bounds__(kTileThreads) void k_tile_list(const int32_t *__restrict__ offsets,
+                                                            int E, int rows, int max_tiles,
+                                                            int4 *__restrict__ tiles) {
+  __shared__ int s_cnt[kTileThreads];
+  const int tid = threadIdx.x;
+  int base = 0, m = 0, c = 0;
+  if (tid < E) {
+    base = offsets[tid];
+    m = offsets[tid + 1] - base;
+    c = (m + rows - 1) / rows;
+  }
+  // inclusive scan of c over the first E threads (E <= 256): Hillis-Steele in LDS
+  s_cnt[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < kTileThreads; o <<= 1) {
+    const int v = tid >= o ? s_cnt[tid - o] : 0;
+    __syncthreads();
+    s_cnt[tid] += v;
+    __syncthreads();
+  }
+  const int total = s_cnt[E - 1];
+  if (tid < E) {
+    const int first = s_cnt[tid] - c;
+    for (int i = 0; i < c; ++i) tiles[first + i] = int4{tid, base + i * rows, min(rows, m - i * rows), 0};
+  }
+  for (int i = total + tid; i < max_tiles; i += kTileThreads) tiles[i] = int4{-1, 0, 0, 0};
+}
+
 // GATED: A = gelu_tanh(X Wg^T) * (X Wu^T) -> A [P][N] bf16; else
-// Y = A Wd^T -> Y [P][N] bf16.  Tiles of ROWS sorted rows.
+// Y = A Wd^T -> Y [P][N] bf16.  Tiles of ROWS sorted rows from the tile list.
 template <int ROWS, int NP, bool GATED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 3 : 2)))
-void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets,
-                                                          int E, Nvfp4 w0, Nvfp4 w1) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
+void k_expert_gemv(GemvArgs p, const int4 *__restrict__ tiles, Nvfp4 w0, Nvfp4 w1) {
   const int wave = threadIdx.x >> 6;
   const int nt0 = (blockIdx.x * 4 + wave) * NP;  // first output row tile of this wave
   if (nt0 * 16 >= p.N) return;                   // past the last column (no barrier follows)
-  int e, m0;
-  if (!find_tile(offsets, E, ROWS, blockIdx.y, e, m0)) return;
-  const int row0 = offsets[e] + m0;
-  const int mrows = min(ROWS, offsets[e + 1] - row0);
-  const int ng = (mrows + 3) >> 2;  // uniform over the workgroup
-  if (ROWS == 8) {
-    if (ng <= 1) gemv_run<1, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-    else gemv_run<2, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-  } else {
-    if (ng <= 1) gemv_run<1, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-    else if (ng == 2) gemv_run<2, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-    else gemv_run<4, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-  }
+  const int4 tile = tiles[blockIdx.y];           // uniform address: one scalar load
+  const int e = tile.x, row0 = tile.y, mrows = tile.z;
+  if (e < 0) return;
+  // rows per MFMA block: the smallest packing that holds the tile (uniform)
+  if (mrows <= 4) gemv_run<4, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
+  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
+  else gemv_run<16, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
 }
 
 bool tensor_ok(const nvfp4_tensor *t, int E, int N, int K) {
@@ -631,6 +713,7 @@ using namespace moe;
 
 struct Ws {
   WsLayout L;
+  int4 *tiles;
   int32_t *x_exp;
   uint32_t *a_max;
   uint16_t *x16, *a;
@@ -640,6 +723,7 @@ Ws ws_ptrs(void *workspace, const WsLayout &L) {
   char *ws = (char *)workspace;
   Ws w;
   w.L = L;
+  w.tiles = (int4 *)(ws + L.tiles);
   w.x_exp = (int32_t *)(ws + L.x_exp);
   w.a_max = (uint32_t *)(ws + L.a_max);
   w.x16 = (uint16_t *)(ws + L.x16);
@@ -658,29 +742,43 @@ int check_common(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I, cons
   // buffer-resource offsets are 32-bit: one expert's tensor and the
   // transposed activations must stay below 2 GiB
   if ((long long)H * I / 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
-  if (gemv_mode(T, top_k, E) && (long long)(H > I ? H : I) * T * top_k * 2 >= (1LL << 31))
-    return MOE_ERR_UNSUPPORTED;
+  if ((long long)(H > I ? H : I) * T * top_k * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < ws_layout(T, top_k, E, H, I).total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
 bool tensor_null(const nvfp4_tensor *t) { return !t || !t->packed || !t->scales || !t->global; }
 
+constexpr int kGemmGateNP = 2;  // tiled mode: gate/up row-tile pairs per wave
+constexpr int kGemmDownNP = 4;  // tiled mode: down row tiles per wave
+
+// 1-D grid of the tiled-mode kernels: every (row block, column block), rounded
+// up to a multiple of the XCD count (the extra workgroups find no block)
+dim3 gemm_grid(int P, int E, int bm, int ncb) {
+  const long long tiles = (P + bm - 1) / bm + (E < P ? E : P);  // sum over experts of ceil(M_e / bm)
+  const long long n = tiles * ncb;
+  return dim3((unsigned)((n + kXcds - 1) / kXcds * kXcds));
+}
+
 template <int MSUB>
-int launch_gate_up(const Ws &w, const int32_t *offsets, const int32_t *sorted_pairs, int top_k,
-                   int E, Nvfp4 g, Nvfp4 u, int H, int I, hipStream_t s) {
-  MOE_LAUNCH((k_expert_gemm<MSUB, 2, true>), dim3(I / kCols, w.L.max_tiles), dim3(kThreads), 0, s,
+int launch_gate_up(const Ws &w, const int32_t *offsets, const int32_t *sorted_pairs, int T,
+                   int top_k, int E, Nvfp4 g, Nvfp4 u, int H, int I, hipStream_t s) {
+  const int ncb = (I + 64 * kGemmGateNP - 1) / (64 * kGemmGateNP);
+  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmGateNP, true>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
+             dim3(kThreads), 0, s,
              (const uint16_t *)w.x16, (const int32_t *)w.x_exp, w.a_max, offsets, sorted_pairs,
-             top_k, E, g, u, H, I, w.a, I);
+             top_k, E, ncb, (uint32_t)((size_t)T * H * 2), g, u, H, I, w.a);
   return MOE_OK;
 }
 
-template <int MSUB, int NT>
-int launch_down(const Ws &w, const int32_t *offsets, int top_k, int E, Nvfp4 d, int H, int I,
-                uint16_t *y, hipStream_t s) {
-  MOE_LAUNCH((k_expert_gemm<MSUB, NT, false>), dim3(H / (kCols * NT), w.L.max_tiles),
-             dim3(kThreads), 0, s, (const uint16_t *)w.a, (const int32_t *)nullptr, w.a_max,
-             offsets, (const int32_t *)nullptr, top_k, E, d, d, I, H, y, H);
+template <int MSUB>
+int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nvfp4 d, int H,
+                int I, uint16_t *y, hipStream_t s) {
+  const int ncb = (H + 64 * kGemmDownNP - 1) / (64 * kGemmDownNP);
+  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
+             dim3(kThreads), 0, s, (const uint16_t *)w.a, (const int32_t *)nullptr, w.a_max, offsets,
+             (const int32_t *)nullptr, top_k, E, ncb, (uint32_t)((size_t)T * top_k * I * 2), d, d,
+             I, H, y);
   return MOE_OK;
 }
 
@@ -715,21 +813,22 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
   Nvfp4 u{up->packed, up->scales, up->global};
   hipStream_t s = (hipStream_t)stream;
   if (gemv_mode(T, top_k, E)) {
+    const int rows = gemv_rows(T, top_k, E);
+    MOE_LAUNCH(k_tile_list, dim3(1), dim3(kTileThreads), 0, s, expert_offsets, E, rows,
+               w.L.max_tiles, w.tiles);
     const int cols = 4 * 16 * kGateNP;  // output columns per workgroup
     const dim3 grid((I + cols - 1) / cols, w.L.max_tiles);
     const GemvArgs a{w.x16, w.x_exp, w.a_max, sorted_pairs, top_k, H, I, T * top_k,
                      (uint32_t)((size_t)T * H * 2), w.a};
-    if (gemv_rows(T, top_k, E) == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true>), grid, dim3(kThreads), 0, s, a, expert_offsets, E, g, u);
+    if (rows == 8)
+      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true>), grid, dim3(kThreads), 0, s, a,
+                 (const int4 *)w.tiles, g, u);
     else
-      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true>), grid, dim3(kThreads), 0, s, a, expert_offsets, E, g, u);
+      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true>), grid, dim3(kThreads), 0, s, a,
+                 (const int4 *)w.tiles, g, u);
     return MOE_OK;
   }
-  switch (choose_msub(T, top_k, E)) {
-    case 1: return launch_gate_up<1>(w, expert_offsets, sorted_pairs, top_k, E, g, u, H, I, s);
-    case 2: return launch_gate_up<2>(w, expert_offsets, sorted_pairs, top_k, E, g, u, H, I, s);
-    default: return launch_gate_up<4>(w, expert_offsets, sorted_pairs, top_k, E, g, u, H, I, s);
-  }
+  return launch_gate_up<4>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
 }
 
 extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets,
@@ -745,26 +844,20 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
   Nvfp4 d{down->packed, down->scales, down->global};
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_mode(T, top_k, E)) {
+  if (gemv_mode(T, top_k, E)) {  // tile list written by nvfp4_expert_gate_up
     const int cols = 4 * 16 * kDownNP;
     const dim3 grid((H + cols - 1) / cols, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
     if (gemv_rows(T, top_k, E) == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kDownNP, false>), grid, dim3(kThreads), 0, s, a, expert_offsets, E, d, d);
+      MOE_LAUNCH((k_expert_gemv<8, kDownNP, false>), grid, dim3(kThreads), 0, s, a,
+                 (const int4 *)w.tiles, d, d);
     else
-      MOE_LAUNCH((k_expert_gemv<16, kDownNP, false>), grid, dim3(kThreads), 0, s, a, expert_offsets, E, d, d);
+      MOE_LAUNCH((k_expert_gemv<16, kDownNP, false>), grid, dim3(kThreads), 0, s, a,
+                 (const int4 *)w.tiles, d, d);
     return MOE_OK;
   }
-  const bool two = H % (2 * kCols) == 0;
-  switch (choose_msub(T, top_k, E)) {
-    case 1: return two ? launch_down<1, 2>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s)
-                       : launch_down<1, 1>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s);
-    case 2: return two ? launch_down<2, 2>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s)
-                       : launch_down<2, 1>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s);
-    default: return two ? launch_down<4, 2>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s)
-                        : launch_down<4, 1>(w, expert_offsets, top_k, E, d, H, I, y_sorted, s);
-  }
+  return launch_down<4>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
 }
 
 extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate,

@@ -259,7 +259,8 @@ def _expert_case(T, k, E, H, I, seed):
 # 64-row tiles; odd H / I multiples of 64 leave partial K units.
 @pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (5, 2, 8, 128, 64), (16, 2, 8, 128, 64),
                                        (24, 4, 16, 256, 128), (37, 4, 8, 192, 128),
-                                       (100, 4, 8, 128, 64), (300, 2, 4, 256, 64)])
+                                       (100, 4, 8, 128, 64), (300, 2, 4, 256, 64),
+                                       (100, 4, 8, 192, 128), (200, 2, 4, 64, 64)])
 def test_expert_mlp_small(T, k, E, H, I):
     c, idx = _expert_case(T, k, E, H, I, seed=T)
     layer = W.build_small_layer(c, k)
