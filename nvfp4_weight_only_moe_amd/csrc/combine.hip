@@ -1,14 +1,17 @@
 // moe_combine: weighted sum of a token's routed expert outputs
 // ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture: sum over k of w_k h2_k).
 // out[t] = sum_j w[t][j] * Y[rank(t, j)], fixed order j = 0, 1, ..., fp32
-// accumulation, one bf16 rounding.  One workgroup per token; each thread owns
-// 8 consecutive outputs (16-byte loads and stores).
+// accumulation, one bf16 rounding.  Workgroup (t, c) covers token t's columns
+// 1024c .. 1024c + 1023; each thread owns 8 consecutive outputs (16-byte
+// loads and stores), so even a decode batch spreads over many workgroups.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
+constexpr int kCombineThreads = 128;
+
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t *__restrict__ y,
                                                  const float *__restrict__ w,
                                                  const int32_t *__restrict__ rank, int T, int K,
                                                  int H, uint16_t *__restrict__ out) {
@@ -32,7 +35,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
       }
     }
   }
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+  const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
+  if (c < H) {
     u32x4 v[MOE_MAX_TOPK];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j)
@@ -66,7 +70,8 @@ extern "C" int moe_combine(const uint16_t *y_sorted, const float *topk_w, const 
   if (T < 0 || top_k <= 0 || H <= 0 || H % 8) return MOE_ERR_SHAPE;
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
-  MOE_LAUNCH(k_combine, dim3(T), dim3(256), 0, (hipStream_t)stream, y_sorted, topk_w,
-                     pair_rank, T, top_k, H, out);
+  MOE_LAUNCH(k_combine, dim3(T, (H + 8 * kCombineThreads - 1) / (8 * kCombineThreads)),
+             dim3(kCombineThreads), 0, (hipStream_t)stream, y_sorted, topk_w, pair_rank, T, top_k,
+             H, out);
   return MOE_OK;
 }
