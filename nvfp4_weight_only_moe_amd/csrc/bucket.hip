@@ -6,8 +6,9 @@
 // p = t*top_k + j.  Pairs with an id outside [0, E) go to an extra bucket E
 // placed after all experts and are counted in the error word.
 //
-// Up to kChunk pairs: one workgroup does everything (LDS histogram, scan,
-// stable scatter).  Beyond that: (1) per-chunk LDS histograms, (2) one
+// Up to kSmallP pairs: one workgroup does everything (LDS histogram, scan,
+// stable scatter).  Beyond that, in chunks of kChunk pairs: (1) per-chunk
+// LDS histograms, (2) one
 // workgroup turns them into expert offsets and per-chunk base positions,
 // (3) per-chunk stable scatter.  The in-chunk rank of a pair among pairs of the
 // same expert comes from a wave "multi-split": 9 ballots give each lane the
@@ -21,7 +22,8 @@ namespace {
 
 constexpr int kBucketThreads = 256;
 constexpr int kBucketWaves = kBucketThreads / kWave;
-constexpr int kChunk = 4096;             // pairs per workgroup
+constexpr int kSmallP = 4096;            // up to this many pairs: one workgroup
+constexpr int kChunk = 1024;             // pairs per workgroup beyond that
 constexpr int kMaxB = MOE_MAX_EXPERTS + 1;  // buckets incl. the invalid one
 
 __device__ __forceinline__ int bucket_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *
                                                                  int32_t *__restrict__ sorted,
                                                                  int32_t *__restrict__ rank,
                                                                  int32_t *__restrict__ err) {
-  __shared__ int s_b[kChunk];
+  __shared__ int s_b[kSmallP];
   __shared__ int s_cnt[kMaxB], s_run[kMaxB];
   __shared__ int s_wcnt[kBucketWaves][kMaxB];
   const int tid = threadIdx.x, nb = E + 1;
@@ -205,7 +207,7 @@ extern "C" int moe_bucket(const int32_t *topk_idx, int32_t T, int32_t top_k, int
   hipStream_t s = (hipStream_t)stream;
   const int P = T * top_k;
   int32_t *err = (int32_t *)workspace;
-  if (P <= kChunk) {
+  if (P <= kSmallP) {
     MOE_LAUNCH(k_bucket_small, dim3(1), dim3(kBucketThreads), 0, s, topk_idx, P, E,
                        expert_offsets, sorted_pairs, pair_rank, err);
     return MOE_OK;

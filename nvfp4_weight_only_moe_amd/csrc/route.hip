@@ -146,12 +146,14 @@ __global__ __launch_bounds__(256) void k_route_logits_few(
   }
 }
 
-// ---- many tokens: 64 tokens x 128 experts per workgroup (16 x 128 per wave),
-// K in chunks of 64 staged in LDS by coalesced row loads.  The split is taken
-// on the activation side when staging: x*scale = hi + lo (both bf16, exact).
-constexpr int kWideKC = 64;
+// ---- many tokens: 64 tokens x 32 experts per workgroup (16 x 32 per wave),
+// so that even 2048 tokens give 128 workgroups.  K in chunks of 128 staged in
+// LDS by coalesced row loads (16 threads per row); the next chunk is loaded
+// into registers while the current one is multiplied.  The split is taken on
+// the activation side when staging: x*scale = hi + lo (both bf16, exact).
+constexpr int kWideKC = 128;
 constexpr int kWideTok = 64;
-constexpr int kWideExp = 128;
+constexpr int kWideExp = 32;
 constexpr int kWideLd = kWideKC + 8;  // bf16 per LDS row (padding spreads banks)
 
 __global__ __launch_bounds__(256) void k_route_logits_wide(
@@ -166,66 +168,85 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
   const int r = lane & 15, g = lane >> 4;
   const int e0 = blockIdx.x * kWideExp;
   const int t0 = blockIdx.y * kWideTok;
-  // staging map: 8 threads per row (8 x 16 B = one 64-element row chunk)
-  const int srow = tid >> 3, scol = (tid & 7) * 8;  // rows srow, srow+32 (x) / +32.. (w)
-  f32x4 acc[8];
+  // staging map: 16 threads per row, rows srow + 16h
+  const int srow = tid >> 4, scol = (tid & 15) * 8;
+  const uint16_t *xrow[4];
+  bool xok[4];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) acc[f] = f32x4{0, 0, 0, 0};
-  float ss[2] = {0.0f, 0.0f};
-  for (int kc = 0; kc < H; kc += kWideKC) {
-    // loads (coalesced rows), then split, then LDS
-    const u32x4 sv = *(const u32x4 *)(scale + kc + scol);
-    u32x4 xv[2], wv[4];
+  for (int h = 0; h < 4; ++h) {
+    const int t = t0 + srow + 16 * h;
+    xok[h] = t < T;
+    xrow[h] = x + (size_t)(xok[h] ? t : 0) * H;
+  }
+  const uint16_t *wrow[2];
+  bool wok[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = t0 + srow + 32 * h;
-      xv[h] = u32x4{0, 0, 0, 0};
-      if (t < T) xv[h] = *(const u32x4 *)(x + (size_t)t * H + kc + scol);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int ee = e0 + srow + 16 * h;
+    wok[h] = ee < E;
+    wrow[h] = w + (size_t)(wok[h] ? ee : 0) * H;
+  }
+  u32x4 xv[4], wv[2], sv;
+  auto load = [&](int kc) {
+    const bool kok = kc + scol < H;  // chunks past the end (H % 128 = 64, or the last prefetch) read zeros
+    const u32x4 s0 = *(const u32x4 *)(scale + (kok ? kc + scol : 0));
+    sv = kok ? s0 : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const int ee = e0 + srow + 32 * h;
-      wv[h] = u32x4{0, 0, 0, 0};
-      if (ee < E) wv[h] = *(const u32x4 *)(w + (size_t)ee * H + kc + scol);
+      const u32x4 v = *(const u32x4 *)(xrow[h] + (kok ? kc + scol : 0));
+      xv[h] = (xok[h] && kok) ? v : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();  // previous chunk fully consumed
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const u32x4 v = *(const u32x4 *)(wrow[h] + (kok ? kc + scol : 0));
+      wv[h] = (wok[h] && kok) ? v : u32x4{0, 0, 0, 0};
+    }
+  };
+  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto store = [&]() {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
       ss[h] += sumsq8(xv[h]);
       bf16x8 hi, lo;
       split_products(xv[h], sv, hi, lo);
-      *(bf16x8 *)(s_xh + (srow + 32 * h) * kWideLd + scol) = hi;
-      *(bf16x8 *)(s_xl + (srow + 32 * h) * kWideLd + scol) = lo;
+      *(bf16x8 *)(s_xh + (srow + 16 * h) * kWideLd + scol) = hi;
+      *(bf16x8 *)(s_xl + (srow + 16 * h) * kWideLd + scol) = lo;
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) *(u32x4 *)(s_w + (srow + 32 * h) * kWideLd + scol) = wv[h];
+    for (int h = 0; h < 2; ++h) *(u32x4 *)(s_w + (srow + 16 * h) * kWideLd + scol) = wv[h];
+  };
+  f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  load(0);
+  for (int kc = 0; kc < H; kc += kWideKC) {
+    store();
     __syncthreads();
+    load(kc + kWideKC);  // next chunk in flight during the MFMAs
 #pragma unroll
     for (int ks = 0; ks < kWideKC; ks += 32) {
       const int k = ks + 8 * g;
       const bf16x8 ah = *(const bf16x8 *)(s_xh + (wave * 16 + r) * kWideLd + k);
       const bf16x8 al = *(const bf16x8 *)(s_xl + (wave * 16 + r) * kWideLd + k);
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
+      for (int f = 0; f < 2; ++f) {
         const bf16x8 b = *(const bf16x8 *)(s_w + (f * 16 + r) * kWideLd + k);
         acc[f] = mfma_bf16(ah, b, acc[f]);
         acc[f] = mfma_bf16(al, b, acc[f]);
       }
     }
+    __syncthreads();
   }
-  // sum of squares per token: 8 threads per row
+  // sum of squares per token: 16 threads per row
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 4; ++h) {
     float v = ss[h];
-    v += __shfl_xor(v, 1, kWave);
-    v += __shfl_xor(v, 2, kWave);
-    v += __shfl_xor(v, 4, kWave);
-    if ((tid & 7) == 0) s_ss[srow + 32 * h] = v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
+    if ((tid & 15) == 0) s_ss[srow + 16 * h] = v;
   }
   __syncthreads();
   const float hs = 1.0f / sqrtf((float)H);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
+  for (int f = 0; f < 2; ++f) {
     const int e = e0 + f * 16 + r;
     if (e >= E) continue;
     const float b = bias ? bias[e] : 0.0f;
