@@ -324,24 +324,37 @@ __device__ __forceinline__ void gemm_run(
 #pragma unroll
     for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
 
+  // One K unit: 4 steps of 32.  The activation fragments of step j+1 are
+  // read from LDS while step j is dequantised and multiplied (two register
+  // sets), and scheduling-group barriers keep that order, so LDS latency
+  // hides behind the MFMAs instead of stalling each of them.
   auto compute = [&](const uint16_t *abuf, const u32x4 (&wv)[NW], const uint32_t (&sv)[NW]) {
     f16x2 bs[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(sv[i]);
+    f16x8 a[2][MSUB];
+#pragma unroll
+    for (int q = 0; q < MSUB; ++q)
+      a[0][q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g) * 8));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if (j < 3) {
+#pragma unroll
+        for (int q = 0; q < MSUB; ++q)
+          a[(j + 1) & 1][q] = __builtin_bit_cast(
+              f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j + 1) * 8));
+      }
       f16x8 b[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) b[i] = dequant8(wv[i][j], bs[i][j >> 1]);
 #pragma unroll
-      for (int q = 0; q < MSUB; ++q) {
-        const f16x8 a = __builtin_bit_cast(
-            f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
+      for (int q = 0; q < MSUB; ++q)
 #pragma unroll
-        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a, b[i], acc[q][i]);
-      }
-      // one K step at a time: bounded fragment live ranges
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[j & 1][q], b[i], acc[q][i]);
+      // order: LDS reads of the next step, dequantisation, MFMAs of this step
+      if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8 * NW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MSUB * NW, 0);
     }
   };
 
@@ -352,32 +365,33 @@ __device__ __forceinline__ void gemm_run(
   // three LDS buffers, unit u+2 issued before unit u is multiplied and
   // waited for one unit later; otherwise two register sets, unit u+3 loaded
   // when unit u+1 has been converted into the LDS double buffer.
-  u32x4 wv[2][NW];
-  uint32_t sv[2][NW];
-  const int nu = (nunits + 1) & ~1;
+  u32x4 wv[3][NW];
+  uint32_t sv[3][NW];
   if (DIRECT) {
+    // weights two units ahead (three register sets, loop unrolled by three;
+    // the steps past the last unit skip their MFMAs, a uniform branch)
     load_a_lds(0, 0);
     load_a_lds(1, 1);
     load_w(0, wv[0], sv[0]);
-    MOE_WAIT_VMCNT(MSUB + 2 * NW);  // unit 0 of the activations has landed
+    load_w(1, wv[1], sv[1]);
+    MOE_WAIT_VMCNT(MSUB + 4 * NW);  // unit 0 of the activations has landed
     __syncthreads();
-    int ring = 0;  // LDS buffer of unit u
-    for (int u0 = 0; u0 < nu; u0 += 2) {
+    const int nu3 = (nunits + 2) / 3 * 3;
+    for (int u0 = 0; u0 < nu3; u0 += 3) {
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int u = u0 + d;
-        const int next2 = ring == 0 ? 2 : ring - 1;  // (u + 2) % 3
-        load_a_lds(u + 2, next2);
-        load_w(u + 1, wv[d ^ 1], sv[d ^ 1]);
+      for (int d = 0; d < 3; ++d) {
+        const int u = u0 + d;  // LDS ring buffer of unit u: u % 3 = d
+        load_a_lds(u + 2, (d + 2) % 3);
+        load_w(u + 2, wv[(d + 2) % 3], sv[(d + 2) % 3]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(s_a[ring], wv[d], sv[d]);
+        if (u < nunits) compute(s_a[d], wv[d], sv[d]);
         __builtin_amdgcn_sched_barrier(0);
-        MOE_WAIT_VMCNT(MSUB + 2 * NW);  // unit u+1 of the activations has landed
+        MOE_WAIT_VMCNT(MSUB + 4 * NW);  // unit u+1 of the activations has landed
         __syncthreads();
-        ring = ring == 2 ? 0 : ring + 1;
       }
     }
   } else {
+    const int nu = (nunits + 1) & ~1;
     u32x4 av[2][MSUB];
     load_a(0, av[0]);
     load_w(0, wv[0], sv[0]);
