@@ -474,10 +474,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ------------------------------------------------------- GEMV mode ----
-// Few rows per expert (decode).  Every wave is an independent stream: no LDS
-// staging and no barrier in the K loop.  A wave owns NW weight row tiles
-// (gated: NP gate tiles and the same NP up tiles; down: NP tiles) of one
-// tile of up to ROWS sorted rows of one expert.
+// Few rows per expert (decode).  A workgroup owns NW weight row tiles (gated:
+// NP gate tiles and the same NP up tiles; down: NP tiles) of one tile of up
+// to ROWS sorted rows of one expert; its 4 waves split K (a quarter of the K
+// units each), stream their share with no LDS staging and no barrier, and
+// add their partial sums in LDS once at the end (in wave order).  Short
+// per-wave streams and many waves keep HBM busy even when a decode batch
+// touches few experts.
 //
 // Packing of R = 4, 8 or 16 rows into one 16x16x32 MFMA output block: the
 // 16 accumulator rows are 16/R groups of R rows.  Lane (r, g) serves row
@@ -489,8 +492,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // the K loop.  Every tile costs 4 MFMAs per weight row tile and K unit, and
 // R/4 activation loads per lane.  Units up to kGemvPD ahead are in flight.
 constexpr int kGemvPD = 1;
-constexpr int kGateNP = 1;  // gate/up row-tile pairs per wave
-constexpr int kDownNP = 2;  // down row tiles per wave
+constexpr int kGateNP = 1;  // gate/up row-tile pairs per workgroup
+constexpr int kDownNP = 2;  // down row tiles per workgroup
+// the K split is used when the unsplit grid would have fewer workgroups
+constexpr int kGemvSplitBelow = 1024;
 
 template <int NL, int NW>
 struct GemvUnit {
@@ -509,15 +514,18 @@ struct GemvArgs {
   uint16_t *out;           // GATED: A [P][N] bf16; else Y [P][N] bf16
 };
 
-template <int R, int NP, bool GATED>
+template <int R, int NP, bool GATED, int KS>
 __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, const Nvfp4 &w1,
-                                         int e, int row0, int mrows, int nt0) {
+                                         int e, int row0, int mrows, int nt0, float *s_red) {
   constexpr int NW = GATED ? 2 * NP : NP;
   constexpr int NL = R / 4;  // activation chunks per lane and unit
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4, h = r / R, m = r % R;
   const int K = p.K, N = p.N;
   const int nunits = (K + kUnitK - 1) / kUnitK;
+  // this wave's share of the K units (KS = 4: the waves split K and their
+  // partial sums meet in LDS after the loop; KS = 1: all of K)
+  const int ub = KS == 1 ? 0 : wave * nunits / KS, ue = KS == 1 ? nunits : (wave + 1) * nunits / KS;
 
   // activation row of this lane
   const bool row_ok = m < mrows;
@@ -543,7 +551,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     vs[i] = (uint32_t)nt * K + lane * 2;
   }
   auto load = [&](int u, GemvUnit<NL, NW> &d) {
-    const bool kok = u < nunits && u * kUnitK + 32 * g < K;
+    const bool kok = u < ue && u * kUnitK + 32 * g < K;
     const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 128 : kOOB;
     // va is kOOB for rows past the tile; kOOB + 256u + 16s stays out of range
     const uint32_t oa = kok ? va + (uint32_t)u * kUnitK * 2 : kOOB;
@@ -594,9 +602,9 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   constexpr int NB = kGemvPD + 1;
   GemvUnit<NL, NW> buf[NB];
 #pragma unroll
-  for (int d = 0; d < kGemvPD; ++d) load(d, buf[d]);
-  const int nu = (nunits + NB - 1) / NB * NB;
-  for (int u0 = 0; u0 < nu; u0 += NB) {
+  for (int d = 0; d < kGemvPD; ++d) load(ub + d, buf[d]);
+  const int nu = (ue - ub + NB - 1) / NB * NB;
+  for (int u0 = ub; u0 < ub + nu; u0 += NB) {
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       load(u0 + d + kGemvPD, buf[(d + kGemvPD) % NB]);
@@ -604,6 +612,20 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       compute(buf[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // ---- the K split: partial sums to LDS, wave 0 adds them in wave order
+  // (a fixed order: the result is the same on every run) and finishes
+  if (KS > 1) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      *(f32x4 *)&s_red[((wave * 64 + lane) * NW + i) * 4] = acc[i];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < KS; ++w)
+#pragma unroll
+      for (int i = 0; i < NW; ++i) acc[i] += *(const f32x4 *)&s_red[((w * 64 + lane) * NW + i) * 4];
   }
 
   // ---- sum the row groups: lane (n, g) holds accumulator rows 4g + jj =
@@ -694,19 +716,25 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_list(const int32_t *__res
 
 // GATED: A = gelu_tanh(X Wg^T) * (X Wu^T) -> A [P][N] bf16; else
 // Y = A Wd^T -> Y [P][N] bf16.  Tiles of ROWS sorted rows from the tile list.
-template <int ROWS, int NP, bool GATED>
+// KS = 1: the 4 waves take 4 consecutive column groups of NP row tiles, each
+// all of K; KS = 4: the 4 waves share one column group and split K (for
+// batches with few tiles, where whole-K streams per wave would leave HBM
+// idle).
+template <int ROWS, int NP, bool GATED, int KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
 void k_expert_gemv(GemvArgs p, const int4 *__restrict__ tiles, Nvfp4 w0, Nvfp4 w1) {
+  constexpr int NW = GATED ? 2 * NP : NP;
+  __shared__ __attribute__((aligned(16))) float s_red[KS > 1 ? KS * 64 * NW * 4 : 4];
   const int wave = threadIdx.x >> 6;
-  const int nt0 = (blockIdx.x * 4 + wave) * NP;  // first output row tile of this wave
-  if (nt0 * 16 >= p.N) return;                   // past the last column (no barrier follows)
-  const int4 tile = tiles[blockIdx.y];           // uniform address: one scalar load
+  const int nt0 = KS == 1 ? (blockIdx.x * 4 + wave) * NP : blockIdx.x * NP;  // first row tile
+  if (nt0 * 16 >= p.N) return;  // past the last column (KS = 4: uniform; KS = 1: no barrier follows)
+  const int4 tile = tiles[blockIdx.y];  // uniform address: one scalar load
   const int e = tile.x, row0 = tile.y, mrows = tile.z;
-  if (e < 0) return;
+  if (e < 0) return;  // uniform
   // rows per MFMA block: the smallest packing that holds the tile (uniform)
-  if (mrows <= 4) gemv_run<4, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
-  else gemv_run<16, NP, GATED>(p, w0, w1, e, row0, mrows, nt0);
+  if (mrows <= 4) gemv_run<4, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else gemv_run<16, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
 }
 
 bool tensor_ok(const nvfp4_tensor *t, int E, int N, int K) {
@@ -830,16 +858,20 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
     const int rows = gemv_rows(T, top_k, E);
     MOE_LAUNCH(k_tile_list, dim3(1), dim3(kTileThreads), 0, s, expert_offsets, E, rows,
                w.L.max_tiles, w.tiles);
-    const int cols = 4 * 16 * kGateNP;  // output columns per workgroup
-    const dim3 grid((I + cols - 1) / cols, w.L.max_tiles);
+    const int gx = (I + 64 * kGateNP - 1) / (64 * kGateNP);  // unsplit: 4 column groups per workgroup
+    const bool split = gx * w.L.max_tiles < kGemvSplitBelow;
+    const dim3 grid(split ? (I + 16 * kGateNP - 1) / (16 * kGateNP) : gx, w.L.max_tiles);
     const GemvArgs a{w.x16, w.x_exp, w.a_max, sorted_pairs, top_k, H, I, T * top_k,
                      (uint32_t)((size_t)T * H * 2), w.a};
-    if (rows == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true>), grid, dim3(kThreads), 0, s, a,
-                 (const int4 *)w.tiles, g, u);
-    else
-      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true>), grid, dim3(kThreads), 0, s, a,
-                 (const int4 *)w.tiles, g, u);
+    const int4 *tl = (const int4 *)w.tiles;
+#define MOE_GEMV_GU(ROWS, KS) \
+  MOE_LAUNCH((k_expert_gemv<ROWS, kGateNP, true, KS>), grid, dim3(kThreads), 0, s, a, tl, g, u)
+    if (rows == 8) {
+      if (split) MOE_GEMV_GU(8, 4); else MOE_GEMV_GU(8, 1);
+    } else {
+      if (split) MOE_GEMV_GU(16, 4); else MOE_GEMV_GU(16, 1);
+    }
+#undef MOE_GEMV_GU
     return MOE_OK;
   }
   return launch_gate_up<4>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
@@ -859,16 +891,20 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
   Nvfp4 d{down->packed, down->scales, down->global};
   hipStream_t s = (hipStream_t)stream;
   if (gemv_mode(T, top_k, E)) {  // tile list written by nvfp4_expert_gate_up
-    const int cols = 4 * 16 * kDownNP;
-    const dim3 grid((H + cols - 1) / cols, w.L.max_tiles);
+    const int gx = (H + 64 * kDownNP - 1) / (64 * kDownNP);
+    const bool split = gx * w.L.max_tiles < kGemvSplitBelow;
+    const dim3 grid(split ? (H + 16 * kDownNP - 1) / (16 * kDownNP) : gx, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
-    if (gemv_rows(T, top_k, E) == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kDownNP, false>), grid, dim3(kThreads), 0, s, a,
-                 (const int4 *)w.tiles, d, d);
-    else
-      MOE_LAUNCH((k_expert_gemv<16, kDownNP, false>), grid, dim3(kThreads), 0, s, a,
-                 (const int4 *)w.tiles, d, d);
+    const int4 *tl = (const int4 *)w.tiles;
+#define MOE_GEMV_DN(ROWS, KS) \
+  MOE_LAUNCH((k_expert_gemv<ROWS, kDownNP, false, KS>), grid, dim3(kThreads), 0, s, a, tl, d, d)
+    if (gemv_rows(T, top_k, E) == 8) {
+      if (split) MOE_GEMV_DN(8, 4); else MOE_GEMV_DN(8, 1);
+    } else {
+      if (split) MOE_GEMV_DN(16, 4); else MOE_GEMV_DN(16, 1);
+    }
+#undef MOE_GEMV_DN
     return MOE_OK;
   }
   return launch_down<4>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
