@@ -375,14 +375,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+S_I = 704  # expert intermediate size of the workloads
+
+
 def gate_up_kernel_name(T, K, E):
     """The kernel nvfp4_expert_gate_up launches for this shape (the dispatch
     rule of the library: few rows per expert -> GEMV mode)."""
     P = T * K
     avg = P // max(1, min(P, E))
     if avg < 24:
-        return f"k_expert_gemv<{8 if P <= 4 * E else 16}, 2, true>"
-    return f"k_expert_gemm<{2 if avg < 64 else 4}, 2, true>"
+        rows = 8 if P <= 4 * E else 16
+        max_tiles = (P + rows - 1) // rows + min(E, P)
+        split = 4 if ((S_I + 63) // 64) * max_tiles < 1024 else 1
+        return f"k_expert_gemv<{rows}, 1, true, {split}>"
+    return "k_expert_gemm<4, 2, true>"
 
 
 def profiled_traffic(workload, kernel):

@@ -140,8 +140,11 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_scan(const int32_t *_
                                                                 int32_t *__restrict__ err) {
   __shared__ int s_tot[kMaxB], s_off[kMaxB];
   const int tid = threadIdx.x, nb = E + 1;
+  // the chunk loops are unrolled so that many independent count loads are
+  // in flight at once (the sums themselves stay in chunk order)
   for (int b = tid; b < nb; b += kBucketThreads) {
     int s = 0;
+#pragma unroll 16
     for (int c = 0; c < nchunks; ++c) s += chunk_cnt[(size_t)c * nb + b];
     s_tot[b] = s;
   }
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_scan(const int32_t *_
   for (int b = tid; b < nb; b += kBucketThreads) {
     offsets[b] = s_off[b];
     int run = s_off[b];
+#pragma unroll 16
     for (int c = 0; c < nchunks; ++c) {
       chunk_base[(size_t)c * nb + b] = run;
       run += chunk_cnt[(size_t)c * nb + b];

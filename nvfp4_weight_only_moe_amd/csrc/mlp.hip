@@ -94,7 +94,10 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
 // ---------------------------------------------------------------- prep ----
 // One wave per token: row maximum -> exponent -> f16 row scaled by
 // 2^(14 - exponent), row-major [T][H]; the other threads clear the per-row
-// maximum of A.
+// maximum of A.  A lane keeps its (up to kPrepV) 16-byte pieces of the row in
+// registers between the two passes, so the row is read once.
+constexpr int kPrepV = 8;  // H <= 64 * 8 * kPrepV; longer rows take a second read
+
 __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ x, int T, int H,
                                                    int P, uint16_t *__restrict__ x16,
                                                    int32_t *__restrict__ x_exp,
@@ -104,8 +107,14 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const uint16_t *row = x + (size_t)t * H;
+  u32x4 keep[kPrepV];
   float amax = 0.0f;
-  for (int k = lane * 8; k < H; k += kWave * 8) {
+#pragma unroll
+  for (int v = 0; v < kPrepV; ++v) {
+    const int k = (v * kWave + lane) * 8;
+    keep[v] = k < H ? *(const u32x4 *)(row + k) : u32x4{0, 0, 0, 0};
+  }
+  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {  // rows longer than kept
     const u32x4 v = *(const u32x4 *)(row + k);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -113,11 +122,17 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
       amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
     }
   }
+#pragma unroll
+  for (int v = 0; v < kPrepV; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(keep[v][i] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(keep[v][i] & 0xFFFF0000u)));
+    }
   amax = wave_max(amax);
   const int ex = row_exponent(amax);
   const float f = __builtin_ldexpf(1.0f, 14 - ex);
-  for (int k = lane * 8; k < H; k += kWave * 8) {
-    const u32x4 v = *(const u32x4 *)(row + k);
+  auto convert = [&](const u32x4 &v) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -125,8 +140,15 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
       const f16 hi = (f16)(__uint_as_float(v[i] & 0xFFFF0000u) * f);
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    *(u32x4 *)(x16 + (size_t)t * H + k) = o;
+    return o;
+  };
+#pragma unroll
+  for (int v = 0; v < kPrepV; ++v) {
+    const int k = (v * kWave + lane) * 8;
+    if (k < H) *(u32x4 *)(x16 + (size_t)t * H + k) = convert(keep[v]);
   }
+  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8)
+    *(u32x4 *)(x16 + (size_t)t * H + k) = convert(*(const u32x4 *)(row + k));
   if (lane == 0) x_exp[t] = ex;
 }
 

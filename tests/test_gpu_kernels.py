@@ -256,11 +256,13 @@ def _expert_case(T, k, E, H, I, seed):
 # Shapes chosen to reach every kernel variant: GEMV mode with 8-row tiles
 # (1 and 2 row groups, experts split over several tiles), GEMV mode with
 # 16-row tiles (1 to 4 row groups), and the LDS-tiled GEMM with 32- and
-# 64-row tiles; odd H / I multiples of 64 leave partial K units.
+# 64-row tiles; odd H / I multiples of 64 leave partial K units; H = 4160
+# takes the prep path for rows longer than the registers keep.
 @pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (5, 2, 8, 128, 64), (16, 2, 8, 128, 64),
                                        (24, 4, 16, 256, 128), (37, 4, 8, 192, 128),
                                        (100, 4, 8, 128, 64), (300, 2, 4, 256, 64),
-                                       (100, 4, 8, 192, 128), (200, 2, 4, 64, 64)])
+                                       (100, 4, 8, 192, 128), (200, 2, 4, 64, 64),
+                                       (3, 1, 2, 4160, 64)])
 def test_expert_mlp_small(T, k, E, H, I):
     c, idx = _expert_case(T, k, E, H, I, seed=T)
     layer = W.build_small_layer(c, k)
