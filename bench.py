@@ -2,8 +2,9 @@
 """Throughput of the NVFP4 weight-only Gemma-4-26B-A4B MoE expert block on one
 MI355X.
 
-A step is one pass of the whole hot path -- moe_route, moe_bucket, the expert
-MLP (prep, gate/up, down) and moe_combine -- over one batch of seeded synthetic
+A step is one pass of the whole hot path -- routing and bucketing (one
+moe_route_bucket call), the expert MLP (prep, gate/up, down) and moe_combine --
+over one batch of seeded synthetic
 tokens, with inputs and weights already resident in HBM.  The default workload
 is one model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts,
 top-8, expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
@@ -25,6 +26,7 @@ import ctypes
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -35,7 +37,7 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
-STAGES = ("route", "bucket", "prep", "gate_up", "down", "combine")
+STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
 
 
 def parse():
@@ -47,6 +49,8 @@ def parse():
                     help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
                          "3: 30-layer decode sweep")
     ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3 (1 or 8)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the token count of workload 0, 1, 2 or 4 (a size sweep)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
@@ -173,7 +177,10 @@ def main():
 
     torch.cuda.set_device(0)
     moe.lib()
-    wl = S.WORKLOADS[args.workload]
+    wl = dict(S.WORKLOADS[args.workload])
+    if args.tokens and args.workload != 3:
+        wl["T"] = (args.tokens,)
+        wl["name"] = re.sub(r"_T\d+", f"_T{args.tokens}", wl["name"])
     H, I, E, K = S.H, S.I, S.E, S.TOP_K
     t_setup = time.perf_counter()
 
@@ -211,13 +218,13 @@ def main():
     from nvfp4_weight_only_moe_amd import _lib as C
 
     def stage_calls(layer, prep_stream=None):
-        """The six stage calls of one block pass, in STAGES order."""
+        """The five stage calls of one block pass, in STAGES order."""
         return [
-            lambda: C.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
-                                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w,
-                                buf.topk_w_raw, buf.logits, stream),
-            lambda: C.moe_bucket(buf.topk_idx, E, buf.expert_offsets, buf.sorted_pairs,
-                                 buf.pair_rank, buf.bucket_ws, stream),
+            lambda: C.moe_route_bucket(x, layer.w_router, layer.router_scale,
+                                       layer.per_expert_scale, layer.logit_bias, K, layer.eps,
+                                       buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
+                                       buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
+                                       buf.bucket_ws, stream),
             lambda: C.nvfp4_expert_prep(x, E, I, K, buf.ws, prep_stream or stream),
             lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
                                            buf.sorted_pairs, T, K, H, buf.ws, stream),
@@ -235,15 +242,14 @@ def main():
         n = 0
         for layers in step_plan:
             for layer in layers:
-                route, bucket, prep, gate_up, down, combine = stage_calls(layer, side)
+                route_bucket, prep, gate_up, down, combine = stage_calls(layer, side)
                 fork, join = fork_join[n]
                 n += 1
                 hip.record(fork, hs, False)
                 hip.wait(hside, fork)
                 prep()
                 hip.record(join, hside, False)
-                route()
-                bucket()
+                route_bucket()
                 hip.wait(hs, join)
                 gate_up()
                 down()

@@ -13,6 +13,7 @@
  *
  * The hot path is four calls, in this order, on one stream:
  *     moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine
+ * (moe_route_bucket may replace the first two).
  *
  * Conventions for every entry point
  *   - Every pointer is a device pointer owned by the caller (for example
@@ -140,6 +141,25 @@ int moe_bucket(const int32_t *topk_idx, int32_t T, int32_t top_k, int32_t E,
                int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
                void *workspace, size_t ws_bytes, void *stream);
 size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
+
+/*
+ * moe_route_bucket -- moe_route followed by moe_bucket in one call, with the
+ * same arguments as the two calls and the same output bytes (topk_idx,
+ * topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs, pair_rank and the
+ * workspace error word).  For small decode batches (T <= 16, H <= 4096) the
+ * top-k selection and the bucketing run in one workgroup of a single kernel
+ * after the logits kernel (one wave per token), which saves a launch on the
+ * latency-bound decode path; otherwise it issues the two calls.
+ *   workspace  >= moe_bucket_workspace_bytes(T, top_k, E) bytes (as moe_bucket)
+ * Errors: those of moe_route and moe_bucket, checked before any work is
+ * queued.
+ */
+int moe_route_bucket(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+                     const uint16_t *per_expert_scale, const float *logit_bias, int32_t T,
+                     int32_t H, int32_t E, int32_t top_k, float eps, int32_t *topk_idx,
+                     float *topk_w, float *topk_w_raw, float *logits, int32_t *expert_offsets,
+                     int32_t *sorted_pairs, int32_t *pair_rank, void *workspace, size_t ws_bytes,
+                     void *stream);
 
 /*
  * nvfp4_expert_mlp -- every routed (token, expert) pair through its expert:

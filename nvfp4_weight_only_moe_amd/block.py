@@ -76,13 +76,19 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
     record timing events around each stage."""
     xe = x if x_expert is None else x_expert
     mark = marks or (lambda name: None)
-    _lib.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale, layer.logit_bias,
-                   layer.top_k, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
-                   stream)
-    mark("route")
-    _lib.moe_bucket(buf.topk_idx, layer.E, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
-                    buf.bucket_ws, stream)
-    mark("bucket")
+    if marks is None:
+        _lib.moe_route_bucket(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                              layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx, buf.topk_w,
+                              buf.topk_w_raw, buf.logits, buf.expert_offsets, buf.sorted_pairs,
+                              buf.pair_rank, buf.bucket_ws, stream)
+    else:
+        _lib.moe_route(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                       layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx, buf.topk_w,
+                       buf.topk_w_raw, buf.logits, stream)
+        mark("route")
+        _lib.moe_bucket(buf.topk_idx, layer.E, buf.expert_offsets, buf.sorted_pairs,
+                        buf.pair_rank, buf.bucket_ws, stream)
+        mark("bucket")
     if marks is None:
         _lib.nvfp4_expert_mlp(xe, layer.gate, layer.up, layer.down, buf.expert_offsets,
                               buf.sorted_pairs, layer.top_k, buf.y_sorted, buf.ws, stream)

@@ -16,6 +16,7 @@
 // in the wave, per-wave counts in LDS order the waves.  No atomics decide any
 // position, so the output is the same on every run.
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -29,12 +30,15 @@ constexpr int kMaxB = MOE_MAX_EXPERTS + 1;  // buckets incl. the invalid one
 __device__ __forceinline__ int bucket_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
 
 // Stable scatter of the n bucket ids in s_b (pairs pbase .. pbase+n-1),
-// starting from the per-bucket positions in s_run (updated in place).
+// starting from the per-bucket positions in s_run (updated in place), by a
+// workgroup of THREADS threads.
+template <int THREADS = kBucketThreads>
 __device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_run,
                                int (*s_wcnt)[kMaxB], int32_t *sorted, int32_t *rank) {
+  constexpr int WAVES = THREADS / kWave;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int base = 0; base < n; base += kBucketThreads) {
+  for (int base = 0; base < n; base += THREADS) {
     const int i = base + tid;
     const bool valid = i < n;
     const int b = valid ? s_b[i] : 0;
@@ -57,10 +61,10 @@ __device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_
       rank[p] = pos;
     }
     __syncthreads();
-    for (int bb = tid; bb < nb; bb += kBucketThreads) {
+    for (int bb = tid; bb < nb; bb += THREADS) {
       int s = 0;
 #pragma unroll
-      for (int w = 0; w < kBucketWaves; ++w) {
+      for (int w = 0; w < WAVES; ++w) {
         s += s_wcnt[w][bb];
         s_wcnt[w][bb] = 0;
       }
@@ -70,8 +74,9 @@ __device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_
   }
 }
 
+template <int THREADS = kBucketThreads>
 __device__ void zero_wcnt(int (*s_wcnt)[kMaxB], int nb) {
-  for (int i = threadIdx.x; i < kBucketWaves * nb; i += kBucketThreads) s_wcnt[i / nb][i % nb] = 0;
+  for (int i = threadIdx.x; i < THREADS / kWave * nb; i += THREADS) s_wcnt[i / nb][i % nb] = 0;
 }
 
 // Exclusive scan of cnt[0..nb) into out[0..nb) by the first wave (nb <= 257).
@@ -93,20 +98,21 @@ __device__ void wave_exclusive_scan(const int *cnt, int *out, int nb) {
   }
 }
 
-__global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *__restrict__ idx,
-                                                                 int P, int E,
-                                                                 int32_t *__restrict__ offsets,
-                                                                 int32_t *__restrict__ sorted,
-                                                                 int32_t *__restrict__ rank,
-                                                                 int32_t *__restrict__ err) {
+// Every step of the bucketing for P <= kSmallP pairs by one workgroup of
+// THREADS threads: LDS histogram, scan, stable scatter.
+template <int THREADS>
+__device__ __forceinline__ void bucket_small(const int32_t *__restrict__ idx, int P, int E,
+                                             int32_t *__restrict__ offsets,
+                                             int32_t *__restrict__ sorted,
+                                             int32_t *__restrict__ rank, int32_t *__restrict__ err) {
   __shared__ int s_b[kSmallP];
   __shared__ int s_cnt[kMaxB], s_run[kMaxB];
-  __shared__ int s_wcnt[kBucketWaves][kMaxB];
+  __shared__ int s_wcnt[THREADS / kWave][kMaxB];
   const int tid = threadIdx.x, nb = E + 1;
-  for (int i = tid; i < nb; i += kBucketThreads) s_cnt[i] = 0;
-  zero_wcnt(s_wcnt, nb);
+  for (int i = tid; i < nb; i += THREADS) s_cnt[i] = 0;
+  zero_wcnt<THREADS>(s_wcnt, nb);
   __syncthreads();
-  for (int p = tid; p < P; p += kBucketThreads) {
+  for (int p = tid; p < P; p += THREADS) {
     const int b = bucket_of(idx[p], E);
     s_b[p] = b;
     atomicAdd(&s_cnt[b], 1);
@@ -114,10 +120,35 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *
   __syncthreads();
   wave_exclusive_scan(s_cnt, s_run, nb);
   __syncthreads();
-  for (int i = tid; i < nb; i += kBucketThreads) offsets[i] = s_run[i];
+  for (int i = tid; i < nb; i += THREADS) offsets[i] = s_run[i];
   if (tid == 0) err[0] = s_cnt[E];
   __syncthreads();
-  scatter_rounds(s_b, P, 0, nb, s_run, s_wcnt, sorted, rank);
+  scatter_rounds<THREADS>(s_b, P, 0, nb, s_run, s_wcnt, sorted, rank);
+}
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *__restrict__ idx,
+                                                                 int P, int E,
+                                                                 int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ sorted,
+                                                                 int32_t *__restrict__ rank,
+                                                                 int32_t *__restrict__ err) {
+  bucket_small<kBucketThreads>(idx, P, E, offsets, sorted, rank, err);
+}
+
+// Selection and bucketing of a decode batch in one workgroup (one launch
+// instead of two): wave w selects for tokens w, w + 16, ... from the logits,
+// then the workgroup buckets the chosen ids (read back after the barrier,
+// which makes the workgroup's global writes visible to all its waves).
+constexpr int kFusedThreads = 1024;
+__global__ __launch_bounds__(kFusedThreads) void k_select_bucket(
+    const float *__restrict__ logits, const uint16_t *__restrict__ pes, int T, int E, int K,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ rank,
+    int32_t *__restrict__ err) {
+  for (int t = threadIdx.x >> 6; t < T; t += kFusedThreads / kWave)
+    select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
+  __syncthreads();
+  bucket_small<kFusedThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket_hist(const int32_t *__restrict__ idx,
@@ -172,10 +203,10 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_scatter(
   const int tid = threadIdx.x, nb = E + 1, c = blockIdx.x;
   const int p0 = c * kChunk, n = min(P, p0 + kChunk) - p0;
   for (int i = tid; i < nb; i += kBucketThreads) s_run[i] = chunk_base[(size_t)c * nb + i];
-  zero_wcnt(s_wcnt, nb);
+  zero_wcnt<kBucketThreads>(s_wcnt, nb);
   for (int i = tid; i < n; i += kBucketThreads) s_b[i] = bucket_of(idx[p0 + i], E);
   __syncthreads();
-  scatter_rounds(s_b, n, p0, nb, s_run, s_wcnt, sorted, rank);
+  scatter_rounds<kBucketThreads>(s_b, n, p0, nb, s_run, s_wcnt, sorted, rank);
 }
 
 size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_off) {
@@ -188,6 +219,21 @@ size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_o
 }
 
 }  // namespace
+}  // namespace moe
+
+namespace moe {
+// Selection + bucketing in one launch for T tokens with T * top_k <= kSmallP
+// (arguments validated by the caller, moe_route_bucket).
+__attribute__((visibility("hidden"))) int launch_select_bucket(
+                         const float *logits, const uint16_t *pes, int T, int E, int top_k,
+                         int32_t *topk_idx, float *topk_w, float *topk_w_raw,
+                         int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+                         void *workspace, hipStream_t s) {
+  MOE_LAUNCH(k_select_bucket, dim3(1), dim3(kFusedThreads), 0, s, logits, pes, T, E, top_k,
+             topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs, pair_rank,
+             (int32_t *)workspace);
+  return MOE_OK;
+}
 }  // namespace moe
 
 extern "C" size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {

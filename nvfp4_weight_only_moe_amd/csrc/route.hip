@@ -22,6 +22,7 @@
 // k rounds of a wave arg-max (ties to the lower id), renormalisation over the
 // k chosen probabilities, times per_expert_scale.
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -263,84 +264,23 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
                                                       int E, int K, int32_t *__restrict__ topk_idx,
                                                       float *__restrict__ topk_w,
                                                       float *__restrict__ topk_w_raw) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float *lg = logits + (size_t)t * E;
-  constexpr int kPer = MOE_MAX_EXPERTS / kWave;  // 4
-  float v[kPer];
-  float m = -__builtin_huge_valf();
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + i * kWave;
-    v[i] = e < E ? lg[e] : -__builtin_huge_valf();
-    m = fmaxf(m, v[i]);
-  }
-  // per_expert_scale of this lane's experts, loaded up front (no dependent
-  // load after the selection)
-  float pv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + i * kWave;
-    pv[i] = e < E ? bf16_to_f32(pes[e]) : 0.0f;
-  }
-  m = wave_max(m);
-  float z = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) z += (lane + i * kWave < E) ? expf(v[i] - m) : 0.0f;
-  z = wave_sum(z);
-  const float inv_z = 1.0f / z;
-
-  uint32_t taken = 0;  // bit i: my element lane + 64 i is already chosen
-  int my_id = -1;      // lane j (< K) keeps the j-th selection
-  float my_p = 0.0f, my_pes = 0.0f;
-  float psum = 0.0f;
-  for (int s = 0; s < K; ++s) {
-    // lane-local best (largest logit, lowest id among equals)
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = lane + i * kWave;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    // per_expert_scale of the winner, from the lane that holds it
-    float pw = pv[0];
-#pragma unroll
-    for (int i = 1; i < kPer; ++i)
-      if (bi / kWave == i) pw = pv[i];
-    pw = __shfl(pw, bi & (kWave - 1), kWave);
-    const float p = expf(bv - m) * inv_z;
-    psum += p;
-    if (lane == s) {
-      my_id = bi;
-      my_p = p;
-      my_pes = pw;
-    }
-  }
-  if (lane < K) {
-    const float wr = my_p / psum;
-    topk_idx[(size_t)t * K + lane] = my_id;
-    topk_w[(size_t)t * K + lane] = wr * my_pes;
-    if (topk_w_raw) topk_w_raw[(size_t)t * K + lane] = wr;
-  }
+  select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
 }
 
 }  // namespace
 }  // namespace moe
+
+namespace moe {
+// Largest batch whose selection and bucketing run in one workgroup
+// (moe_route_bucket); larger batches select over many workgroups.
+constexpr int kFusedMaxT = 16;
+int launch_select_bucket(const float *logits, const uint16_t *pes, int T, int E, int top_k,
+                         int32_t *topk_idx, float *topk_w, float *topk_w_raw,
+                         int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+                         void *workspace, hipStream_t s);
+}
 
 extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
                          const uint16_t *per_expert_scale, const float *logit_bias, int32_t T,
@@ -372,4 +312,47 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
   MOE_LAUNCH(k_route_select, dim3((T + 3) / 4), dim3(256), 0, s, logits, per_expert_scale,
                      T, E, top_k, topk_idx, topk_w, topk_w_raw);
   return MOE_OK;
+}
+
+extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
+                                const uint16_t *router_scale, const uint16_t *per_expert_scale,
+                                const float *logit_bias, int32_t T, int32_t H, int32_t E,
+                                int32_t top_k, float eps, int32_t *topk_idx, float *topk_w,
+                                float *topk_w_raw, float *logits, int32_t *expert_offsets,
+                                int32_t *sorted_pairs, int32_t *pair_rank, void *workspace,
+                                size_t ws_bytes, void *stream) {
+  using namespace moe;
+  // the checks of moe_route and moe_bucket, before anything is queued
+  if (!w_router || !router_scale || !per_expert_scale || !expert_offsets || !workspace)
+    return MOE_ERR_NULL;
+  if (T > 0 && (!x || !topk_idx || !topk_w || !logits || !sorted_pairs || !pair_rank))
+    return MOE_ERR_NULL;
+  if (T < 0 || H <= 0 || H % 64 || E <= 0 || top_k <= 0 || top_k > E) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS || E % 16 || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
+  if (ws_bytes < moe_bucket_workspace_bytes(T, top_k, E)) return MOE_ERR_WORKSPACE;
+  const int nv = (H + 511) / 512;
+  if (T > kFusedMaxT || nv > kFewMaxV || T * top_k > 4096) {
+    const int st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
+                             top_k, eps, topk_idx, topk_w, topk_w_raw, logits, stream);
+    if (st != MOE_OK) return st;
+    return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
+                      ws_bytes, stream);
+  }
+  if (T == 0)  // empty batch: the offsets are all zero, as moe_bucket writes them
+    return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
+                      ws_bytes, stream);
+  hipStream_t s = (hipStream_t)stream;
+  switch (nv) {
+#define MOE_FEW(NV)                                                                          \
+  case NV:                                                                                   \
+    MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, \
+               router_scale, logit_bias, T, H, E, eps, logits);                              \
+    break;
+    MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
+    default: MOE_FEW(8)
+#undef MOE_FEW
+  }
+  return launch_select_bucket(logits, per_expert_scale, T, E, top_k, topk_idx, topk_w, topk_w_raw,
+                              expert_offsets, sorted_pairs, pair_rank, workspace, s);
 }

@@ -27,7 +27,7 @@ def L():
 
 def test_header_declares_the_hot_path():
     names = _declared()
-    for n in ("moe_route", "moe_bucket", "nvfp4_expert_mlp", "moe_combine"):
+    for n in ("moe_route", "moe_bucket", "moe_route_bucket", "nvfp4_expert_mlp", "moe_combine"):
         assert n in names
 
 
@@ -75,6 +75,25 @@ def test_bucket_rejects(L):
     assert L.moe_bucket(FAKE, 64, 17, 128, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -4
     assert L.moe_bucket(FAKE, 64, 8, 300, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -4
     assert L.moe_bucket(FAKE, -2, 8, 128, FAKE, FAKE, FAKE, FAKE, ws, NULL) == -2
+
+
+def test_route_bucket_rejects(L):
+    ws = L.moe_bucket_workspace_bytes(64, 8, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, NULL, 64, 2816, 128, 8, 1e-6, FAKE, FAKE, NULL, FAKE,
+            FAKE, FAKE, FAKE, FAKE, ws, NULL]
+    assert L.moe_route_bucket(*args[:18], ws - 1, NULL) == -3   # bucket workspace too small
+    a = list(args); a[17] = NULL
+    assert L.moe_route_bucket(*a) == -1                          # workspace NULL
+    a = list(args); a[15] = NULL
+    assert L.moe_route_bucket(*a) == -1                          # sorted_pairs NULL with T > 0
+    a = list(args); a[6] = 2800
+    assert L.moe_route_bucket(*a) == -2                          # H % 64
+    a = list(args); a[7] = 120
+    assert L.moe_route_bucket(*a) == -4                          # E % 16
+    a = list(args); a[8] = 17
+    assert L.moe_route_bucket(*a) == -4                          # top_k > 16
+    a = list(args); a[5] = -1
+    assert L.moe_route_bucket(*a) == -2
 
 
 def _tensor(E, N, K, layout=1):

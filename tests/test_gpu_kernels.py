@@ -245,6 +245,54 @@ def test_bucket_invalid_ids_counted_and_parked(T):
     assert off[E] == T * k - err
 
 
+# ---------------------------------------------- fused routing + bucketing
+@pytest.mark.parametrize("T,H,E,k", [(0, 2816, 128, 8), (1, 2816, 128, 8), (4, 2816, 128, 8), (16, 2816, 128, 8),
+                                     (17, 2816, 128, 8), (64, 2816, 128, 8), (65, 2816, 128, 8),
+                                     (333, 2816, 128, 8), (9, 192, 16, 3), (64, 4096, 256, 16),
+                                     (30, 4160, 32, 4)])
+def test_route_bucket_matches_oracle_and_separate_calls(T, H, E, k):
+    """moe_route_bucket: the routing against the oracle (the same bar as
+    moe_route), the bucketing bit-exact against the oracle's bucketing of the
+    experts it chose, and every output byte equal to moe_route + moe_bucket."""
+    router = S.router_params(E % 7, h=H, e=E, zipf=(T == 17))
+    x = S.activations(93, T, h=H)
+    wr, sc, pes, bias = W.router_to_device(router)
+    xd = _bits(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    wsb = moe.moe_bucket_workspace_bytes(T, k, E)
+
+    def outs():
+        return dict(idx=torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+                    w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                    w_raw=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                    lg=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                    off=torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+                    sp=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+                    pr=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+                    ws=torch.full((wsb,), 0x55, dtype=torch.uint8, device="cuda"))
+    a, b = outs(), outs()
+    moe.moe_route_bucket(xd, wr, sc, pes, bias, k, 1e-6, a["idx"], a["w"], a["w_raw"], a["lg"],
+                         a["off"], a["sp"], a["pr"], a["ws"])
+    moe.moe_route(xd, wr, sc, pes, bias, k, 1e-6, b["idx"], b["w"], b["w_raw"], b["lg"])
+    moe.moe_bucket(b["idx"], E, b["off"], b["sp"], b["pr"], b["ws"])
+    torch.cuda.synchronize()
+    for n in ("idx", "w", "w_raw", "lg", "off", "sp", "pr"):
+        assert torch.equal(a[n].view(torch.int32), b[n].view(torch.int32)), n
+    assert int(a["ws"][:4].view(torch.int32)[0]) == 0
+    idx = a["idx"].cpu().numpy()
+    ref_b = M.bucket(idx, E)
+    assert np.array_equal(a["off"].cpu().numpy(), ref_b["offsets"])
+    assert np.array_equal(a["sp"].cpu().numpy(), ref_b["sorted_pairs"])
+    assert np.array_equal(a["pr"].cpu().numpy(), ref_b["pair_rank"])
+    if T:
+        r = router_f64(router)
+        ref = M.route(F.bf16_bits_to_f64(x), r["w_router"], r["scale"], r["per_expert_scale"], k,
+                      r["bias"])
+        assert np.max(np.abs(a["lg"].cpu().numpy() - ref["logits"])) <= 2e-7
+        differ = check_route(idx, a["w"].cpu().numpy(), a["w_raw"].cpu().numpy(), ref,
+                             r["per_expert_scale"])
+        assert len(differ) <= max(1, T // 200)
+
+
 # ---------------------------------------------------------------- experts
 def _expert_case(T, k, E, H, I, seed):
     c = S.small_case(seed, T, H, I, E, k)
