@@ -391,9 +391,7 @@ def gate_up_kernel_name(T, K, E):
     avg = P // max(1, min(P, E))
     if avg < 24:
         rows = 8 if P <= 4 * E else 16
-        max_tiles = (P + rows - 1) // rows + min(E, P)
-        split = 4 if ((S_I + 63) // 64) * max_tiles < 1024 else 1
-        return f"k_expert_gemv<{rows}, 1, true, {split}>"
+        return f"k_expert_gemv<{rows}, 2, true, 4>"
     return "k_expert_gemm<4, 2, true>"
 
 

@@ -513,10 +513,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // chunks j in [h NL, h NL + NL) of its rows; the groups are summed once after
 // the K loop.  Every tile costs 4 MFMAs per weight row tile and K unit, and
 // R/4 activation loads per lane.  Units up to kGemvPD ahead are in flight.
+//
+// Weight row tiles per wave (NP): every tile of a wave shares the wave's
+// activation loads, and each activation load costs the CU about as much as a
+// weight load, so more tiles per wave pay off where a unit needs several
+// activation loads (16-row tiles) or where the K split is on.  Gate/up (K =
+// hidden, long) always takes the K split with 2 gate + 2 up tiles per wave:
+// 4x the waves of the unsplit layout, each with a quarter of K.  Down (K =
+// expert intermediate, short) keeps whole-K waves unless its grid is small.
 constexpr int kGemvPD = 1;
-constexpr int kGateNP = 1;  // gate/up row-tile pairs per workgroup
-constexpr int kDownNP = 2;  // down row tiles per workgroup
-// the K split is used when the unsplit grid would have fewer workgroups
+constexpr int kGateNP = 2;       // gate/up row-tile pairs per wave (K split)
+constexpr int kDownNP = 2;       // down row tiles per wave (8-row tiles)
+constexpr int kDownNPWide = 4;   // ... with 16-row tiles
+// down takes the K split when the unsplit grid would have fewer workgroups
 constexpr int kGemvSplitBelow = 1024;
 
 template <int NL, int NW>
@@ -739,9 +748,9 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_list(const int32_t *__res
 // GATED: A = gelu_tanh(X Wg^T) * (X Wu^T) -> A [P][N] bf16; else
 // Y = A Wd^T -> Y [P][N] bf16.  Tiles of ROWS sorted rows from the tile list.
 // KS = 1: the 4 waves take 4 consecutive column groups of NP row tiles, each
-// all of K; KS = 4: the 4 waves share one column group and split K (for
-// batches with few tiles, where whole-K streams per wave would leave HBM
-// idle).
+// all of K; KS = 4: the 4 waves share one column group and split K (gate/up
+// always; down for batches with few tiles, where whole-K streams per wave
+// would leave HBM idle).
 template <int ROWS, int NP, bool GATED, int KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
 void k_expert_gemv(GemvArgs p, const int4 *__restrict__ tiles, Nvfp4 w0, Nvfp4 w1) {
@@ -880,20 +889,15 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
     const int rows = gemv_rows(T, top_k, E);
     MOE_LAUNCH(k_tile_list, dim3(1), dim3(kTileThreads), 0, s, expert_offsets, E, rows,
                w.L.max_tiles, w.tiles);
-    const int gx = (I + 64 * kGateNP - 1) / (64 * kGateNP);  // unsplit: 4 column groups per workgroup
-    const bool split = gx * w.L.max_tiles < kGemvSplitBelow;
-    const dim3 grid(split ? (I + 16 * kGateNP - 1) / (16 * kGateNP) : gx, w.L.max_tiles);
+    // the 4 waves of a workgroup split K for one column group of kGateNP row tiles
+    const dim3 grid((I + 16 * kGateNP - 1) / (16 * kGateNP), w.L.max_tiles);
     const GemvArgs a{w.x16, w.x_exp, w.a_max, sorted_pairs, top_k, H, I, T * top_k,
                      (uint32_t)((size_t)T * H * 2), w.a};
     const int4 *tl = (const int4 *)w.tiles;
-#define MOE_GEMV_GU(ROWS, KS) \
-  MOE_LAUNCH((k_expert_gemv<ROWS, kGateNP, true, KS>), grid, dim3(kThreads), 0, s, a, tl, g, u)
-    if (rows == 8) {
-      if (split) MOE_GEMV_GU(8, 4); else MOE_GEMV_GU(8, 1);
-    } else {
-      if (split) MOE_GEMV_GU(16, 4); else MOE_GEMV_GU(16, 1);
-    }
-#undef MOE_GEMV_GU
+    if (rows == 8)
+      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a, tl, g, u);
+    else
+      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a, tl, g, u);
     return MOE_OK;
   }
   return launch_gate_up<4>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
@@ -913,18 +917,20 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
   Nvfp4 d{down->packed, down->scales, down->global};
   hipStream_t s = (hipStream_t)stream;
   if (gemv_mode(T, top_k, E)) {  // tile list written by nvfp4_expert_gate_up
-    const int gx = (H + 64 * kDownNP - 1) / (64 * kDownNP);
+    const int rows = gemv_rows(T, top_k, E);
+    const int np = rows == 16 ? kDownNPWide : kDownNP;
+    const int gx = (H + 64 * np - 1) / (64 * np);
     const bool split = gx * w.L.max_tiles < kGemvSplitBelow;
-    const dim3 grid(split ? (H + 16 * kDownNP - 1) / (16 * kDownNP) : gx, w.L.max_tiles);
+    const dim3 grid(split ? (H + 16 * np - 1) / (16 * np) : gx, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
     const int4 *tl = (const int4 *)w.tiles;
-#define MOE_GEMV_DN(ROWS, KS) \
-  MOE_LAUNCH((k_expert_gemv<ROWS, kDownNP, false, KS>), grid, dim3(kThreads), 0, s, a, tl, d, d)
-    if (gemv_rows(T, top_k, E) == 8) {
-      if (split) MOE_GEMV_DN(8, 4); else MOE_GEMV_DN(8, 1);
+#define MOE_GEMV_DN(ROWS, NP, KS) \
+  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS>), grid, dim3(kThreads), 0, s, a, tl, d, d)
+    if (rows == 8) {
+      if (split) MOE_GEMV_DN(8, kDownNP, 4); else MOE_GEMV_DN(8, kDownNP, 1);
     } else {
-      if (split) MOE_GEMV_DN(16, 4); else MOE_GEMV_DN(16, 1);
+      if (split) MOE_GEMV_DN(16, kDownNPWide, 4); else MOE_GEMV_DN(16, kDownNPWide, 1);
     }
 #undef MOE_GEMV_DN
     return MOE_OK;

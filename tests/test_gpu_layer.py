@@ -91,6 +91,16 @@ def test_layer_T64_all_tokens(layer0, oracle_experts):
     print(f"T=64 rel_frob={err:.3e} worst_row={worst_row:.3e}")
 
 
+@pytest.mark.parametrize("T", [16, 128])
+def test_layer_decode_sizes_all_tokens(layer0, oracle_experts, T):
+    # T = 16: GEMV with the K split; T = 128: 16-row GEMV tiles, unsplit
+    x = S.activations(5, T)
+    buf = _run(layer0, x)
+    err, worst_row = _check_block(buf, x, S.router_params(0), oracle_experts)
+    assert worst_row <= 1e-2
+    print(f"T={T} rel_frob={err:.3e} worst_row={worst_row:.3e}")
+
+
 def test_layer_T2048_zipf_sampled(layer0_zipf, oracle_experts):
     x = S.activations(2, 2048)
     buf = _run(layer0_zipf, x)
