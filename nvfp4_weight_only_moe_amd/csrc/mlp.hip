@@ -48,7 +48,7 @@ struct Nvfp4 {
 };
 
 struct WsLayout {
-  size_t tiles, x_exp, a_max, x16, a, total;
+  size_t x_exp, a_max, x16, a, total;
   int max_tiles;
 };
 
@@ -73,16 +73,15 @@ int tile_rows(int T, int top_k, int E) {
   return gemv_mode(T, top_k, E) ? gemv_rows(T, top_k, E) : kBM * choose_msub(T, top_k, E);
 }
 
-// Workspace: the GEMV-mode tile list [max_tiles] int4, token exponents [T],
-// per-row max of A [P], the f16 activations [T][H], A [P][I] bf16.
+// Workspace: token exponents [T], per-row max of A [P], the f16 activations
+// [T][H], A [P][I] bf16.  max_tiles bounds the tile count (sum over experts
+// of ceil(M_e / rows)) for the grids.
 WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
   WsLayout L;
   const size_t P = (size_t)T * top_k;
   const int bm = tile_rows(T, top_k, E);
   L.max_tiles = (int)((P + bm - 1) / bm + (size_t)(E < (int)P ? E : (int)P));
-  const bool gemv = gemv_mode(T, top_k, E);
-  L.tiles = 0;
-  L.x_exp = L.tiles + (gemv ? moe_align_up((size_t)L.max_tiles * 16, 256) : 0);
+  L.x_exp = 0;
   L.a_max = L.x_exp + moe_align_up((size_t)T * 4, 256);
   L.x16 = L.a_max + moe_align_up(P * 4, 256);
   L.a = L.x16 + moe_align_up((size_t)T * H * 2, 256);
@@ -710,39 +709,62 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   }
 }
 
-// The GEMV-mode tile list: tile i = (expert, first sorted row, rows) for
-// "expert e contributes ceil(M_e / rows) tiles of rows rows", in expert order;
-// entries up to max_tiles past the last tile get expert -1.  One workgroup:
-// per-expert counts, a scan in LDS, then each thread writes its experts'
-// tiles.  Computed once per launch so that every GEMV workgroup finds its
-// tile with a single scalar load.
-constexpr int kTileThreads = 256;
-__global__ __launch_bounds__(kTileThreads) void k_tile_list(const int32_t *__restrict__ offsets,
-                                                            int E, int rows, int max_tiles,
-                                                            int4 *__restrict__ tiles) {
-  __shared__ int s_cnt[kTileThreads];
-  const int tid = threadIdx.x;
-  int base = 0, m = 0, c = 0;
-  if (tid < E) {
-    base = offsets[tid];
-    m = offsets[tid + 1] - base;
-    c = (m + rows - 1) / rows;
+// Tile y of the GEMV grid, for "expert e contributes ceil(M_e / rows) tiles
+// of rows rows, in expert order": each wave finds it from the expert offsets
+// (E + 1 ints, L2-resident) with a DPP prefix sum over the per-expert tile
+// counts -- about the latency of one load, so no separate tile-list kernel.
+// Lane l takes experts PER*l .. PER*l + PER - 1.  Returns false when y is at
+// or past the tile count (uniform).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_zero_fill(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_zero_fill<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_zero_fill<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_zero_fill<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_zero_fill<0x118, 0xF>(v);  // row_shr:8 (rows of 16 now scanned)
+  v += dpp_zero_fill<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
+                                          int y, int &e, int &row0, int &mrows) {
+  constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4u);
+  int off[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i)
+    off[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ro, (uint32_t)(PER * lane + i) * 4u, 0, 0);
+  int c[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = PER * lane + i < E ? (off[i + 1] - off[i] + rows - 1) / rows : 0;
+    sum += c[i];
   }
-  // inclusive scan of c over the first E threads (E <= 256): Hillis-Steele in LDS
-  s_cnt[tid] = c;
-  __syncthreads();
-  for (int o = 1; o < kTileThreads; o <<= 1) {
-    const int v = tid >= o ? s_cnt[tid - o] : 0;
-    __syncthreads();
-    s_cnt[tid] += v;
-    __syncthreads();
+  const int incl = wave_incl_scan(sum);
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (y >= total) return false;
+  const int excl = incl - sum;
+  const unsigned long long hit = __ballot(y >= excl && y < incl);
+  const int src = (int)__builtin_ctzll(hit);
+  // the owning lane resolves which of its experts and which tile of it
+  int ee = 0, r0 = 0, mr = 0, base = excl;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (y >= base && y < base + c[i]) {
+      const int t = y - base;
+      ee = PER * lane + i;
+      r0 = off[i] + t * rows;
+      mr = min(rows, off[i + 1] - r0);
+    }
+    base += c[i];
   }
-  const int total = s_cnt[E - 1];
-  if (tid < E) {
-    const int first = s_cnt[tid] - c;
-    for (int i = 0; i < c; ++i) tiles[first + i] = int4{tid, base + i * rows, min(rows, m - i * rows), 0};
-  }
-  for (int i = total + tid; i < max_tiles; i += kTileThreads) tiles[i] = int4{-1, 0, 0, 0};
+  e = __builtin_amdgcn_readlane(ee, src);
+  row0 = __builtin_amdgcn_readlane(r0, src);
+  mrows = __builtin_amdgcn_readlane(mr, src);
+  return true;
 }
 
 // GATED: A = gelu_tanh(X Wg^T) * (X Wu^T) -> A [P][N] bf16; else
@@ -753,15 +775,14 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_list(const int32_t *__res
 // would leave HBM idle).
 template <int ROWS, int NP, bool GATED, int KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
-void k_expert_gemv(GemvArgs p, const int4 *__restrict__ tiles, Nvfp4 w0, Nvfp4 w1) {
+void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets, int E, Nvfp4 w0, Nvfp4 w1) {
   constexpr int NW = GATED ? 2 * NP : NP;
   __shared__ __attribute__((aligned(16))) float s_red[KS > 1 ? KS * 64 * NW * 4 : 4];
   const int wave = threadIdx.x >> 6;
   const int nt0 = KS == 1 ? (blockIdx.x * 4 + wave) * NP : blockIdx.x * NP;  // first row tile
   if (nt0 * 16 >= p.N) return;  // past the last column (KS = 4: uniform; KS = 1: no barrier follows)
-  const int4 tile = tiles[blockIdx.y];  // uniform address: one scalar load
-  const int e = tile.x, row0 = tile.y, mrows = tile.z;
-  if (e < 0) return;  // uniform
+  int e, row0, mrows;
+  if (!find_tile(offsets, E, ROWS, blockIdx.y, e, row0, mrows)) return;  // uniform
   // rows per MFMA block: the smallest packing that holds the tile (uniform)
   if (mrows <= 4) gemv_run<4, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
   else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
@@ -786,7 +807,6 @@ using namespace moe;
 
 struct Ws {
   WsLayout L;
-  int4 *tiles;
   int32_t *x_exp;
   uint32_t *a_max;
   uint16_t *x16, *a;
@@ -796,7 +816,6 @@ Ws ws_ptrs(void *workspace, const WsLayout &L) {
   char *ws = (char *)workspace;
   Ws w;
   w.L = L;
-  w.tiles = (int4 *)(ws + L.tiles);
   w.x_exp = (int32_t *)(ws + L.x_exp);
   w.a_max = (uint32_t *)(ws + L.a_max);
   w.x16 = (uint16_t *)(ws + L.x16);
@@ -887,17 +906,16 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
   hipStream_t s = (hipStream_t)stream;
   if (gemv_mode(T, top_k, E)) {
     const int rows = gemv_rows(T, top_k, E);
-    MOE_LAUNCH(k_tile_list, dim3(1), dim3(kTileThreads), 0, s, expert_offsets, E, rows,
-               w.L.max_tiles, w.tiles);
     // the 4 waves of a workgroup split K for one column group of kGateNP row tiles
     const dim3 grid((I + 16 * kGateNP - 1) / (16 * kGateNP), w.L.max_tiles);
     const GemvArgs a{w.x16, w.x_exp, w.a_max, sorted_pairs, top_k, H, I, T * top_k,
                      (uint32_t)((size_t)T * H * 2), w.a};
-    const int4 *tl = (const int4 *)w.tiles;
     if (rows == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a, tl, g, u);
+      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a,
+                 expert_offsets, E, g, u);
     else
-      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a, tl, g, u);
+      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a,
+                 expert_offsets, E, g, u);
     return MOE_OK;
   }
   return launch_gate_up<4>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
@@ -916,7 +934,7 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
   Nvfp4 d{down->packed, down->scales, down->global};
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_mode(T, top_k, E)) {  // tile list written by nvfp4_expert_gate_up
+  if (gemv_mode(T, top_k, E)) {
     const int rows = gemv_rows(T, top_k, E);
     const int np = rows == 16 ? kDownNPWide : kDownNP;
     const int gx = (H + 64 * np - 1) / (64 * np);
@@ -924,9 +942,9 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
     const dim3 grid(split ? (H + 16 * np - 1) / (16 * np) : gx, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
-    const int4 *tl = (const int4 *)w.tiles;
-#define MOE_GEMV_DN(ROWS, NP, KS) \
-  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS>), grid, dim3(kThreads), 0, s, a, tl, d, d)
+#define MOE_GEMV_DN(ROWS, NP, KS)                                                         \
+  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS>), grid, dim3(kThreads), 0, s, a, expert_offsets, \
+             E, d, d)
     if (rows == 8) {
       if (split) MOE_GEMV_DN(8, kDownNP, 4); else MOE_GEMV_DN(8, kDownNP, 1);
     } else {
