@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t *__r
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+      o[i] = f32x2_to_bf16x2(acc[2 * i], acc[2 * i + 1]);
     *(u32x4 *)(out + (size_t)t * H + c) = o;
   }
 }

@@ -29,6 +29,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// round to nearest even by the hardware conversion (one instruction; a NaN
+// becomes a quiet NaN): for results that are never NaN by construction
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
 // ---- NVFP4 decode ----------------------------------------------------------
 // E2M1 x E4M3 products have at most 6 significant bits and lie in
 // [2^-10, 2688]: exact in f16.  So a block decodes as: hardware FP4 -> f16
@@ -87,6 +96,24 @@ __device__ __forceinline__ int row_exponent(float amax) {
   int e;
   (void)__builtin_frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
   return e - 1;                      // floor(log2 amax)
+}
+
+// Maximum over the 16 lanes of each DPP row (lanes 16g .. 16g + 15), in every
+// lane of the row: DPP moves (xor 1, xor 2, half-row mirror, row mirror)
+// instead of LDS permutes.  Unsigned: non-negative floats compare like their
+// bit patterns.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+// |b| of a bf16 as the bit pattern of an f32 (ordered like the magnitudes;
+// NaN counts as 0)
+__device__ __forceinline__ uint32_t bf16_abs_bits(uint16_t b) {
+  const uint32_t mag = b & 0x7FFFu;
+  return mag > 0x7F80u ? 0u : mag << 16;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

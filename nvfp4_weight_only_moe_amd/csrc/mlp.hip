@@ -151,9 +151,14 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
   if (lane == 0) x_exp[t] = ex;
 }
 
+// gelu_tanh(g) = 0.5 g (1 + tanh(u)), u = sqrt(2/pi) (g + 0.044715 g^3), in the
+// equal form g / (1 + exp(-2u)) (1 + tanh(u) = 2 / (1 + exp(-2u))): one
+// hardware exp2 and one reciprocal (each about 1 ulp) instead of a tanh.
+// Large |u| saturates correctly: exp -> inf gives 0, exp -> 0 gives g.
 __device__ __forceinline__ float gelu_tanh(float g) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+  const float c2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float t = c2 * (g + 0.044715f * g * g * g);
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // ------------------------------------------------- grouped expert GEMM ----
@@ -180,37 +185,61 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 constexpr int kUnitK = 128;
 constexpr int kXcds = 8;
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts, then the
+// row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_zero_fill(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_zero_fill<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_zero_fill<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_zero_fill<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_zero_fill<0x118, 0xF>(v);  // row_shr:8 (rows of 16 now scanned)
+  v += dpp_zero_fill<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
 // Logical block `L` of the order (expert e, column block cb, row block m):
-// expert e holds ceil(M_e / bm) * ncb consecutive blocks.  One wave-wide scan
+// expert e holds ceil(M_e / bm) * ncb consecutive blocks.  Lane l takes
+// experts PER*l .. PER*l + PER - 1; one DPP prefix sum over the lanes
 // (scalar results).  False past the last block.
 __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int ncb, int L,
                            int &e, int &m0, int &cb) {
+  constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
   const int lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < E; base += kWave) {
-    const int ee = base + lane;
-    const int c = ee < E ? (offsets[ee + 1] - offsets[ee] + bm - 1) / bm * ncb : 0;
-    int incl = c;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4u);
+  int off[PER + 1];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += u;
-    }
-    const int total = carry + __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
-    if (L < total) {
-      const bool hit = L >= carry + incl - c && L < carry + incl;
-      const unsigned long long mask = __ballot(hit);
-      const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)mask) - 1);
-      e = base + src;
-      const int rem = L - carry - __builtin_amdgcn_readfirstlane(__shfl(incl - c, src, kWave));
-      const int nblk = __builtin_amdgcn_readfirstlane(__shfl(c, src, kWave)) / ncb;
-      cb = rem / nblk;
-      m0 = (rem - cb * nblk) * bm;
-      return true;
-    }
-    carry = total;
+  for (int i = 0; i <= PER; ++i)
+    off[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ro, (uint32_t)(PER * lane + i) * 4u, 0, 0);
+  int nblk[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    nblk[i] = PER * lane + i < E ? (off[i + 1] - off[i] + bm - 1) / bm : 0;
+    sum += nblk[i] * ncb;
   }
-  return false;
+  const int incl = wave_incl_scan(sum);
+  if (L >= __builtin_amdgcn_readlane(incl, kWave - 1)) return false;
+  const int excl = incl - sum;
+  const int src = (int)__builtin_ctzll(__ballot(L >= excl && L < incl));
+  int ee = 0, rem = 0, nb = 1, base = excl;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = nblk[i] * ncb;
+    if (L >= base && L < base + n) {
+      rem = L - base;
+      ee = PER * lane + i;
+      nb = nblk[i];
+    }
+    base += n;
+  }
+  e = __builtin_amdgcn_readlane(ee, src);
+  rem = __builtin_amdgcn_readlane(rem, src);
+  nb = __builtin_amdgcn_readlane(nb, src);
+  cb = rem / nb;  // scalar
+  m0 = (rem - cb * nb) * bm;
+  return true;
 }
 
 // LDS layout of the activation block: [rows][128] f16, no padding; the
@@ -447,17 +476,16 @@ __device__ __forceinline__ void gemm_run(
         const int m = q * kBM + 4 * g + jj;
         const bool ok = m < mrows;
         const float f = s_rowscale[m];
-        float rmax = 0.0f;
+        uint32_t rmax = 0;  // max |A| of the row (f32 bits)
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const float G = acc[q][i][jj] * (gg * f), U = acc[q][NP + i][jj] * (gu * f);
-          const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
+          const uint16_t ab = f32_to_bf16_rne(gelu_tanh(G) * U);
           if (ok) out[(size_t)(row0 + m) * N + (nt0 + i) * 16 + r] = ab;
-          rmax = fmaxf(rmax, ok ? fabsf(bf16_to_f32(ab)) : 0.0f);
+          rmax = max(rmax, ok ? bf16_abs_bits(ab) : 0u);
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, kWave));
-        if (r == 0 && ok) atomicMax(&a_max[row0 + m], __float_as_uint(rmax));
+        rmax = row16_max_u32(rmax);
+        if (r == 0 && ok) atomicMax(&a_max[row0 + m], rmax);
       }
     }
   } else {
@@ -473,7 +501,7 @@ __device__ __forceinline__ void gemm_run(
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
             const int n = (nt0 + i) * 16 + r;
-            if (n < N) out[(size_t)(row0 + m) * N + n] = f32_to_bf16(acc[q][i][jj] * f);
+            if (n < N) out[(size_t)(row0 + m) * N + n] = f32_to_bf16_rne(acc[q][i][jj] * f);
           }
         }
       }
@@ -679,17 +707,16 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       const bool ok = mr < R && mr < mrows;
       float f = 0.0f;
       if (ok) f = __builtin_ldexpf(1.0f, p.x_exp[p.sorted_pairs[row0 + mr] / p.top_k] - 14);
-      float rmax = 0.0f;
+      uint32_t rmax = 0;  // max |A| of the row (f32 bits)
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const float G = acc[i][jj] * (gg * f), U = acc[NP + i][jj] * (gu * f);
-        const uint16_t ab = f32_to_bf16(gelu_tanh(G) * U);
+        const uint16_t ab = f32_to_bf16_rne(gelu_tanh(G) * U);
         if (ok) p.out[(size_t)(row0 + mr) * N + (nt0 + i) * 16 + r] = ab;
-        rmax = fmaxf(rmax, ok ? fabsf(bf16_to_f32(ab)) : 0.0f);
+        rmax = max(rmax, ok ? bf16_abs_bits(ab) : 0u);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, kWave));
-      if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], __float_as_uint(rmax));
+      rmax = row16_max_u32(rmax);
+      if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], rmax);
     }
   } else {
     const float gd = w0.global[e];
@@ -702,7 +729,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const int n = (nt0 + i) * 16 + r;
-          if (n < N) p.out[(size_t)(row0 + mr) * N + n] = f32_to_bf16(acc[i][jj] * f);
+          if (n < N) p.out[(size_t)(row0 + mr) * N + n] = f32_to_bf16_rne(acc[i][jj] * f);
         }
       }
     }
@@ -715,19 +742,6 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
 // counts -- about the latency of one load, so no separate tile-list kernel.
 // Lane l takes experts PER*l .. PER*l + PER - 1.  Returns false when y is at
 // or past the tile count (uniform).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_zero_fill(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
-}
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += dpp_zero_fill<0x111, 0xF>(v);  // row_shr:1
-  v += dpp_zero_fill<0x112, 0xF>(v);  // row_shr:2
-  v += dpp_zero_fill<0x114, 0xF>(v);  // row_shr:4
-  v += dpp_zero_fill<0x118, 0xF>(v);  // row_shr:8 (rows of 16 now scanned)
-  v += dpp_zero_fill<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
                                           int y, int &e, int &row0, int &mrows) {
   constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
