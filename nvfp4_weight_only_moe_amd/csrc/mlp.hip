@@ -253,6 +253,13 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
+// Register budget of the K loop: weight register sets of the LDS-direct
+// (gate/up) pipeline (3: weights two units ahead; 2: one unit ahead) and
+// activation fragment sets (2: the next step's fragments are read from LDS
+// while this step multiplies; 1: read just before use).
+constexpr int kGemmWeightSets = 3;
+constexpr int kGemmAFragSets = 2;
+
 // DIRECT: the activations are f16 in memory (gate/up): buffer loads write
 // them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
 // through registers and are converted to f16 with the row's power of two.
@@ -382,27 +389,27 @@ __device__ __forceinline__ void gemm_run(
     f16x2 bs[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(sv[i]);
-    f16x8 a[2][MSUB];
+    constexpr int NA = kGemmAFragSets;
+    f16x8 a[NA][MSUB];
+    auto read_a = [&](int j, f16x8 (&dst)[MSUB]) {
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q)
-      a[0][q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g) * 8));
+      for (int q = 0; q < MSUB; ++q)
+        dst[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
+    };
+    if (NA == 2) read_a(0, a[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < 3) {
-#pragma unroll
-        for (int q = 0; q < MSUB; ++q)
-          a[(j + 1) & 1][q] = __builtin_bit_cast(
-              f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j + 1) * 8));
-      }
+      if (NA == 2 && j < 3) read_a(j + 1, a[(j + 1) % NA]);
+      if (NA == 1) read_a(j, a[0]);
       f16x8 b[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) b[i] = dequant8(wv[i][j], bs[i][j >> 1]);
 #pragma unroll
       for (int q = 0; q < MSUB; ++q)
 #pragma unroll
-        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[j & 1][q], b[i], acc[q][i]);
-      // order: LDS reads of the next step, dequantisation, MFMAs of this step
-      if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
+        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[j % NA][q], b[i], acc[q][i]);
+      // order: LDS reads (of the next step with two fragment sets), dequantisation, MFMAs
+      if (NA == 1 || j < 3) __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8 * NW, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, MSUB * NW, 0);
     }
@@ -415,28 +422,32 @@ __device__ __forceinline__ void gemm_run(
   // three LDS buffers, unit u+2 issued before unit u is multiplied and
   // waited for one unit later; otherwise two register sets, unit u+3 loaded
   // when unit u+1 has been converted into the LDS double buffer.
-  u32x4 wv[3][NW];
-  uint32_t sv[3][NW];
+  constexpr int WS = DIRECT ? kGemmWeightSets : 2;  // weight register sets
+  u32x4 wv[WS][NW];
+  uint32_t sv[WS][NW];
   if (DIRECT) {
-    // weights two units ahead (three register sets, loop unrolled by three;
-    // the steps past the last unit skip their MFMAs, a uniform branch)
+    // weights WS - 1 units ahead (WS register sets); the loop is unrolled
+    // by a multiple of the 3 LDS buffers and of WS, and the steps past the
+    // last unit skip their MFMAs (a uniform branch)
+    constexpr int UNR = WS == 3 ? 3 : 6;
+    constexpr int AHEAD = MSUB + 2 * NW * (WS - 1);  // loads issued after a unit's activations
     load_a_lds(0, 0);
     load_a_lds(1, 1);
-    load_w(0, wv[0], sv[0]);
-    load_w(1, wv[1], sv[1]);
-    MOE_WAIT_VMCNT(MSUB + 4 * NW);  // unit 0 of the activations has landed
-    __syncthreads();
-    const int nu3 = (nunits + 2) / 3 * 3;
-    for (int u0 = 0; u0 < nu3; u0 += 3) {
 #pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        const int u = u0 + d;  // LDS ring buffer of unit u: u % 3 = d
+    for (int i = 0; i < WS - 1; ++i) load_w(i, wv[i], sv[i]);
+    MOE_WAIT_VMCNT(AHEAD);  // unit 0 of the activations has landed
+    __syncthreads();
+    const int nuu = (nunits + UNR - 1) / UNR * UNR;
+    for (int u0 = 0; u0 < nuu; u0 += UNR) {
+#pragma unroll
+      for (int d = 0; d < UNR; ++d) {
+        const int u = u0 + d;  // LDS ring buffer of unit u: u % 3 = d % 3
         load_a_lds(u + 2, (d + 2) % 3);
-        load_w(u + 2, wv[(d + 2) % 3], sv[(d + 2) % 3]);
+        load_w(u + WS - 1, wv[(d + WS - 1) % WS], sv[(d + WS - 1) % WS]);
         __builtin_amdgcn_sched_barrier(0);
-        if (u < nunits) compute(s_a[d], wv[d], sv[d]);
+        if (u < nunits) compute(s_a[d % 3], wv[d % WS], sv[d % WS]);
         __builtin_amdgcn_sched_barrier(0);
-        MOE_WAIT_VMCNT(MSUB + 4 * NW);  // unit u+1 of the activations has landed
+        MOE_WAIT_VMCNT(AHEAD);  // unit u+1 of the activations has landed
         __syncthreads();
       }
     }

@@ -78,37 +78,44 @@ __global__ __launch_bounds__(256) void k_route_logits_few(
     float eps, float *__restrict__ logits) {
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // scale*W of this lane's K elements (exact in fp32); lanes past H hold 0
-  float sw[NV * 8];
+  // workgroup (e, y) takes tokens 16y .. 16y+15, 4 per wave
+  constexpr int kTPW = 4;
+  const int t0 = blockIdx.y * 16 + wave * kTPW;
+  // every load first (the W row, the scale and the wave's token rows do not
+  // depend on each other, so their latencies overlap); lanes past H read row
+  // start 0 and are masked below
   int koff[NV];
+  u32x4 wv[NV], sv[NV], xv[kTPW][NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int k = (v * 64 + lane) * 8;
-    const bool ok = k < H;
-    koff[v] = ok ? k : 0;
-    const u32x4 wv = *(const u32x4 *)(w + (size_t)e * H + koff[v]);
-    const u32x4 sv = *(const u32x4 *)(scale + koff[v]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = __uint_as_float(wv[i] << 16) * __uint_as_float(sv[i] << 16);
-      const float p1 = __uint_as_float(wv[i] & 0xFFFF0000u) * __uint_as_float(sv[i] & 0xFFFF0000u);
-      sw[v * 8 + 2 * i] = ok ? p0 : 0.0f;
-      sw[v * 8 + 2 * i + 1] = ok ? p1 : 0.0f;
-    }
+    koff[v] = k < H ? k : 0;
+    wv[v] = *(const u32x4 *)(w + (size_t)e * H + koff[v]);
+    sv[v] = *(const u32x4 *)(scale + koff[v]);
   }
-  const float hs = 1.0f / sqrtf((float)H);
-  const float b = bias ? bias[e] : 0.0f;
-  // workgroup (e, y) takes tokens 16y .. 16y+15, 4 per wave; the rows of the
-  // wave's tokens are all requested before any is used
-  constexpr int kTPW = 4;
-  const int t0 = blockIdx.y * 16 + wave * kTPW;
-  u32x4 xv[kTPW][NV];
 #pragma unroll
   for (int q = 0; q < kTPW; ++q) {
     const int t = min(t0 + q, T - 1);
 #pragma unroll
     for (int v = 0; v < NV; ++v) xv[q][v] = *(const u32x4 *)(x + (size_t)t * H + koff[v]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // scale*W of this lane's K elements (exact in fp32); lanes past H hold 0
+  float sw[NV * 8];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const bool ok = (v * 64 + lane) * 8 < H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = __uint_as_float(wv[v][i] << 16) * __uint_as_float(sv[v][i] << 16);
+      const float p1 =
+          __uint_as_float(wv[v][i] & 0xFFFF0000u) * __uint_as_float(sv[v][i] & 0xFFFF0000u);
+      sw[v * 8 + 2 * i] = ok ? p0 : 0.0f;
+      sw[v * 8 + 2 * i + 1] = ok ? p1 : 0.0f;
+    }
+  }
+  const float hs = 1.0f / sqrtf((float)H);
+  const float b = bias ? bias[e] : 0.0f;
   float dot[kTPW], ss[kTPW];
 #pragma unroll
   for (int q = 0; q < kTPW; ++q) {
@@ -127,24 +134,19 @@ __global__ __launch_bounds__(256) void k_route_logits_few(
       }
     }
   }
+  // wave sums (DPP rows, then the four rows; uniform results); lane q writes token q
+  float d = 0.0f, q2 = 0.0f;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-    for (int q = 0; q < kTPW; ++q) {
-      dot[q] += __shfl_xor(dot[q], o, kWave);
-      ss[q] += __shfl_xor(ss[q], o, kWave);
+  for (int q = 0; q < kTPW; ++q) {
+    const float dq = wave_sum_u(dot[q]), sq = wave_sum_u(ss[q]);
+    if (lane == q) {
+      d = dq;
+      q2 = sq;
     }
-  if (lane < kTPW) {
-    float d = dot[0], q2 = ss[0];
-#pragma unroll
-    for (int q = 1; q < kTPW; ++q)
-      if (lane == q) {
-        d = dot[q];
-        q2 = ss[q];
-      }
-    const int t = t0 + lane;
-    if (t < T) logits[(size_t)t * E + e] = d * (1.0f / sqrtf(q2 / (float)H + eps) * hs) + b;
   }
+  const int t = t0 + lane;
+  if (lane < kTPW && t < T)
+    logits[(size_t)t * E + e] = d * (1.0f / sqrtf(q2 / (float)H + eps) * hs) + b;
 }
 
 // ---- many tokens: 64 tokens x 32 experts per workgroup (16 x 32 per wave),
