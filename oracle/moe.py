@@ -22,6 +22,13 @@ Readings (the pages leave these open):
   the result (compared as sets).
 * The bucket order is (expert, token, slot); the routing weight multiplies the
   expert output after the down projection.
+* The learned norms around the branch (``pre_feedforward_layernorm_2`` on the
+  expert input, ``post_feedforward_layernorm_2`` on the weighted sum) are
+  RMSNorms with a multiplicative per-channel weight and the same epsilon; a
+  checkpoint that stores the weight as an offset from 1 passes 1 + w.  The
+  layer's residual add and ``layer_scalar`` follow the branch; its dense MLP
+  and the outer ``post_feedforward_layernorm`` are not part of the block, so
+  ``sparse_branch`` gives residual + branch (times layer_scalar) without them.
 """
 import numpy as np
 
@@ -201,3 +208,30 @@ def moe_block_dense(x, x_expert, router, gate, up, down, k=8, eps=1e-6):
         contrib = mask[:, e:e + 1] * ye
         out = contrib if out is None else out + contrib
     return out
+
+
+def rms_norm(x, weight, eps=1e-6):
+    """Learned RMSNorm of each row (float64): x / sqrt(mean(x^2) + eps) * weight.
+
+    "Gemma 4 26B-A4B (MoE) - Core AI", Architecture code sketch: the experts
+    read pre_feedforward_layernorm_2(residual); the weighted expert sum goes
+    through post_feedforward_layernorm_2."""
+    x = np.asarray(x, np.float64)
+    inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * inv * np.asarray(weight, np.float64)
+
+
+def sparse_branch(residual, router, pre_norm, post_norm, gate, up, down, k=8, eps=1e-6,
+                  ids=None, layer_scalar=1.0, add_residual=True):
+    """The sparse branch of a layer with its two learned norms (float64), same
+    page and sketch: the router reads the raw residual, the experts read
+    rms_norm(residual, pre_norm), and the weighted sum of the routed outputs
+    passes through rms_norm(., post_norm).  Returns dict(out, branch, x_expert,
+    block): out = (residual + branch) * layer_scalar (without the residual when
+    ``add_residual`` is false)."""
+    res = np.asarray(residual, np.float64)
+    x_expert = rms_norm(res, pre_norm, eps)
+    blk = moe_block(res, x_expert, router, gate, up, down, k, eps, ids)
+    branch = rms_norm(blk["out"], post_norm, eps)
+    out = ((res + branch) if add_residual else branch) * layer_scalar
+    return dict(out=out, branch=branch, x_expert=x_expert, block=blk)

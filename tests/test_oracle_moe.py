@@ -172,3 +172,49 @@ def test_synth_shapes_and_determinism():
     assert len(rows) == 3
     base = S.activations(4, 300, outliers=False)
     assert np.array_equal(np.delete(x, rows, 0), np.delete(base, rows, 0))
+
+
+# ------------------------------------------------ learned norms (NEXT-1)
+def test_rms_norm_vs_torch_library_routine():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 96)) * rng.uniform(0.1, 30.0, (5, 1))
+    w = rng.uniform(0.5, 1.5, 96)
+    got = M.rms_norm(x, w, 1e-6)
+    ref = TF.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(w), eps=1e-6).numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_rms_norm_closed_forms():
+    w = np.linspace(0.5, 2.0, 64)
+    # a constant row c: every element is c / sqrt(c^2 + eps) * w
+    for c in (3.0, -0.25):
+        got = M.rms_norm(np.full((1, 64), c), w, 1e-6)[0]
+        assert np.allclose(got, c / math.sqrt(c * c + 1e-6) * w, rtol=0, atol=1e-15)
+    # scale-free when eps = 0; the output has root-mean-square |w|_rms for w = const
+    x = np.random.default_rng(3).standard_normal((4, 64))
+    assert np.allclose(M.rms_norm(7.5 * x, w, 0.0), M.rms_norm(x, w, 0.0), rtol=1e-14, atol=0)
+    y = M.rms_norm(x, np.full(64, 2.0), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 2.0, rtol=1e-14)
+    # a zero row stays zero (eps keeps it finite)
+    assert np.all(M.rms_norm(np.zeros((1, 64)), w, 1e-6) == 0.0)
+
+
+def test_sparse_branch_composition():
+    c = S.small_case(11, 4, 32, 16, 8, 2)
+    r = {k: (F.bf16_bits_to_f64(v) if v is not None and k != "bias" else v)
+         for k, v in c["router"].items()}
+    x = F.bf16_bits_to_f64(c["x"])
+    fn = {n: (lambda m: (lambda e: F.bf16_bits_to_f64(m[e])))(c[n]) for n in ("gate", "up", "down")}
+    pre = np.linspace(0.5, 1.5, 32)
+    post = np.linspace(1.5, 0.5, 32)
+    sb = M.sparse_branch(x, r, pre, post, fn["gate"], fn["up"], fn["down"], k=2, layer_scalar=0.75)
+    # by definition: the block on the normed expert input, then the post-norm, residual, scalar
+    blk = M.moe_block(x, M.rms_norm(x, pre), r, fn["gate"], fn["up"], fn["down"], k=2)
+    assert np.array_equal(sb["out"], (x + M.rms_norm(blk["out"], post)) * 0.75)
+    # the routing depends on the raw residual only: the pre-norm weight does not change it
+    sb2 = M.sparse_branch(x, r, 3.0 * pre, post, fn["gate"], fn["up"], fn["down"], k=2)
+    assert np.array_equal(sb2["block"]["route"]["idx"], sb["block"]["route"]["idx"])
+    # a zero post-norm weight leaves the residual times the scalar
+    z = M.sparse_branch(x, r, pre, np.zeros(32), fn["gate"], fn["up"], fn["down"], k=2,
+                        layer_scalar=2.0)
+    assert np.array_equal(z["out"], 2.0 * x)
