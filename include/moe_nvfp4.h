@@ -228,10 +228,52 @@ int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets, i
  *   y_sorted [T*top_k][H] bf16, topk_w [T][top_k] float, pair_rank [T*top_k]
  *   out      out [T][H] bf16
  * A pair whose rank is outside [0, T*top_k) contributes nothing.
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k <= 0, H <= 0, H % 8).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k <= 0, H <= 0, H % 8),
+ * MOE_ERR_UNSUPPORTED (top_k > MOE_MAX_TOPK).
  */
 int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pair_rank, int32_t T,
                 int32_t top_k, int32_t H, uint16_t *out, void *stream);
+
+/*
+ * The learned norms around the sparse branch ("Gemma 4 26B-A4B (MoE) - Core
+ * AI", Architecture code sketch: the experts read
+ * pre_feedforward_layernorm_2(residual); the weighted sum passes through
+ * post_feedforward_layernorm_2; the layer then adds the residual and scales
+ * by layer_scalar).  Each norm is an RMSNorm with a multiplicative weight:
+ *   rmsnorm(v) = v / sqrt(mean(v^2) + eps) * norm_weight     (fp32)
+ * (a checkpoint that stores the weight as an offset from 1 passes 1 + w).
+ * The layer's dense MLP and its outer post_feedforward_layernorm are outside
+ * the block.
+ *
+ * nvfp4_expert_prep_rmsnorm -- nvfp4_expert_prep with x_expert =
+ * rmsnorm(x): the norm is computed from the bf16 row of x in fp32 and feeds
+ * the expert kernels' per-row f16 rescale directly (no bf16 rounding of the
+ * normed row).  Queue it in place of nvfp4_expert_prep, before
+ * nvfp4_expert_gate_up, with the same workspace and shape arguments.
+ *   x            [T][H] bf16 (the raw residual; the router reads the same x)
+ *   norm_weight  [H] bf16
+ * Errors: those of nvfp4_expert_prep; MOE_ERR_NULL (norm_weight);
+ * MOE_ERR_SHAPE (eps < 0 or NaN).
+ */
+int nvfp4_expert_prep_rmsnorm(const uint16_t *x, const uint16_t *norm_weight, float eps, int32_t T,
+                              int32_t top_k, int32_t E, int32_t H, int32_t I, void *workspace,
+                              size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine_rmsnorm -- moe_combine followed by the post norm, the residual
+ * add and the layer scalar:
+ *   s = sum_j topk_w[t][j] * y_sorted[pair_rank[t*top_k+j]]   (fp32, j order)
+ *   out[t] = (residual[t] + rmsnorm(s)) * layer_scalar         (one bf16 rounding)
+ *   norm_weight  [H] bf16
+ *   residual     [T][H] bf16, or NULL for none; out may be the same buffer
+ *                (each element is read before it is written, by one thread)
+ * Errors: as moe_combine; MOE_ERR_NULL (norm_weight); MOE_ERR_SHAPE (eps < 0
+ * or NaN); MOE_ERR_UNSUPPORTED (H > 8192).
+ */
+int moe_combine_rmsnorm(const uint16_t *y_sorted, const float *topk_w, const int32_t *pair_rank,
+                        const uint16_t *norm_weight, float eps, const uint16_t *residual,
+                        float layer_scalar, int32_t T, int32_t top_k, int32_t H, uint16_t *out,
+                        void *stream);
 
 /*
  * nvfp4_quantize -- weight preparation: the block quantiser of the

@@ -34,7 +34,7 @@ GROUP = 16
 SEED = 0
 
 # key tags
-_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER = range(7)
+_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER, _NORM = range(8)
 GATE, UP, DOWN = 0, 1, 2
 
 WORKLOADS = {
@@ -116,6 +116,14 @@ def router_params(layer, seed=SEED, h=H, e=E, zipf=False):
         rank = _rng(seed, (_ZIPF, layer)).permutation(e) + 1
         p["bias"] = (-1.2 * beta * np.log(rank)).astype(np.float32)
     return p
+
+
+def norm_weights(layer, seed=SEED, h=H):
+    """The two learned norm weights around the sparse branch of one layer
+    (pre- and post-norm), bf16 bits [h] each ~ U(0.5, 1.5)."""
+    pre = _rng(seed, (_NORM, layer, 0)).uniform(0.5, 1.5, h)
+    post = _rng(seed, (_NORM, layer, 1)).uniform(0.5, 1.5, h)
+    return f32_to_bf16_bits(pre.astype(np.float32)), f32_to_bf16_bits(post.astype(np.float32))
 
 
 def activations(workload, t, seed=SEED, h=H, outliers=False):

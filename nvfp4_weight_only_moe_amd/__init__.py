@@ -6,13 +6,14 @@ the four-call block sequence (``block``) and device-resident synthetic
 workloads (``workload``).
 """
 from ._lib import (EXPORTED, LAYOUT_CANONICAL, LAYOUT_TILED, MoeError, Nvfp4Weights, lib, moe_bucket, moe_bucket_workspace_bytes,
-                   moe_combine, moe_route, moe_route_bucket, moe_workspace_bytes, nvfp4_dequant_bf16,
-                   nvfp4_expert_down, nvfp4_expert_gate_up, nvfp4_expert_mlp, nvfp4_expert_prep,
-                   nvfp4_quantize, nvfp4_repack)
-from .block import MoeBuffers, MoeLayer, forward
+                   moe_combine, moe_combine_rmsnorm, moe_route, moe_route_bucket,
+                   moe_workspace_bytes, nvfp4_dequant_bf16, nvfp4_expert_down, nvfp4_expert_gate_up,
+                   nvfp4_expert_mlp, nvfp4_expert_prep, nvfp4_expert_prep_rmsnorm, nvfp4_quantize,
+                   nvfp4_repack)
+from .block import BranchNorms, MoeBuffers, MoeLayer, forward, forward_branch
 
 __all__ = ["EXPORTED", "MoeError", "Nvfp4Weights", "lib", "moe_bucket", "moe_bucket_workspace_bytes",
-           "moe_combine", "moe_route", "moe_route_bucket", "moe_workspace_bytes", "nvfp4_dequant_bf16",
+           "moe_combine", "moe_combine_rmsnorm", "nvfp4_expert_prep_rmsnorm", "moe_route", "moe_route_bucket", "moe_workspace_bytes", "nvfp4_dequant_bf16",
            "nvfp4_expert_mlp", "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
            "nvfp4_quantize", "nvfp4_repack", "LAYOUT_CANONICAL", "LAYOUT_TILED", "MoeBuffers",
-           "MoeLayer", "forward"]
+           "MoeLayer", "forward", "BranchNorms", "forward_branch"]

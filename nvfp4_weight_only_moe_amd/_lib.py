@@ -19,7 +19,8 @@ _ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
 
 EXPORTED = ("moe_route", "moe_route_bucket", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
-            "moe_workspace_bytes", "moe_combine", "nvfp4_quantize", "nvfp4_repack",
+            "moe_workspace_bytes", "moe_combine", "nvfp4_expert_prep_rmsnorm",
+            "moe_combine_rmsnorm", "nvfp4_quantize", "nvfp4_repack",
             "nvfp4_dequant_bf16", "moe_status_str", "moe_abi_version")
 
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
@@ -65,6 +66,10 @@ def lib(path=None):
         "nvfp4_expert_down": (ctypes.c_int, [P, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
         "moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "moe_combine": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "nvfp4_expert_prep_rmsnorm": (ctypes.c_int, [vp, vp, f32, i32, i32, i32, i32, i32, vp, sz,
+                                                     vp]),
+        "moe_combine_rmsnorm": (ctypes.c_int, [vp, vp, vp, vp, f32, vp, f32, i32, i32, i32, vp,
+                                               vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_repack": (ctypes.c_int, [P, vp, vp, vp]),
         "nvfp4_dequant_bf16": (ctypes.c_int, [P, i32, vp, vp]),
@@ -220,6 +225,17 @@ def nvfp4_expert_prep(x_expert, E, I, top_k, workspace, stream=None):
     _check("nvfp4_expert_prep", st)
 
 
+def nvfp4_expert_prep_rmsnorm(x, norm_weight, eps, E, I, top_k, workspace, stream=None):
+    """nvfp4_expert_prep with the learned RMSNorm of x as the expert input."""
+    T, H = x.shape
+    st = lib().nvfp4_expert_prep_rmsnorm(_ptr(x, _B16, (T, H), "x"),
+                                         _ptr(norm_weight, _B16, (H,), "norm_weight"), float(eps),
+                                         T, top_k, E, H, I, _ptr(workspace, None, None, "workspace"),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream))
+    _check("nvfp4_expert_prep_rmsnorm", st)
+
+
 def nvfp4_expert_gate_up(gate, up, expert_offsets, sorted_pairs, T, top_k, H, workspace,
                          stream=None):
     cg, cu = gate.c(), up.c()
@@ -250,6 +266,21 @@ def moe_combine(y_sorted, topk_w, pair_rank, out, stream=None):
                            _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"), T, top_k, H,
                            _ptr(out, _B16, (T, H), "out"), _stream(stream))
     _check("moe_combine", st)
+
+
+def moe_combine_rmsnorm(y_sorted, topk_w, pair_rank, norm_weight, eps, out, residual=None,
+                        layer_scalar=1.0, stream=None):
+    """out = (residual + rmsnorm(sum_j w_j y_j)) * layer_scalar (residual optional)."""
+    T, top_k = topk_w.shape
+    H = out.shape[1]
+    res = None if residual is None else _ptr(residual, _B16, (T, H), "residual")
+    st = lib().moe_combine_rmsnorm(_ptr(y_sorted, _B16, (T * top_k, H), "y_sorted"),
+                                   _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
+                                   _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"),
+                                   _ptr(norm_weight, _B16, (H,), "norm_weight"), float(eps), res,
+                                   float(layer_scalar), T, top_k, H, _ptr(out, _B16, (T, H), "out"),
+                                   _stream(stream))
+    _check("moe_combine_rmsnorm", st)
 
 
 def nvfp4_quantize(w, out, stream=None):

@@ -104,3 +104,34 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
     _lib.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream)
     mark("combine")
     return buf.out
+
+
+@dataclass
+class BranchNorms:
+    """The learned norms around the sparse branch and the layer's residual
+    step ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture sketch)."""
+    pre: torch.Tensor               # [H] bf16, pre_feedforward_layernorm_2 weight
+    post: torch.Tensor              # [H] bf16, post_feedforward_layernorm_2 weight
+    eps: float = 1e-6
+    layer_scalar: float = 1.0
+    add_residual: bool = True
+
+
+def forward_branch(layer: MoeLayer, residual, buf: MoeBuffers, norms: BranchNorms, stream=None):
+    """The sparse branch with its norms: the router reads the raw residual, the
+    experts read rmsnorm(residual, pre), and buf.out = (residual +
+    rmsnorm(sum_k w_k y_k, post)) * layer_scalar (no residual when
+    ``norms.add_residual`` is false)."""
+    _lib.moe_route_bucket(residual, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                          layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx, buf.topk_w,
+                          buf.topk_w_raw, buf.logits, buf.expert_offsets, buf.sorted_pairs,
+                          buf.pair_rank, buf.bucket_ws, stream)
+    _lib.nvfp4_expert_prep_rmsnorm(residual, norms.pre, norms.eps, layer.E, layer.I, layer.top_k,
+                                   buf.ws, stream)
+    _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs, buf.T,
+                              layer.top_k, layer.H, buf.ws, stream)
+    _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,
+                           buf.ws, stream)
+    _lib.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank, norms.post, norms.eps,
+                             buf.out, residual if norms.add_residual else None,
+                             norms.layer_scalar, stream)

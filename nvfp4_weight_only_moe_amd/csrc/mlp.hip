@@ -97,8 +97,13 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
 // registers between the two passes, so the row is read once.
 constexpr int kPrepV = 8;  // H <= 64 * 8 * kPrepV; longer rows take a second read
 
-__global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ x, int T, int H,
-                                                   int P, uint16_t *__restrict__ x16,
+// NORM: the expert input is the learned RMSNorm of x, y = x / sqrt(mean(x^2)
+// + eps) * norm_w, computed in fp32 from the kept row (sum of squares in a
+// fixed order) and rescaled to f16 like a plain row.
+template <bool NORM>
+__global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ norm_w, float eps,
+                                                   int T, int H, int P, uint16_t *__restrict__ x16,
                                                    int32_t *__restrict__ x_exp,
                                                    uint32_t *__restrict__ a_max) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -106,37 +111,75 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const uint16_t *row = x + (size_t)t * H;
-  u32x4 keep[kPrepV];
-  float amax = 0.0f;
+  u32x4 keep[kPrepV], gkeep[kPrepV];
 #pragma unroll
   for (int v = 0; v < kPrepV; ++v) {
     const int k = (v * kWave + lane) * 8;
     keep[v] = k < H ? *(const u32x4 *)(row + k) : u32x4{0, 0, 0, 0};
+    if (NORM) gkeep[v] = k < H ? *(const u32x4 *)(norm_w + k) : u32x4{0, 0, 0, 0};
   }
-  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {  // rows longer than kept
-    const u32x4 v = *(const u32x4 *)(row + k);
+  // 1 / rms of the row (NORM)
+  float inv = 1.0f;
+  if (NORM) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kPrepV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(keep[v][i] << 16), hi = __uint_as_float(keep[v][i] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {  // rows longer than kept
+      const u32x4 v = *(const u32x4 *)(row + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    inv = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  // the 8 expert-input values of a 16-byte piece (bf16 x, and norm_w when NORM)
+  auto values = [&](const u32x4 &xv, const u32x4 &gv, float (&y)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+      y[2 * i] = __uint_as_float(xv[i] << 16);
+      y[2 * i + 1] = __uint_as_float(xv[i] & 0xFFFF0000u);
+      if (NORM) {
+        y[2 * i] = y[2 * i] * inv * __uint_as_float(gv[i] << 16);
+        y[2 * i + 1] = y[2 * i + 1] * inv * __uint_as_float(gv[i] & 0xFFFF0000u);
+      }
     }
+  };
+  auto gload = [&](int k) { return NORM ? *(const u32x4 *)(norm_w + k) : u32x4{0, 0, 0, 0}; };
+  float amax = 0.0f;
+  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {
+    float y[8];
+    values(*(const u32x4 *)(row + k), gload(k), y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
   }
 #pragma unroll
-  for (int v = 0; v < kPrepV; ++v)
+  for (int v = 0; v < kPrepV; ++v) {
+    float y[8];
+    values(keep[v], gkeep[v], y);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(keep[v][i] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(keep[v][i] & 0xFFFF0000u)));
-    }
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  }
   amax = wave_max(amax);
   const int ex = row_exponent(amax);
   const float f = __builtin_ldexpf(1.0f, 14 - ex);
-  auto convert = [&](const u32x4 &v) {
+  auto convert = [&](const u32x4 &xv, const u32x4 &gv) {
+    float y[8];
+    values(xv, gv, y);
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f16 lo = (f16)(__uint_as_float(v[i] << 16) * f);
-      const f16 hi = (f16)(__uint_as_float(v[i] & 0xFFFF0000u) * f);
+      const f16 lo = (f16)(y[2 * i] * f);
+      const f16 hi = (f16)(y[2 * i + 1] * f);
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
     return o;
@@ -144,10 +187,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ 
 #pragma unroll
   for (int v = 0; v < kPrepV; ++v) {
     const int k = (v * kWave + lane) * 8;
-    if (k < H) *(u32x4 *)(x16 + (size_t)t * H + k) = convert(keep[v]);
+    if (k < H) *(u32x4 *)(x16 + (size_t)t * H + k) = convert(keep[v], gkeep[v]);
   }
   for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8)
-    *(u32x4 *)(x16 + (size_t)t * H + k) = convert(*(const u32x4 *)(row + k));
+    *(u32x4 *)(x16 + (size_t)t * H + k) = convert(*(const u32x4 *)(row + k), gload(k));
   if (lane == 0) x_exp[t] = ex;
 }
 
@@ -909,8 +952,23 @@ extern "C" int nvfp4_expert_prep(const uint16_t *x_expert, int32_t T, int32_t to
   if (st != MOE_OK || T == 0) return st;
   const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
   const int P = T * top_k;
-  MOE_LAUNCH(k_prep, dim3((T + 3) / 4), dim3(kThreads), 0, (hipStream_t)stream, x_expert, T, H,
-             P, w.x16, w.x_exp, w.a_max);
+  MOE_LAUNCH(k_prep<false>, dim3((T + 3) / 4), dim3(kThreads), 0, (hipStream_t)stream, x_expert,
+             (const uint16_t *)nullptr, 0.0f, T, H, P, w.x16, w.x_exp, w.a_max);
+  return MOE_OK;
+}
+
+extern "C" int nvfp4_expert_prep_rmsnorm(const uint16_t *x, const uint16_t *norm_weight, float eps,
+                                         int32_t T, int32_t top_k, int32_t E, int32_t H,
+                                         int32_t I, void *workspace, size_t ws_bytes,
+                                         void *stream) {
+  if (!norm_weight || (T > 0 && !x)) return MOE_ERR_NULL;
+  if (!(eps >= 0.0f)) return MOE_ERR_SHAPE;
+  int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
+  const int P = T * top_k;
+  MOE_LAUNCH(k_prep<true>, dim3((T + 3) / 4), dim3(kThreads), 0, (hipStream_t)stream, x,
+             norm_weight, eps, T, H, P, w.x16, w.x_exp, w.a_max);
   return MOE_OK;
 }
 

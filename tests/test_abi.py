@@ -151,6 +151,35 @@ def test_combine_quantize_dequant_reject(L):
     assert L.nvfp4_repack(ctypes.byref(_tensor(2, 20, 64, layout=0)), FAKE, FAKE, NULL) == -2
 
 
+def test_norm_entry_points_reject(L):
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 17, 2816, FAKE, NULL) == -4        # top_k > 16
+    # moe_combine_rmsnorm(y, w, rank, norm_w, eps, residual, scalar, T, k, H, out, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, 1e-6, NULL, 1.0, 4, 8, 2816, FAKE, NULL]
+    a = list(ok); a[3] = NULL
+    assert L.moe_combine_rmsnorm(*a) == -1                                      # norm weight
+    a = list(ok); a[4] = -1.0
+    assert L.moe_combine_rmsnorm(*a) == -2                                      # eps < 0
+    a = list(ok); a[4] = float("nan")
+    assert L.moe_combine_rmsnorm(*a) == -2
+    a = list(ok); a[9] = 8200
+    assert L.moe_combine_rmsnorm(*a) == -4                                      # H > 8192
+    a = list(ok); a[9] = 2812
+    assert L.moe_combine_rmsnorm(*a) == -2                                      # H % 8
+    a = list(ok); a[8] = 17
+    assert L.moe_combine_rmsnorm(*a) == -4                                      # top_k > 16
+    # nvfp4_expert_prep_rmsnorm(x, norm_w, eps, T, k, E, H, I, ws, ws_bytes, stream)
+    ws = L.moe_workspace_bytes(4, 8, 128, 2816, 704)
+    ok = [FAKE, FAKE, 1e-6, 4, 8, 128, 2816, 704, FAKE, ws, NULL]
+    a = list(ok); a[1] = NULL
+    assert L.nvfp4_expert_prep_rmsnorm(*a) == -1
+    a = list(ok); a[0] = NULL
+    assert L.nvfp4_expert_prep_rmsnorm(*a) == -1
+    a = list(ok); a[2] = -0.5
+    assert L.nvfp4_expert_prep_rmsnorm(*a) == -2
+    a = list(ok); a[9] = ws - 1
+    assert L.nvfp4_expert_prep_rmsnorm(*a) == -3
+
+
 def test_workspace_sizes_cover_buffers(L):
     T, k, E, H, I = 16384, 8, 128, 2816, 704
     P = T * k

@@ -370,3 +370,40 @@ def test_combine(T, k, H):
     got = out.float().cpu().numpy()
     # one bf16 rounding of an fp32 sum: |err| <= 2^-8 |ref| + fp32 slack
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
+# ------------------------------------------------ combine + post-norm
+@pytest.mark.parametrize("T,k,H,resid,inplace", [(5, 3, 2816, True, False), (7, 8, 200, False, False),
+                                                 (3, 8, 8192, True, True), (64, 8, 2816, True, False),
+                                                 (2, 16, 64, True, True)])
+def test_combine_rmsnorm(T, k, H, resid, inplace):
+    rng = np.random.default_rng(100 * T + k)
+    P = T * k
+    y = S.f32_to_bf16_bits(rng.standard_normal((P, H)).astype(np.float32))
+    w = rng.uniform(0.05, 1.5, (T, k)).astype(np.float32)
+    rank = rng.permutation(P).astype(np.int32)
+    g = S.f32_to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    res = S.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    scalar = 0.625
+    res_d = _bits(res) if resid else None
+    out = res_d if (inplace and resid) else torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine_rmsnorm(_bits(y), torch.from_numpy(w).cuda(), torch.from_numpy(rank).cuda(),
+                            _bits(g), 1e-6, out, residual=res_d, layer_scalar=scalar)
+    torch.cuda.synchronize()
+    s_ = M.combine(F.bf16_bits_to_f64(y), w.astype(np.float64), rank, k)
+    ref = M.rms_norm(s_, F.bf16_bits_to_f64(g), 1e-6)
+    if resid:
+        ref = ref + F.bf16_bits_to_f64(res)
+    ref = ref * scalar
+    got = out.float().cpu().numpy()
+    # fp32 sum, norm and residual add, one bf16 rounding
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
+def test_combine_rmsnorm_empty_batch():
+    out = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine_rmsnorm(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+                            torch.empty((0, 8), dtype=torch.float32, device="cuda"),
+                            torch.empty((0,), dtype=torch.int32, device="cuda"), g, 1e-6, out)
+    torch.cuda.synchronize()

@@ -122,6 +122,52 @@ def test_layer_T16384_zipf_outliers_sampled(layer0_zipf, oracle_experts):
     print(f"T=16384 outlier rows rel_frob={e1:.3e} normal rows={e2:.3e}")
 
 
+# ------------------------------------- sparse branch with its learned norms
+def _branch_check(layer, x_bits, router_p, oe, T_sample=None, add_residual=True, scalar=0.8):
+    T = x_bits.shape[0]
+    pre, post = S.norm_weights(0)
+    norms = moe.BranchNorms(W.to_device_bf16(pre), W.to_device_bf16(post), 1e-6, scalar,
+                            add_residual)
+    buf = moe.MoeBuffers(T, layer.H, layer.I, layer.E, layer.top_k)
+    x = W.to_device_bf16(x_bits)
+    moe.forward_branch(layer, x, buf, norms)
+    torch.cuda.synchronize()
+    r = router_f64(router_p)
+    xs = F.bf16_bits_to_f64(x_bits)
+    toks = np.arange(T) if T_sample is None else np.asarray(T_sample)
+    gidx = buf.topk_idx.cpu().numpy()[toks]
+    ref_r = M.route(xs[toks], r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])
+    check_route(gidx, buf.topk_w.cpu().numpy()[toks], buf.topk_w_raw.cpu().numpy()[toks], ref_r,
+                r["per_expert_scale"])
+    oe.prefetch(np.unique(gidx))
+    ref = M.sparse_branch(xs[toks], r, F.bf16_bits_to_f64(pre), F.bf16_bits_to_f64(post),
+                          oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
+                          ids=gidx.astype(np.int64), layer_scalar=scalar, add_residual=add_residual)
+    got = buf.out.float().cpu().numpy()[toks]
+    assert np.all(np.isfinite(got))
+    return rel_frob(got, ref["out"]), rel_frob(got / scalar - (xs[toks] if add_residual else 0.0),
+                                                ref["branch"])
+
+
+@pytest.mark.parametrize("T", [4, 64])
+def test_branch_with_norms_all_tokens(layer0, oracle_experts, T):
+    x = S.activations(6, T)
+    err_out, err_branch = _branch_check(layer0, x, S.router_params(0), oracle_experts)
+    assert err_out <= REL_FROB_TOL, err_out
+    # without the residual the branch itself is the output
+    e2, eb2 = _branch_check(layer0, x, S.router_params(0), oracle_experts, add_residual=False)
+    assert eb2 <= REL_FROB_TOL and e2 <= REL_FROB_TOL, (e2, eb2)
+    print(f"T={T} branch with norms: out {err_out:.3e}, branch alone {eb2:.3e}")
+
+
+def test_branch_with_norms_prefill_sampled(layer0_zipf, oracle_experts):
+    x = S.activations(7, 2048)
+    sample = np.linspace(0, 2047, 10).astype(int)
+    e, _ = _branch_check(layer0_zipf, x, S.router_params(0, zipf=True), oracle_experts, sample,
+                         add_residual=False)
+    assert e <= REL_FROB_TOL, e
+
+
 def test_layer_deterministic(layer0):
     x = S.activations(1, 64)
     a = _run(layer0, x)
