@@ -49,6 +49,9 @@ def parse():
                     help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
                          "3: 30-layer decode sweep")
     ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3 (1 or 8)")
+    ap.add_argument("--chain", action="store_true",
+                    help="workload 3: chain the layers through the residual (each layer's sparse "
+                         "branch with its learned norms reads the previous layer's output)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the token count of workload 0, 1, 2 or 4 (a size sweep)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
@@ -198,12 +201,24 @@ def main():
         step_layers = [[r] for r in reps]
     x = Wl.to_device_bf16(S.activations(args.workload, T, outliers=wl["outliers"]))
     buf = moe.MoeBuffers(T, H, I, E, K)
+    # chained sweep: layer l reads xs[l] and writes xs[l + 1] (xs[0] = x, so
+    # every step runs the same chain)
+    chain = args.chain and args.workload == 3
+    if chain:
+        wl["name"] += "_chained"
+        norms = [moe.BranchNorms(*[Wl.to_device_bf16(a) for a in S.norm_weights(l)])
+                 for l in range(len(step_layers[0]))]
+        xs = [x] + [torch.empty_like(x) for _ in step_layers[0]]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
     def one_step(s, marks=None):
-        for layer in step_layers[s % len(step_layers)]:
-            moe.forward(layer, x, buf, marks=marks)
+        for li, layer in enumerate(step_layers[s % len(step_layers)]):
+            if chain:
+                moe.forward_branch(layer, xs[li], buf, norms[li])
+                xs[li + 1].copy_(buf.out)
+            else:
+                moe.forward(layer, x, buf, marks=marks)
 
     for s in range(args.warmup):
         one_step(s)
@@ -217,20 +232,33 @@ def main():
     hs, hside = ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side.cuda_stream)
     from nvfp4_weight_only_moe_amd import _lib as C
 
-    def stage_calls(layer, prep_stream=None):
-        """The five stage calls of one block pass, in STAGES order."""
+    def stage_calls(layer, prep_stream=None, li=0):
+        """The five stage calls of one block pass (layer li of the step), in
+        STAGES order."""
+        x_in = xs[li] if chain else x
+        if chain:
+            nm = norms[li]
+            prep = lambda: C.nvfp4_expert_prep_rmsnorm(x_in, nm.pre, nm.eps, E, I, K, buf.ws,
+                                                       prep_stream or stream)
+            combine = lambda: C.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank,
+                                                    nm.post, nm.eps, xs[li + 1], x_in,
+                                                    nm.layer_scalar, stream)
+        else:
+            prep = lambda: C.nvfp4_expert_prep(x_in, E, I, K, buf.ws, prep_stream or stream)
+            combine = lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out,
+                                            stream)
         return [
-            lambda: C.moe_route_bucket(x, layer.w_router, layer.router_scale,
+            lambda: C.moe_route_bucket(x_in, layer.w_router, layer.router_scale,
                                        layer.per_expert_scale, layer.logit_bias, K, layer.eps,
                                        buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
                                        buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
                                        buf.bucket_ws, stream),
-            lambda: C.nvfp4_expert_prep(x, E, I, K, buf.ws, prep_stream or stream),
+            prep,
             lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
                                            buf.sorted_pairs, T, K, H, buf.ws, stream),
             lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K, buf.y_sorted,
                                         buf.ws, stream),
-            lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream),
+            combine,
         ]
 
     step_plan = [step_layers[(args.warmup + s) % len(step_layers)] for s in range(args.steps)]
@@ -241,8 +269,8 @@ def main():
         previous layer's combine and joined before the gate/up GEMM."""
         n = 0
         for layers in step_plan:
-            for layer in layers:
-                route_bucket, prep, gate_up, down, combine = stage_calls(layer, side)
+            for li, layer in enumerate(layers):
+                route_bucket, prep, gate_up, down, combine = stage_calls(layer, side, li)
                 fork, join = fork_join[n]
                 n += 1
                 hip.record(fork, hs, False)
@@ -282,12 +310,12 @@ def main():
     # child graph between timing-event nodes (serial order, one stream)
     calls = []
     for layers in step_plan:
-        for layer in layers:
-            calls += stage_calls(layer)
+        for li, layer in enumerate(layers):
+            calls += stage_calls(layer, None, li)
     bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
     if not args.eager:
-        chain = hip.timed_chain(hs, calls, bounds)
-        hip.launch(chain, hs)
+        timed_graph = hip.timed_chain(hs, calls, bounds)
+        hip.launch(timed_graph, hs)
         events_mode = "hip_graph_with_event_nodes"
     else:
         hip.record(bounds[0], hs, False)
@@ -314,8 +342,12 @@ def main():
     P = T * K
     if args.workload == 3:
         U_layers = []
-        for layer in step_layers[0]:
-            moe.forward(layer, x, buf)
+        for li, layer in enumerate(step_layers[0]):
+            if chain:
+                moe.forward_branch(layer, xs[li], buf, norms[li])
+                xs[li + 1].copy_(buf.out)
+            else:
+                moe.forward(layer, x, buf)
             torch.cuda.synchronize()
             U_layers.append(int((np.diff(buf.expert_offsets.cpu().numpy()) > 0).sum()))
         U_total = sum(U_layers)
@@ -347,6 +379,7 @@ def main():
                    "timing": mode},
         "detail": {
             "stage_timing": events_mode,
+            "chained_layers": bool(chain),
             "gpu_ms_per_step_with_event_nodes": float(np.mean(gpu_step_ms)),
             "stage_avg_us": stage_avg_us,
             "active_experts": U_total,

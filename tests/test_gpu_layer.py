@@ -168,6 +168,38 @@ def test_branch_with_norms_prefill_sampled(layer0_zipf, oracle_experts):
     assert e <= REL_FROB_TOL, e
 
 
+def test_chained_layers_teacher_forced():
+    """Three layers chained through the residual (layer l reads layer l-1's
+    bf16 output), each layer checked against the oracle's sparse branch on
+    the input the GPU actually gave it."""
+    T, scalar = 4, 0.9
+    x_bits = S.activations(8, T)
+    x = W.to_device_bf16(x_bits)
+    for l in range(3):
+        layer = W.build_layer(l, zipf=False)
+        pre, post = S.norm_weights(l)
+        norms = moe.BranchNorms(W.to_device_bf16(pre), W.to_device_bf16(post), 1e-6, scalar)
+        buf = moe.MoeBuffers(T, layer.H, layer.I, layer.E, layer.top_k)
+        moe.forward_branch(layer, x, buf, norms)
+        torch.cuda.synchronize()
+        xin = F.bf16_bits_to_f64(x.view(torch.int16).cpu().numpy().view(np.uint16))
+        r = router_f64(S.router_params(l))
+        gidx = buf.topk_idx.cpu().numpy()
+        ref_r = M.route(xin, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])
+        check_route(gidx, buf.topk_w.cpu().numpy(), buf.topk_w_raw.cpu().numpy(), ref_r,
+                    r["per_expert_scale"])
+        oe = OracleExperts(l)
+        oe.prefetch(np.unique(gidx))
+        ref = M.sparse_branch(xin, r, F.bf16_bits_to_f64(pre), F.bf16_bits_to_f64(post),
+                              oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
+                              ids=gidx.astype(np.int64), layer_scalar=scalar)
+        got = buf.out.float().cpu().numpy()
+        assert rel_frob(got, ref["out"]) <= REL_FROB_TOL
+        x = buf.out.clone()
+        del layer
+        torch.cuda.empty_cache()
+
+
 def test_layer_deterministic(layer0):
     x = S.activations(1, 64)
     a = _run(layer0, x)
