@@ -2,8 +2,9 @@
 
 The product is the HIP library ``libmoe_nvfp4.so`` behind the C ABI in
 ``include/moe_nvfp4.h``; this package is its thin Python binding (``_lib``),
-the four-call block sequence (``block``) and device-resident synthetic
-workloads (``workload``).
+the four-call block sequence (``block``), device-resident synthetic
+workloads (``workload``) and the loader of two-level NVFP4 checkpoint tensors
+(``checkpoint``).
 """
 from ._lib import (EXPORTED, LAYOUT_CANONICAL, LAYOUT_TILED, MoeError, Nvfp4Weights, lib, moe_bucket, moe_bucket_workspace_bytes,
                    moe_combine, moe_combine_rmsnorm, moe_route, moe_route_bucket,
