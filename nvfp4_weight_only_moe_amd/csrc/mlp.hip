@@ -302,6 +302,8 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
 // while this step multiplies; 1: read just before use).
 constexpr int kGemmWeightSets = 3;
 constexpr int kGemmAFragSets = 2;
+// dequantise the next K step's weights while this step's MFMAs run
+constexpr bool kGemmPipeDequant = true;
 
 // DIRECT: the activations are f16 in memory (gate/up): buffer loads write
 // them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
@@ -432,6 +434,38 @@ __device__ __forceinline__ void gemm_run(
     f16x2 bs[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(sv[i]);
+    if (kGemmPipeDequant) {
+      // the weights of step j + 1 are dequantised while the MFMAs of step j
+      // run (two register sets), one MFMA between every two VALU ops
+      f16x8 a[MSUB], b[2][NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) b[0][i] = dequant8(wv[i][0], bs[i][0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < MSUB; ++q)
+          a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
+        if (j < 3) {
+#pragma unroll
+          for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = dequant8(wv[i][j + 1], bs[i][(j + 1) >> 1]);
+        }
+#pragma unroll
+        for (int q = 0; q < MSUB; ++q)
+#pragma unroll
+          for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[q], b[j & 1][i], acc[q][i]);
+        __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
+        if (j < 3) {
+#pragma unroll
+          for (int m = 0; m < MSUB * NW; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (8 * NW) / (MSUB * NW), 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, MSUB * NW, 0);
+        }
+      }
+      return;
+    }
     constexpr int NA = kGemmAFragSets;
     f16x8 a[NA][MSUB];
     auto read_a = [&](int j, f16x8 (&dst)[MSUB]) {
