@@ -159,7 +159,7 @@ def _route_gpu(x_bits, p, k, E):
     return idx.cpu().numpy(), w.cpu().numpy(), wr_raw.cpu().numpy(), lg.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,zipf,outliers", [(1, False, False), (4, False, False),
+@pytest.mark.parametrize("T,zipf,outliers", [(1, False, False), (4, False, False), (8192, True, True),
                                              (64, False, False), (333, True, False),
                                              (2048, True, True)])
 def test_route_model_shape(T, zipf, outliers):
