@@ -151,6 +151,32 @@ __global__ __launch_bounds__(kFusedThreads) void k_select_bucket(
   bucket_small<kFusedThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
 }
 
+// Selection over many workgroups (a wave per token, 4 tokens per workgroup),
+// then the bucketing by the workgroup that finishes last: after its writes a
+// workgroup takes one release fence and increments the arrival counter
+// (zeroed by the logits kernel queued just before); the one that sees the
+// final count takes an acquire fence and buckets every pair.  No workgroup
+// waits for another.
+__global__ __launch_bounds__(kBucketThreads) void k_select_bucket_last(
+    const float *__restrict__ logits, const uint16_t *__restrict__ pes, int T, int E, int K,
+    int32_t *topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ rank,
+    int32_t *__restrict__ err, int32_t *__restrict__ arrive) {
+  __shared__ int s_last;
+  const int t = blockIdx.x * (kBucketThreads / kWave) + (threadIdx.x >> 6);
+  if (t < T) select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
+  __syncthreads();  // every wave's stores have left for L2
+  if (threadIdx.x == 0) {
+    __threadfence();  // release: this workgroup's selections, visible device-wide
+    const bool last = atomicAdd(arrive, 1) == (int)gridDim.x - 1;
+    if (last) __threadfence();  // acquire: every workgroup's selections
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;  // uniform
+  bucket_small<kBucketThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
+}
+
 __global__ __launch_bounds__(kBucketThreads) void k_bucket_hist(const int32_t *__restrict__ idx,
                                                                 int P, int E,
                                                                 int32_t *__restrict__ chunk_cnt) {
@@ -223,15 +249,22 @@ size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_o
 
 namespace moe {
 // Selection + bucketing in one launch for T tokens with T * top_k <= kSmallP
-// (arguments validated by the caller, moe_route_bucket).
+// (arguments validated by the caller, moe_route_bucket): one workgroup, or
+// many with the bucketing by the last to finish (the arrival counter is word
+// 1 of the workspace, zeroed by the logits kernel before).
 __attribute__((visibility("hidden"))) int launch_select_bucket(
                          const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, hipStream_t s) {
-  MOE_LAUNCH(k_select_bucket, dim3(1), dim3(kFusedThreads), 0, s, logits, pes, T, E, top_k,
-             topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs, pair_rank,
-             (int32_t *)workspace);
+                         void *workspace, bool last_arrival, hipStream_t s) {
+  int32_t *err = (int32_t *)workspace;
+  if (last_arrival)
+    MOE_LAUNCH(k_select_bucket_last, dim3((T + kBucketWaves - 1) / kBucketWaves),
+               dim3(kBucketThreads), 0, s, logits, pes, T, E, top_k, topk_idx, topk_w,
+               topk_w_raw, expert_offsets, sorted_pairs, pair_rank, err, err + 1);
+  else
+    MOE_LAUNCH(k_select_bucket, dim3(1), dim3(kFusedThreads), 0, s, logits, pes, T, E, top_k,
+               topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs, pair_rank, err);
   return MOE_OK;
 }
 }  // namespace moe

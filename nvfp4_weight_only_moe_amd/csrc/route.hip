@@ -75,9 +75,11 @@ template <int NV>  // 16-byte vectors per lane: lane holds k = (v*64 + lane)*8 .
 __global__ __launch_bounds__(256) void k_route_logits_few(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
-    float eps, float *__restrict__ logits) {
+    float eps, float *__restrict__ logits, int32_t *__restrict__ arrive) {
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the arrival counter of the selection kernel that follows (when given)
+  if (arrive && e == 0 && blockIdx.y == 0 && threadIdx.x == 0) *arrive = 0;
   // workgroup (e, y) takes tokens 16y .. 16y+15, 4 per wave
   constexpr int kTPW = 4;
   const int t0 = blockIdx.y * 16 + wave * kTPW;
@@ -275,13 +277,15 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
 }  // namespace moe
 
 namespace moe {
-// Largest batch whose selection and bucketing run in one workgroup
-// (moe_route_bucket); larger batches select over many workgroups.
+// moe_route_bucket: up to kFusedMaxT tokens the selection and the bucketing
+// run in one workgroup; up to kLastMaxT tokens the selection runs over many
+// workgroups and the last one to finish buckets (one launch either way).
 constexpr int kFusedMaxT = 16;
+constexpr int kLastMaxT = 64;
 int launch_select_bucket(const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, hipStream_t s);
+                         void *workspace, bool last_arrival, hipStream_t s);
 }
 
 extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -301,7 +305,7 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
 #define MOE_FEW(NV)                                                                          \
   case NV:                                                                                   \
     MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, router_scale, \
-               logit_bias, T, H, E, eps, logits);                                            \
+               logit_bias, T, H, E, eps, logits, (int32_t *)nullptr);                        \
     break;
       MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
       default: MOE_FEW(8)
@@ -334,7 +338,7 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   if (ws_bytes < moe_bucket_workspace_bytes(T, top_k, E)) return MOE_ERR_WORKSPACE;
   const int nv = (H + 511) / 512;
-  if (T > kFusedMaxT || nv > kFewMaxV || T * top_k > 4096) {
+  if (T > kLastMaxT || nv > kFewMaxV || T * top_k > 4096) {
     const int st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
                              top_k, eps, topk_idx, topk_w, topk_w_raw, logits, stream);
     if (st != MOE_OK) return st;
@@ -345,16 +349,20 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
     return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
                       ws_bytes, stream);
   hipStream_t s = (hipStream_t)stream;
+  // the arrival counter of the many-workgroup selection: word 1 of the
+  // workspace, zeroed by the logits kernel of this call
+  const bool last_arrival = T > kFusedMaxT;
+  int32_t *arrive = last_arrival ? (int32_t *)workspace + 1 : nullptr;
   switch (nv) {
 #define MOE_FEW(NV)                                                                          \
   case NV:                                                                                   \
     MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, \
-               router_scale, logit_bias, T, H, E, eps, logits);                              \
+               router_scale, logit_bias, T, H, E, eps, logits, arrive);                      \
     break;
     MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
     default: MOE_FEW(8)
 #undef MOE_FEW
   }
   return launch_select_bucket(logits, per_expert_scale, T, E, top_k, topk_idx, topk_w, topk_w_raw,
-                              expert_offsets, sorted_pairs, pair_rank, workspace, s);
+                              expert_offsets, sorted_pairs, pair_rank, workspace, last_arrival, s);
 }

@@ -246,7 +246,7 @@ def test_bucket_invalid_ids_counted_and_parked(T):
 
 
 # ---------------------------------------------- fused routing + bucketing
-@pytest.mark.parametrize("T,H,E,k", [(0, 2816, 128, 8), (1, 2816, 128, 8), (4, 2816, 128, 8), (16, 2816, 128, 8),
+@pytest.mark.parametrize("T,H,E,k", [(0, 2816, 128, 8), (1, 2816, 128, 8), (4, 2816, 128, 8), (16, 2816, 128, 8), (33, 2816, 128, 8), (64, 2816, 256, 16),
                                      (17, 2816, 128, 8), (64, 2816, 128, 8), (65, 2816, 128, 8),
                                      (333, 2816, 128, 8), (9, 192, 16, 3), (64, 4096, 256, 16),
                                      (30, 4160, 32, 4)])
