@@ -148,10 +148,9 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  * topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs, pair_rank and the
  * workspace error word).  For decode batches (T <= 64, H <= 4096) the top-k
  * selection and the bucketing run in one kernel after the logits kernel,
- * which saves a launch on the latency-bound decode path: one workgroup for
- * T <= 16, else one wave per token over many workgroups, the last of which
- * to finish does the bucketing (no workgroup waits for another).  Otherwise
- * it issues the two calls.
+ * which saves a launch on the latency-bound decode path: one wave per token
+ * over ceil(T/4) workgroups, the last of which to finish does the bucketing
+ * (no workgroup waits for another).  Otherwise it issues the two calls.
  *   workspace  >= moe_bucket_workspace_bytes(T, top_k, E) bytes (as moe_bucket);
  *              word 1 is the call's arrival counter (no initial value needed)
  * Errors: those of moe_route and moe_bucket, checked before any work is

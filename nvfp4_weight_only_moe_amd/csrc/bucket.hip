@@ -135,22 +135,6 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_small(const int32_t *
   bucket_small<kBucketThreads>(idx, P, E, offsets, sorted, rank, err);
 }
 
-// Selection and bucketing of a decode batch in one workgroup (one launch
-// instead of two): wave w selects for tokens w, w + 16, ... from the logits,
-// then the workgroup buckets the chosen ids (read back after the barrier,
-// which makes the workgroup's global writes visible to all its waves).
-constexpr int kFusedThreads = 1024;
-__global__ __launch_bounds__(kFusedThreads) void k_select_bucket(
-    const float *__restrict__ logits, const uint16_t *__restrict__ pes, int T, int E, int K,
-    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ rank,
-    int32_t *__restrict__ err) {
-  for (int t = threadIdx.x >> 6; t < T; t += kFusedThreads / kWave)
-    select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
-  __syncthreads();
-  bucket_small<kFusedThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
-}
-
 // Selection over many workgroups (a wave per token, 4 tokens per workgroup),
 // then the bucketing by the workgroup that finishes last: after its writes a
 // workgroup takes one release fence and increments the arrival counter
@@ -249,22 +233,17 @@ size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_o
 
 namespace moe {
 // Selection + bucketing in one launch for T tokens with T * top_k <= kSmallP
-// (arguments validated by the caller, moe_route_bucket): one workgroup, or
-// many with the bucketing by the last to finish (the arrival counter is word
-// 1 of the workspace, zeroed by the logits kernel before).
+// (arguments validated by the caller, moe_route_bucket); the arrival counter
+// is word 1 of the workspace, zeroed by the logits kernel queued before.
 __attribute__((visibility("hidden"))) int launch_select_bucket(
                          const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, bool last_arrival, hipStream_t s) {
+                         void *workspace, hipStream_t s) {
   int32_t *err = (int32_t *)workspace;
-  if (last_arrival)
-    MOE_LAUNCH(k_select_bucket_last, dim3((T + kBucketWaves - 1) / kBucketWaves),
-               dim3(kBucketThreads), 0, s, logits, pes, T, E, top_k, topk_idx, topk_w,
-               topk_w_raw, expert_offsets, sorted_pairs, pair_rank, err, err + 1);
-  else
-    MOE_LAUNCH(k_select_bucket, dim3(1), dim3(kFusedThreads), 0, s, logits, pes, T, E, top_k,
-               topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs, pair_rank, err);
+  MOE_LAUNCH(k_select_bucket_last, dim3((T + kBucketWaves - 1) / kBucketWaves),
+             dim3(kBucketThreads), 0, s, logits, pes, T, E, top_k, topk_idx, topk_w, topk_w_raw,
+             expert_offsets, sorted_pairs, pair_rank, err, err + 1);
   return MOE_OK;
 }
 }  // namespace moe

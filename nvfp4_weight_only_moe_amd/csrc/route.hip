@@ -277,15 +277,13 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
 }  // namespace moe
 
 namespace moe {
-// moe_route_bucket: up to kFusedMaxT tokens the selection and the bucketing
-// run in one workgroup; up to kLastMaxT tokens the selection runs over many
-// workgroups and the last one to finish buckets (one launch either way).
-constexpr int kFusedMaxT = 16;
-constexpr int kLastMaxT = 64;
+// moe_route_bucket: up to kFusedMaxT tokens the selection runs over many
+// workgroups and the last one to finish buckets, in one launch.
+constexpr int kFusedMaxT = 64;
 int launch_select_bucket(const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, bool last_arrival, hipStream_t s);
+                         void *workspace, hipStream_t s);
 }
 
 extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -338,7 +336,7 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   if (ws_bytes < moe_bucket_workspace_bytes(T, top_k, E)) return MOE_ERR_WORKSPACE;
   const int nv = (H + 511) / 512;
-  if (T > kLastMaxT || nv > kFewMaxV || T * top_k > 4096) {
+  if (T > kFusedMaxT || nv > kFewMaxV || T * top_k > 4096) {
     const int st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
                              top_k, eps, topk_idx, topk_w, topk_w_raw, logits, stream);
     if (st != MOE_OK) return st;
@@ -349,10 +347,9 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
     return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
                       ws_bytes, stream);
   hipStream_t s = (hipStream_t)stream;
-  // the arrival counter of the many-workgroup selection: word 1 of the
-  // workspace, zeroed by the logits kernel of this call
-  const bool last_arrival = T > kFusedMaxT;
-  int32_t *arrive = last_arrival ? (int32_t *)workspace + 1 : nullptr;
+  // the arrival counter of the selection kernel: word 1 of the workspace,
+  // zeroed by the logits kernel of this call
+  int32_t *arrive = (int32_t *)workspace + 1;
   switch (nv) {
 #define MOE_FEW(NV)                                                                          \
   case NV:                                                                                   \
@@ -364,5 +361,5 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
 #undef MOE_FEW
   }
   return launch_select_bucket(logits, per_expert_scale, T, E, top_k, topk_idx, topk_w, topk_w_raw,
-                              expert_offsets, sorted_pairs, pair_rank, workspace, last_arrival, s);
+                              expert_offsets, sorted_pairs, pair_rank, workspace, s);
 }
