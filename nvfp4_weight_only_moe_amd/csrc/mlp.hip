@@ -679,8 +679,20 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   const int arow = GATED ? p.sorted_pairs[prow] / p.top_k : prow;
   const uint32_t va = row_ok ? (uint32_t)arow * (uint32_t)K * 2 + (uint32_t)(32 * g + 8 * h * NL) * 2
                              : kOOB;
+  // the power of two of this lane's activation row: GATED, the token's
+  // exponent (the row was rescaled by prep); else from the row's max |A|.
+  // Requested here, used after the K loop: the epilogue takes the exponent of
+  // its row 4g + jj from lane 4g + jj (whose activation row it is).
+  int row_ex = 0;
   float a_scale = 1.0f;
-  if (!GATED) a_scale = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(p.a_max[prow])));
+  if (GATED) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x_exp, (uint32_t)(p.P / p.top_k) * 4u);
+    row_ex = (int)__builtin_amdgcn_raw_buffer_load_b32(rx, row_ok ? (uint32_t)arow * 4u : kOOB, 0, 0);
+  } else {
+    row_ex = row_exponent(__uint_as_float(p.a_max[prow]));
+    a_scale = __builtin_ldexpf(1.0f, 14 - row_ex);
+  }
+  const float ep_g0 = w0.global[e], ep_g1 = GATED ? w1.global[e] : 0.0f;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_src, p.a_bytes);
 
   // weight streams: expert e's tensors through buffer resources; offsets past
@@ -787,14 +799,18 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       acc[i][jj] = t;
     }
 
+  // exponent of the epilogue rows 4g + jj (lane 4g + jj holds row 4g + jj)
+  int ep_ex[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) ep_ex[jj] = __shfl(row_ex, (4 * g + jj) & 15, kWave);
+
   if (GATED) {
-    const float gg = w0.global[e], gu = w1.global[e];
+    const float gg = ep_g0, gu = ep_g1;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int mr = 4 * g + jj;  // row of this lane's sums (valid when mr < R)
       const bool ok = mr < R && mr < mrows;
-      float f = 0.0f;
-      if (ok) f = __builtin_ldexpf(1.0f, p.x_exp[p.sorted_pairs[row0 + mr] / p.top_k] - 14);
+      const float f = ok ? __builtin_ldexpf(1.0f, ep_ex[jj] - 14) : 0.0f;
       uint32_t rmax = 0;  // max |A| of the row (f32 bits)
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
@@ -807,13 +823,12 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], rmax);
     }
   } else {
-    const float gd = w0.global[e];
+    const float gd = ep_g0;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int mr = 4 * g + jj;
       if (mr < R && mr < mrows) {
-        const float f =
-            gd * __builtin_ldexpf(1.0f, row_exponent(__uint_as_float(p.a_max[row0 + mr])) - 14);
+        const float f = gd * __builtin_ldexpf(1.0f, ep_ex[jj] - 14);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const int n = (nt0 + i) * 16 + r;
