@@ -395,15 +395,15 @@ def main():
     # the f16 activations and A written), the f16 MFMA one for prefill (its
     # algorithmic flops 2 P 2 I H); the other one is reported beside it.
     gu_kernel = gate_up_kernel_name(T, K, E)
+    traffic = profiled_traffic(wl["name"], gu_kernel)   # HBM bytes per launch (counters)
     hbm = {"kernel": gu_kernel, "bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
-           "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
-           "traffic": profiled_traffic(wl["name"], gu_kernel),
+           "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": traffic,
            "alg_bytes_per_launch": gate_up_alg_bytes, "avg_launch_us": gu_us,
            "units": f"{U_mean:g} active experts x {gu_w_bytes} B + {T} x {H} x 2 B + {P} x {I} x 2 B"}
     gu_flops = 2.0 * P * 2 * I * H
     tflops = gu_flops / (gu_us * 1e-6) / 1e12
     mfma = {"kernel": gu_kernel, "bound": "mfma", "achieved": tflops, "peak": F16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": tflops / F16_MFMA_PEAK_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": tflops / F16_MFMA_PEAK_TFLOPS, "traffic": traffic,
             "alg_flops_per_launch": gu_flops, "avg_launch_us": gu_us}
     if args.workload in (2, 4):
         out["roofline"], out["roofline_hbm"] = mfma, hbm
