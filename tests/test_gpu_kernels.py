@@ -313,6 +313,25 @@ def _expert_case(T, k, E, H, I, seed):
                                        (3, 1, 2, 4160, 64)])
 def test_expert_mlp_small(T, k, E, H, I):
     c, idx = _expert_case(T, k, E, H, I, seed=T)
+    _check_expert_mlp(c, idx, T, k, E, H, I)
+
+
+def test_expert_mlp_skewed_gemv_mode():
+    # GEMV mode (fewer than 24 rows per active expert on average) with popular
+    # experts far above one tile of rows (several tiles each) next to experts
+    # with a handful of rows
+    T, k, E, H, I = 300, 8, 128, 128, 64
+    c = S.small_case(123, T, H, I, E, k)
+    rng = np.random.default_rng(5)
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    assert counts.max() > 64 and 0 < (counts[counts > 0] <= 32).sum() and T * k < 24 * E
+    _check_expert_mlp(c, idx, T, k, E, H, I)
+
+
+def _check_expert_mlp(c, idx, T, k, E, H, I):
     layer = W.build_small_layer(c, k)
     off, sp, pr, _ = _bucket_gpu(idx, E)
     x = _bits(c["x"])

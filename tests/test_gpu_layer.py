@@ -101,6 +101,19 @@ def test_layer_decode_sizes_all_tokens(layer0, oracle_experts, T):
     print(f"T={T} rel_frob={err:.3e} worst_row={worst_row:.3e}")
 
 
+@pytest.mark.parametrize("T", [24, 256, 512])
+def test_layer_intermediate_T_zipf(layer0_zipf, oracle_experts, T):
+    """Batched decode with skewed (Zipf) routing at token counts around the
+    GEMV / GEMM crossover (fewer / more than 24 rows per active expert on
+    average): every token for T = 24, a sample beyond."""
+    x = S.activations(9, T)
+    buf = _run(layer0_zipf, x)
+    sample = None if T <= 64 else np.linspace(0, T - 1, 16).astype(int)
+    err, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, sample)
+    counts = np.diff(buf.expert_offsets.cpu().numpy())
+    print(f"T={T} zipf rel_frob={err:.3e} rows/active expert={counts.sum() / max(1, (counts > 0).sum()):.1f}")
+
+
 def test_layer_T2048_zipf_sampled(layer0_zipf, oracle_experts):
     x = S.activations(2, 2048)
     buf = _run(layer0_zipf, x)
