@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the token count of workload 0, 1, 2 or 4 (a size sweep)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "q4_0", "aff4"],
+                    help="expert weight format (the int4 ones: seeded codes and fp16 scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -159,9 +161,19 @@ class HipRuntime:
         self._ok(self.h.hipGraphLaunch(exe, stream), "hipGraphLaunch")
 
 
-def expert_bytes_per_expert(H, I):
-    # packed nibbles + E4M3 scales + FP32 global, gate + up + down
-    return 3 * (H * I // 2 + H * I // 16 + 4)
+# scale bytes per 32 weights: two E4M3 codes (NVFP4), one fp16 d (q4_0), fp16 s and b (aff4)
+SCALE_BYTES_PER_32 = {"nvfp4": 2, "q4_0": 2, "aff4": 4}
+FORMAT_INDEX = {"nvfp4": 0, "q4_0": 1, "aff4": 2}
+
+
+def proj_bytes(H, I, fmt="nvfp4"):
+    """Bytes of one expert's [I, H] (or [H, I]) projection: packed nibbles,
+    block scales, and the FP32 tensor scale of NVFP4."""
+    return H * I // 2 + H * I * SCALE_BYTES_PER_32[fmt] // 32 + (4 if fmt == "nvfp4" else 0)
+
+
+def expert_bytes_per_expert(H, I, fmt="nvfp4"):
+    return 3 * proj_bytes(H, I, fmt)
 
 
 def main():
@@ -187,15 +199,24 @@ def main():
     H, I, E, K = S.H, S.I, S.E, S.TOP_K
     t_setup = time.perf_counter()
 
+    fmt = args.format
+    if fmt != "nvfp4":
+        wl["name"] += f"_{fmt}"
+
+    def make_layer(l, zipf):
+        if fmt == "nvfp4":
+            return Wl.build_layer(l, zipf=zipf)
+        return Wl.build_int4_layer(fmt, l, zipf=zipf)
+
     if args.workload == 3:
         T = args.sweep_T
-        layers = [Wl.build_layer(l, zipf=False) for l in range(S.LAYERS)]
+        layers = [make_layer(l, False) for l in range(S.LAYERS)]
         step_layers = [layers]                       # one step = the 30-layer sweep
         replicas = 1                                 # 12.85 GB of distinct weights per sweep
     else:
         T = wl["T"][0]
-        base = Wl.build_layer(0, zipf=wl["zipf"])
-        touched = expert_bytes_per_expert(H, I) * min(E, T * K)
+        base = make_layer(0, wl["zipf"])
+        touched = expert_bytes_per_expert(H, I, fmt) * min(E, T * K)
         replicas = args.replicas or max(2, min(16, math.ceil(1.5 * 2 ** 30 / touched) + 1))
         reps = Wl.replicate_experts(base, replicas)
         step_layers = [[r] for r in reps]
@@ -353,8 +374,8 @@ def main():
         U_total = sum(U_layers)
     else:
         U_layers, U_total = [U], U
-    per_exp = expert_bytes_per_expert(H, I)
-    gu_w_bytes = 2 * (H * I // 2 + H * I // 16 + 4)
+    per_exp = expert_bytes_per_expert(H, I, fmt)
+    gu_w_bytes = 2 * proj_bytes(H, I, fmt)
     step_s = ms_per_step / 1e3
     U_mean = U_total / n_layers                 # active experts per gate/up launch
     gate_up_alg_bytes = gu_w_bytes * U_mean + T * H * 2 + P * I * 2     # per launch
@@ -372,8 +393,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 weights (e2m1 x e4m3 x fp32) x bf16 activations; f16 MFMA, fp32 accumulate",
-        "data": "synthetic (seeded; bf16 N(0,0.02) experts quantised to NVFP4 on the GPU)",
+        "dtype": DTYPES[fmt] + " x bf16 activations; f16 MFMA, fp32 accumulate",
+        "data": DATA[fmt],
         "config": {"workload": wl["name"], "tokens": T, "hidden": H, "experts": E, "top_k": K,
                    "moe_intermediate": I, "layers": n_layers, "weight_replicas": replicas,
                    "timing": mode},
@@ -394,7 +415,7 @@ def main():
     # decode (its algorithmic bytes: the active experts' gate and up tensors,
     # the f16 activations and A written), the f16 MFMA one for prefill (its
     # algorithmic flops 2 P 2 I H); the other one is reported beside it.
-    gu_kernel = gate_up_kernel_name(T, K, E)
+    gu_kernel = gate_up_kernel_name(T, K, E, fmt)
     traffic = profiled_traffic(wl["name"], gu_kernel)   # HBM bytes per launch (counters)
     hbm = {"kernel": gu_kernel, "bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
            "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": traffic,
@@ -415,17 +436,25 @@ def main():
 
 
 S_I = 704  # expert intermediate size of the workloads
+DTYPES = {"nvfp4": "nvfp4 weights (e2m1 x e4m3 x fp32)",
+          "q4_0": "int4 q4_0 weights ((q - 8) x fp16 d per 32)",
+          "aff4": "int4 affine weights (q x fp16 s + fp16 b per 32)"}
+DATA = {"nvfp4": "synthetic (seeded; bf16 N(0,0.02) experts quantised to NVFP4 on the GPU)",
+        "q4_0": "synthetic (seeded; uniform int4 codes, fp16 d ~ U(0.004, 0.008))",
+        "aff4": "synthetic (seeded; uniform int4 codes, fp16 s ~ U(0.004, 0.008), "
+                "b ~ U(-0.06, -0.035))"}
 
 
-def gate_up_kernel_name(T, K, E):
+def gate_up_kernel_name(T, K, E, fmt="nvfp4"):
     """The kernel nvfp4_expert_gate_up launches for this shape (the dispatch
     rule of the library: few rows per expert -> GEMV mode)."""
     P = T * K
     avg = P // max(1, min(P, E))
+    f = FORMAT_INDEX[fmt]
     if avg < 24:
         rows = 8 if P <= 4 * E else 16
-        return f"k_expert_gemv<{rows}, 2, true, 4>"
-    return "k_expert_gemm<4, 2, true>"
+        return f"k_expert_gemv<{rows}, 2, true, 4, {f}>"
+    return f"k_expert_gemm<4, 2, true, {f}>"
 
 
 def profiled_traffic(workload, kernel):
@@ -475,6 +504,7 @@ def cpu_baseline(args, wl, T):
     from threadpoolctl import threadpool_limits
     import moe_synth as S
     from oracle import formats as F
+    from oracle import int4 as Q
     from oracle import moe as M
     from oracle.quantize import quantize
     from concurrent.futures import ThreadPoolExecutor
@@ -487,20 +517,33 @@ def cpu_baseline(args, wl, T):
     ids = M.route(x, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])["idx"]
     todo = [(proj, int(e)) for e in np.unique(ids) for proj in (S.GATE, S.UP, S.DOWN)]
 
+    fmt = args.format
+
     def q(item):
         proj, e = item
+        if fmt != "nvfp4":
+            return item, S.int4_expert(fmt, 0, proj, e)
         return item, quantize(F.bf16_bits_to_f64(S.expert_weight(0, proj, e)))
 
     with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
         packed = dict(ex.map(q, todo))                    # weight preparation, untimed
-    fn = {proj: (lambda e, proj=proj: F.dequantize(*packed[(proj, e)])) for proj in (S.GATE, S.UP, S.DOWN)}
+
+    def decode(item):
+        if fmt == "nvfp4":
+            return F.dequantize(*packed[item])
+        p, sb = packed[item]
+        bits = sb.view(np.uint16)
+        if fmt == "q4_0":
+            return Q.decode_q4_0(p, bits)
+        return Q.decode_aff4(p, bits.reshape(bits.shape[0], -1, 2))
+    fn = {proj: (lambda e, proj=proj: decode((proj, e))) for proj in (S.GATE, S.UP, S.DOWN)}
     with threadpool_limits(1):
         t0 = time.perf_counter()
         M.moe_block(x, x, r, fn[S.GATE], fn[S.UP], fn[S.DOWN], k=8)
         dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} of the {T} tokens of {wl['name']} through the fp64 oracle block "
-                      f"(route, bucket, NVFP4 decode of the {len(todo) // 3} touched experts, "
+                      f"(route, bucket, {fmt} decode of the {len(todo) // 3} touched experts, "
                       f"expert MLPs, combine); {dt:.1f} s"}
 
 

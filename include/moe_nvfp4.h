@@ -55,6 +55,12 @@ extern "C" {
 #define MOE_LAYOUT_CANONICAL 0 /* the row-major layout below (the pages' packed-U8 form) */
 #define MOE_LAYOUT_TILED 1     /* the same bytes permuted into 16-row x 128-K tiles      */
 
+/* Weight formats of an nvfp4_tensor (the `format` field). */
+#define MOE_FORMAT_NVFP4 0 /* E2M1 x E4M3 per 16 x FP32 per tensor                     */
+#define MOE_FORMAT_Q4_0 1  /* (q - 8) * d, fp16 d per 32 ("Gemma 4 26B-A4B (MoE) -
+                              Core AI", Compression recipe: the q4_0 grid)           */
+#define MOE_FORMAT_AFF4 2  /* q * s + b, fp16 s and b per 32 (same page: aff4)         */
+
 /*
  * One stack of NVFP4 weights, one tensor per expert, canonical layout:
  *   packed [E][N][K/2]  uint8: element k of row n is nibble (k & 1) of byte
@@ -78,6 +84,20 @@ extern "C" {
  * Scales likewise: tile t starts at byte t*K, unit u at +128u, lane l at +2l
  * holds the two scale bytes of row 16t+r for k = 128u + 32g .. +31.
  * Sizes per expert are unchanged: N*K/2 and N*K/16 bytes.
+ *
+ * The int4 formats (MOE_FORMAT_Q4_0, MOE_FORMAT_AFF4) use the same struct:
+ *   packed [E][N][K/2]  uint8: unsigned codes q = 0..15, nibble order as above.
+ *   scales  Q4_0: [E][N][K/32] fp16 d;  AFF4: [E][N][K/32][2] fp16 (s, b),
+ *                       for elements 32b..32b+31 of row n.
+ *   global  not read (may be NULL).
+ * Element value: Q4_0 (q - 8) * d, AFF4 q * s + b.  The expert kernels
+ * multiply each weight rounded once to f16 (round to nearest even; a zero
+ * weight may come out as +0 where the exact product is -0).  Scales and
+ * biases must be finite, and for Q4_0 |d| <= 8188 (so that 8d is finite).  Tiled
+ * int4 stacks use the same tiles, with the 8 nibbles of every packed dword
+ * permuted so that nibble p holds element 2p (p < 4) or 2(p - 4) + 1, and the
+ * scales of lane l of unit u of tile t at byte t*K*SB/2 + 64*SB*u + SB*l
+ * (SB = 2 for Q4_0, 4 for AFF4).
  */
 typedef struct {
   const uint8_t *packed;
@@ -85,6 +105,7 @@ typedef struct {
   const float *global;
   int32_t E, N, K;
   int32_t layout; /* MOE_LAYOUT_CANONICAL or MOE_LAYOUT_TILED */
+  int32_t format; /* MOE_FORMAT_NVFP4, MOE_FORMAT_Q4_0 or MOE_FORMAT_AFF4 */
 } nvfp4_tensor;
 
 /*
@@ -183,11 +204,16 @@ int moe_route_bucket(const uint16_t *x, const uint16_t *w_router, const uint16_t
  * overflows; values more than 2^29 below the row's largest lose low bits);
  * fp32 accumulation; the FP32 tensor scale and the power of two are applied
  * to the fp32 sums; A is rounded to bf16 between the projections, Y to bf16.
+ * The int4 formats (MOE_FORMAT_Q4_0, MOE_FORMAT_AFF4) run on the same kernels
+ * with only the weight decode changed: each weight enters the MFMA rounded
+ * once to f16 (one fused f16 multiply-add of the code with its block's scale
+ * and bias).  gate and up must have the same format; down may differ.
  * Errors: MOE_ERR_NULL; MOE_ERR_SHAPE (T < 0, top_k <= 0, H or I <= 0,
  * descriptor shapes not [E][I][H], [E][I][H], [E][H][I] with one E);
  * MOE_ERR_UNSUPPORTED (H % 64, I % 64, E > MOE_MAX_EXPERTS,
- * top_k > MOE_MAX_TOPK, a descriptor not in MOE_LAYOUT_TILED, one expert's
- * packed tensor or the activation copies past 2 GiB); MOE_ERR_WORKSPACE.
+ * top_k > MOE_MAX_TOPK, a descriptor not in MOE_LAYOUT_TILED, an unknown
+ * format or gate and up of different formats, one expert's packed tensor or
+ * the activation copies past 2 GiB); MOE_ERR_WORKSPACE.
  */
 int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate, const nvfp4_tensor *up,
                      const nvfp4_tensor *down, const int32_t *expert_offsets,
@@ -298,10 +324,11 @@ int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *
 
 /*
  * nvfp4_repack -- weight preparation: canonical -> MOE_LAYOUT_TILED (a pure
- * permutation of bytes, see nvfp4_tensor).  src must be canonical; the
- * outputs have src's sizes and must not overlap src.
+ * permutation of bytes, and of the nibbles of int4 formats, see
+ * nvfp4_tensor), for every format.  src must be canonical; the outputs have
+ * src's sizes and must not overlap src.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (E, N <= 0, N % 16, K <= 0, K % 32),
- * MOE_ERR_UNSUPPORTED (src not canonical).
+ * MOE_ERR_UNSUPPORTED (src not canonical, unknown format).
  */
 int nvfp4_repack(const nvfp4_tensor *src, uint8_t *packed_tiled, uint8_t *scales_tiled,
                  void *stream);
@@ -313,9 +340,20 @@ int nvfp4_repack(const nvfp4_tensor *src, uint8_t *packed_tiled, uint8_t *scales
  * block scale x per-tensor F32).  A check of the unpacking used by the
  * expert kernels.
  *   out [N][K] bf16
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (e outside [0, E), N or K <= 0, K % 32).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (e outside [0, E), N or K <= 0, K % 32),
+ * MOE_ERR_UNSUPPORTED (a format other than MOE_FORMAT_NVFP4).
  */
 int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream);
+
+/*
+ * moe_dequant_f16 -- the f16 weights the expert kernels multiply, for expert
+ * e of a stack of any format and layout, through the kernels' own decode:
+ * NVFP4 E2M1 * E4M3 (exact, without the FP32 tensor scale); Q4_0 and AFF4
+ * the value rounded once to f16.  A check of the weight decode.
+ *   out [N][K] fp16 bit patterns
+ * Errors: as nvfp4_dequant_bf16, MOE_ERR_UNSUPPORTED (unknown format).
+ */
+int moe_dequant_f16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream);
 
 /* Text of a status code (static storage). */
 const char *moe_status_str(int status);

@@ -22,6 +22,12 @@ Recipe (every value is drawn once and rounded once, round-to-nearest-even):
   selection this makes the first choice roughly Zipf(1.2).
 * outlier tokens (long prefill): ceil(0.01 T) rows chosen without replacement
   are multiplied by 20 and rounded to bf16 again.
+* int4 expert stacks (the q4_0 and aff4 formats of "Gemma 4 26B-A4B (MoE) -
+  Core AI", Compression recipe), drawn directly in the stored form: codes
+  uniform on 0..15, two per byte (low nibble = even k); per block of 32 along
+  K one fp16 d ~ U(0.004, 0.008) (q4_0), or one fp16 s ~ U(0.004, 0.008) and
+  one fp16 b ~ U(-0.06, -0.035) (aff4), rounded to fp16 once.  The decoded
+  weights are then of the size of the N(0, 0.02) bf16 weights above.
 """
 from concurrent.futures import ThreadPoolExecutor
 import math
@@ -34,7 +40,7 @@ GROUP = 16
 SEED = 0
 
 # key tags
-_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER, _NORM = range(8)
+_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER, _NORM, _INT4 = range(9)
 GATE, UP, DOWN = 0, 1, 2
 
 WORKLOADS = {
@@ -159,3 +165,45 @@ def small_case(seed, t, h, i, e, k, zipf=False):
         bias = (-1.2 * 0.02 * np.log(rng.permutation(e) + 1)).astype(np.float32)
     return dict(x=x, router=dict(w_router=w, scale=scale, per_expert_scale=pes, bias=bias),
                 gate=gate, up=up, down=down)
+
+
+# fp16 scale bytes per block of 32 weights of a row
+INT4_SCALE_BYTES = {"q4_0": 2, "aff4": 4}
+
+
+def _int4_draw(rng, fmt, n, k):
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    nb = k // 32
+    if fmt == "q4_0":
+        sc = rng.uniform(0.004, 0.008, (n, nb)).astype(np.float16)
+    elif fmt == "aff4":
+        sc = np.empty((n, nb, 2), dtype=np.float16)
+        sc[..., 0] = rng.uniform(0.004, 0.008, (n, nb))
+        sc[..., 1] = rng.uniform(-0.06, -0.035, (n, nb))
+    else:
+        raise ValueError(f"unknown int4 format {fmt}")
+    return packed, np.ascontiguousarray(sc).view(np.uint8).reshape(n, -1)
+
+
+def int4_expert(fmt, layer, proj, expert, seed=SEED, h=H, i=I):
+    """One expert's int4 projection: (packed u8 [N, K/2], scale bytes u8
+    [N, K/32 * INT4_SCALE_BYTES[fmt]]) -- fp16 d, or fp16 (s, b) pairs."""
+    n, k = proj_shape(proj, h, i)
+    return _int4_draw(_rng(seed, (_INT4, fmt == "aff4", layer, proj, expert)), fmt, n, k)
+
+
+def int4_stack(fmt, layer, proj, seed=SEED, h=H, i=I, e=E):
+    """int4_expert for experts 0..e-1, stacked: ([E, N, K/2], [E, N, ...])."""
+    parts = [int4_expert(fmt, layer, proj, x, seed, h, i) for x in range(e)]
+    return np.stack([p for p, _ in parts]), np.stack([s for _, s in parts])
+
+
+def small_int4_case(seed, fmt, t, h, i, e, k, zipf=False):
+    """small_case's x and router with int4 expert stacks (gate, up, down as
+    (packed, scale bytes) pairs of [E, N, ...] arrays)."""
+    c = small_case(seed, t, h, i, e, k, zipf)
+    rng = _rng(seed, (_INT4, 99, fmt == "aff4", t, h, i, e, k))
+    for name, (n, kk) in (("gate", (i, h)), ("up", (i, h)), ("down", (h, i))):
+        parts = [_int4_draw(rng, fmt, n, kk) for _ in range(e)]
+        c[name] = (np.stack([p for p, _ in parts]), np.stack([s for _, s in parts]))
+    return c

@@ -21,9 +21,14 @@ EXPORTED = ("moe_route", "moe_route_bucket", "moe_bucket", "moe_bucket_workspace
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
             "moe_workspace_bytes", "moe_combine", "nvfp4_expert_prep_rmsnorm",
             "moe_combine_rmsnorm", "nvfp4_quantize", "nvfp4_repack",
-            "nvfp4_dequant_bf16", "moe_status_str", "moe_abi_version")
+            "nvfp4_dequant_bf16", "moe_dequant_f16", "moe_status_str", "moe_abi_version")
 
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+FORMAT_NVFP4, FORMAT_Q4_0, FORMAT_AFF4 = 0, 1, 2
+FORMATS = {"nvfp4": FORMAT_NVFP4, "q4_0": FORMAT_Q4_0, "aff4": FORMAT_AFF4}
+# scale bytes per 32 weights of a row: NVFP4 two E4M3 codes, Q4_0 one fp16 d,
+# AFF4 one fp16 s and one fp16 b
+SCALE_BYTES_PER_32 = {FORMAT_NVFP4: 2, FORMAT_Q4_0: 2, FORMAT_AFF4: 4}
 
 
 class MoeError(RuntimeError):
@@ -36,7 +41,7 @@ class MoeError(RuntimeError):
 class Nvfp4TensorC(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("global_", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("K", ctypes.c_int32), ("layout", ctypes.c_int32), ("format", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +78,7 @@ def lib(path=None):
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_repack": (ctypes.c_int, [P, vp, vp, vp]),
         "nvfp4_dequant_bf16": (ctypes.c_int, [P, i32, vp, vp]),
+        "moe_dequant_f16": (ctypes.c_int, [P, i32, vp, vp]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_abi_version": (ctypes.c_int, []),
     }
@@ -111,36 +117,52 @@ _B16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
 class Nvfp4Weights:
-    """One NVFP4 stack: packed [E,N,K/2] u8, scales [E,N,K/16] u8, global [E] f32,
-    in the canonical or the tiled byte layout (same sizes)."""
+    """One stack of 4-bit expert weights: packed [E,N,K/2] u8 codes, scales
+    [E,N,K*SB/32] bytes (SB = SCALE_BYTES_PER_32[fmt]: NVFP4 E4M3 codes per 16,
+    Q4_0 fp16 d per 32, AFF4 fp16 (s, b) per 32), global [E] f32 (NVFP4; None
+    for the int4 formats), in the canonical or the tiled byte layout (same
+    sizes)."""
 
-    def __init__(self, packed, scales, global_scale, layout=LAYOUT_CANONICAL):
+    def __init__(self, packed, scales, global_scale, layout=LAYOUT_CANONICAL, fmt=FORMAT_NVFP4):
+        if fmt not in SCALE_BYTES_PER_32:
+            raise ValueError(f"unknown weight format {fmt}")
         self.packed, self.scales, self.global_scale = packed, scales, global_scale
         self.E, self.N, k2 = packed.shape
         self.K = 2 * k2
         self.layout = layout
+        self.format = fmt
+
+    @property
+    def scale_bytes_per_row(self):
+        return self.K * SCALE_BYTES_PER_32[self.format] // 32
 
     @classmethod
-    def empty(cls, E, N, K, device="cuda", layout=LAYOUT_CANONICAL):
+    def empty(cls, E, N, K, device="cuda", layout=LAYOUT_CANONICAL, fmt=FORMAT_NVFP4):
+        sb = K * SCALE_BYTES_PER_32[fmt] // 32
+        g = torch.empty((E,), dtype=torch.float32, device=device) if fmt == FORMAT_NVFP4 else None
         return cls(torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
-                   torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
-                   torch.empty((E,), dtype=torch.float32, device=device), layout)
+                   torch.empty((E, N, sb), dtype=torch.uint8, device=device), g, layout, fmt)
 
     def c(self):
         _ptr(self.packed, torch.uint8, (self.E, self.N, self.K // 2), "packed")
-        _ptr(self.scales, torch.uint8, (self.E, self.N, self.K // 16), "scales")
-        _ptr(self.global_scale, torch.float32, (self.E,), "global")
-        return Nvfp4TensorC(self.packed.data_ptr(), self.scales.data_ptr(),
-                            self.global_scale.data_ptr(), self.E, self.N, self.K, self.layout)
+        _ptr(self.scales, torch.uint8, (self.E, self.N, self.scale_bytes_per_row), "scales")
+        if self.format == FORMAT_NVFP4 or self.global_scale is not None:
+            _ptr(self.global_scale, torch.float32, (self.E,), "global")
+        g = self.global_scale.data_ptr() if self.global_scale is not None else None
+        return Nvfp4TensorC(self.packed.data_ptr(), self.scales.data_ptr(), g, self.E, self.N,
+                            self.K, self.layout, self.format)
+
+    def _g(self, f):
+        return None if self.global_scale is None else f(self.global_scale)
 
     def select(self, e0, e1):
         """Experts e0..e1-1 (views, no copy)."""
-        return Nvfp4Weights(self.packed[e0:e1], self.scales[e0:e1], self.global_scale[e0:e1],
-                            self.layout)
+        return Nvfp4Weights(self.packed[e0:e1], self.scales[e0:e1],
+                            self._g(lambda g: g[e0:e1]), self.layout, self.format)
 
     def clone(self):
-        return Nvfp4Weights(self.packed.clone(), self.scales.clone(), self.global_scale.clone(),
-                            self.layout)
+        return Nvfp4Weights(self.packed.clone(), self.scales.clone(), self._g(torch.clone),
+                            self.layout, self.format)
 
 
 def moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps,
@@ -298,7 +320,7 @@ def nvfp4_repack(w, stream=None):
     if w.layout != LAYOUT_CANONICAL:
         raise ValueError("nvfp4_repack takes canonical weights")
     out = Nvfp4Weights(torch.empty_like(w.packed), torch.empty_like(w.scales), w.global_scale,
-                       LAYOUT_TILED)
+                       LAYOUT_TILED, w.format)
     c = w.c()
     st = lib().nvfp4_repack(ctypes.byref(c), _ptr(out.packed, torch.uint8, None, "packed"),
                             _ptr(out.scales, torch.uint8, None, "scales"), _stream(stream))
@@ -311,3 +333,13 @@ def nvfp4_dequant_bf16(w, e, out, stream=None):
     st = lib().nvfp4_dequant_bf16(ctypes.byref(c), e, _ptr(out, _B16, (w.N, w.K), "out"),
                                   _stream(stream))
     _check("nvfp4_dequant_bf16", st)
+
+
+def moe_dequant_f16(w, e, out, stream=None):
+    """The f16 weights the expert kernels multiply for expert e (any format
+    and layout; NVFP4 without its FP32 tensor scale)."""
+    c = w.c()
+    st = lib().moe_dequant_f16(ctypes.byref(c), e,
+                               _ptr(out, (torch.float16, torch.int16, torch.uint16), (w.N, w.K),
+                                    "out"), _stream(stream))
+    _check("moe_dequant_f16", st)

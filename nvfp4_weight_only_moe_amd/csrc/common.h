@@ -60,6 +60,89 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16 s) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// ---- int4 weight formats --------------------------------------------------
+// Tiled int4 dwords hold their 8 nibbles permuted: nibble p is element 2p
+// (p < 4) or 2(p - 4) + 1, so that pair i = (nibble i, nibble 4 + i) is
+// (element 2i, element 2i + 1).  OR-ing a code into the mantissa of the f16
+// 1024 gives 1024 + q exactly; subtracting 1024 leaves q.
+__device__ __forceinline__ f16x2 int4_pair(uint32_t w, int i) {
+  const uint32_t h = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+  const f16x2 base = {(f16)1024.0f, (f16)1024.0f};
+  return __builtin_bit_cast(f16x2, h) - base;
+}
+// the tiled nibble order of a canonical dword (weight preparation and checks)
+__device__ __forceinline__ uint32_t int4_tile_dword(uint32_t c) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int el = p < 4 ? 2 * p : 2 * (p - 4) + 1;
+    t |= ((c >> (4 * el)) & 15u) << (4 * p);
+  }
+  return t;
+}
+
+// Decode of one weight format inside the expert kernels: the bytes of scale
+// data a lane loads per 128-K unit (its 32 elements of one row), their
+// per-unit preparation, and the 8 f16 operands of dword j of the lane's 16
+// packed bytes.
+template <int FMT>
+struct WeightFmt;
+template <>
+struct WeightFmt<MOE_FORMAT_NVFP4> {
+  static constexpr int kScaleBytes = 2;  // two E4M3 block codes
+  struct Prep {
+    f16x2 s;
+  };
+  static __device__ __forceinline__ Prep prep(uint32_t raw) { return {block_scales_f16(raw)}; }
+  static __device__ __forceinline__ f16x8 dequant(uint32_t w, const Prep &p, int j) {
+    return dequant8(w, p.s[j >> 1]);
+  }
+};
+template <>
+struct WeightFmt<MOE_FORMAT_Q4_0> {
+  static constexpr int kScaleBytes = 2;  // fp16 d; w = (q - 8) d = fma(q, d, -8d), -8d exact
+  struct Prep {
+    f16x2 d, nb;
+  };
+  static __device__ __forceinline__ Prep prep(uint32_t raw) {
+    const f16 d = __builtin_bit_cast(f16, (uint16_t)raw);
+    const f16 nb = d * (f16)(-8.0f);
+    return {f16x2{d, d}, f16x2{nb, nb}};
+  }
+  static __device__ __forceinline__ f16x8 dequant(uint32_t w, const Prep &p, int) {
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 v = __builtin_elementwise_fma(int4_pair(w, i), p.d, p.nb);
+      o[2 * i] = v[0];
+      o[2 * i + 1] = v[1];
+    }
+    return o;
+  }
+};
+template <>
+struct WeightFmt<MOE_FORMAT_AFF4> {
+  static constexpr int kScaleBytes = 4;  // fp16 s, fp16 b; w = fma(q, s, b)
+  struct Prep {
+    f16x2 s, b;
+  };
+  static __device__ __forceinline__ Prep prep(uint32_t raw) {
+    const f16 s = __builtin_bit_cast(f16, (uint16_t)raw);
+    const f16 b = __builtin_bit_cast(f16, (uint16_t)(raw >> 16));
+    return {f16x2{s, s}, f16x2{b, b}};
+  }
+  static __device__ __forceinline__ f16x8 dequant(uint32_t w, const Prep &p, int) {
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 v = __builtin_elementwise_fma(int4_pair(w, i), p.s, p.b);
+      o[2 * i] = v[0];
+      o[2 * i + 1] = v[1];
+    }
+    return o;
+  }
+};
+
 // ---- buffer loads ------------------------------------------------------------
 // Raw buffer resource over [base, base + bytes): a load at a byte offset at
 // or beyond `bytes` returns zeros (hardware range check), which is how lanes
@@ -78,6 +161,14 @@ __device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+// the scale data of one lane and unit of a weight format
+template <int SB>
+__device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return SB == 4 ? bload4(r, off) : bload2(r, off);
 }
 
 // C[16x16] += A[16x32] * B[32x16]; lane l holds A[l%16][8(l/16)+i],

@@ -308,7 +308,7 @@ constexpr bool kGemmPipeDequant = true;
 // DIRECT: the activations are f16 in memory (gate/up): buffer loads write
 // them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
 // through registers and are converted to f16 with the row's power of two.
-template <int MSUB, int NP, bool GATED>
+template <int MSUB, int NP, bool GATED, int FMT>
 __device__ __forceinline__ void gemm_run(
     const uint16_t *__restrict__ a_src, const int32_t *__restrict__ x_exp,
     uint32_t *__restrict__ a_max, const int32_t *__restrict__ offsets,
@@ -317,6 +317,8 @@ __device__ __forceinline__ void gemm_run(
   constexpr bool DIRECT = GATED;
   constexpr int BM = kBM * MSUB;
   constexpr int NW = GATED ? 2 * NP : NP;  // weight row tiles streamed by a wave
+  using WF = WeightFmt<FMT>;
+  constexpr int SB = WF::kScaleBytes;       // scale bytes per lane and K unit
   constexpr int NBUF = DIRECT ? 3 : 2;  // LDS activation buffers
   __shared__ __attribute__((aligned(16))) uint16_t s_a[NBUF][BM * kUnitK];
   __shared__ float s_rowscale[BM];
@@ -407,16 +409,16 @@ __device__ __forceinline__ void gemm_run(
     const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
     const int nt = nt0 + (GATED ? i % NP : i);
     rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
-    rs[i] = make_rsrc(w.scales + (size_t)e * N * (K / 16), (uint32_t)((size_t)N * (K / 16)));
+    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
     vw[i] = wave_on ? (uint32_t)nt * 16 * (K / 2) + lane * 16 : kOOB;
-    vs[i] = wave_on ? (uint32_t)nt * K + lane * 2 : kOOB;
+    vs[i] = wave_on ? (uint32_t)nt * K * SB / 2 + lane * SB : kOOB;
   }
   auto load_w = [&](int u, u32x4 (&wv)[NW], uint32_t (&sv)[NW]) {
     const bool ok = u < nunits && u * kUnitK + 32 * g < K;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       wv[i] = bload16_nt(rw[i], ok ? vw[i] + (uint32_t)u * 1024 : kOOB);
-      sv[i] = bload2(rs[i], ok ? vs[i] + (uint32_t)u * 128 : kOOB);
+      sv[i] = load_scale<SB>(rs[i], ok ? vs[i] + (uint32_t)u * 64 * SB : kOOB);
     }
   };
 
@@ -431,15 +433,15 @@ __device__ __forceinline__ void gemm_run(
   // sets), and scheduling-group barriers keep that order, so LDS latency
   // hides behind the MFMAs instead of stalling each of them.
   auto compute = [&](const uint16_t *abuf, const u32x4 (&wv)[NW], const uint32_t (&sv)[NW]) {
-    f16x2 bs[NW];
+    typename WF::Prep bs[NW];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(sv[i]);
+    for (int i = 0; i < NW; ++i) bs[i] = WF::prep(sv[i]);
     if (kGemmPipeDequant) {
       // the weights of step j + 1 are dequantised while the MFMAs of step j
       // run (two register sets), one MFMA between every two VALU ops
       f16x8 a[MSUB], b[2][NW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) b[0][i] = dequant8(wv[i][0], bs[i][0]);
+      for (int i = 0; i < NW; ++i) b[0][i] = WF::dequant(wv[i][0], bs[i], 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -447,7 +449,7 @@ __device__ __forceinline__ void gemm_run(
           a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
         if (j < 3) {
 #pragma unroll
-          for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = dequant8(wv[i][j + 1], bs[i][(j + 1) >> 1]);
+          for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = WF::dequant(wv[i][j + 1], bs[i], j + 1);
         }
 #pragma unroll
         for (int q = 0; q < MSUB; ++q)
@@ -480,7 +482,7 @@ __device__ __forceinline__ void gemm_run(
       if (NA == 1) read_a(j, a[0]);
       f16x8 b[NW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) b[i] = dequant8(wv[i][j], bs[i][j >> 1]);
+      for (int i = 0; i < NW; ++i) b[i] = WF::dequant(wv[i][j], bs[i], j);
 #pragma unroll
       for (int q = 0; q < MSUB; ++q)
 #pragma unroll
@@ -555,7 +557,8 @@ __device__ __forceinline__ void gemm_run(
 
   // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
   if (GATED) {
-    const float gg = w0.global[e], gu = w1.global[e];
+    const float gg = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
+    const float gu = FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
 #pragma unroll
     for (int q = 0; q < MSUB; ++q) {
       if (q >= nq) break;
@@ -577,7 +580,7 @@ __device__ __forceinline__ void gemm_run(
       }
     }
   } else {
-    const float gd = w0.global[e];
+    const float gd = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
 #pragma unroll
     for (int q = 0; q < MSUB; ++q) {
       if (q >= nq) break;
@@ -597,7 +600,7 @@ __device__ __forceinline__ void gemm_run(
   }
 }
 
-template <int MSUB, int NP, bool GATED>
+template <int MSUB, int NP, bool GATED, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_expert_gemm(
     const uint16_t *__restrict__ a_src,  // GATED: x16 [T][K] f16; else A [P][K] bf16
     const int32_t *__restrict__ x_exp,   // GATED: exponent of each token
@@ -606,7 +609,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int E, int ncb, uint32_t a_bytes,
     Nvfp4 w0, Nvfp4 w1,                  // GATED: gate, up; else w0 = down
     int K, int N, uint16_t *__restrict__ out) {
-  gemm_run<MSUB, NP, GATED>(a_src, x_exp, a_max, offsets, sorted_pairs, top_k, E, ncb, a_bytes, w0,
+  gemm_run<MSUB, NP, GATED, FMT>(a_src, x_exp, a_max, offsets, sorted_pairs, top_k, E, ncb, a_bytes, w0,
                             w1, K, N, out);
 }
 
@@ -660,7 +663,7 @@ struct GemvArgs {
   uint16_t *out;           // GATED: A [P][N] bf16; else Y [P][N] bf16
 };
 
-template <int R, int NP, bool GATED, int KS>
+template <int R, int NP, bool GATED, int KS, int FMT>
 __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, const Nvfp4 &w1,
                                          int e, int row0, int mrows, int nt0, float *s_red) {
   constexpr int NW = GATED ? 2 * NP : NP;
@@ -692,7 +695,10 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     row_ex = row_exponent(__uint_as_float(p.a_max[prow]));
     a_scale = __builtin_ldexpf(1.0f, 14 - row_ex);
   }
-  const float ep_g0 = w0.global[e], ep_g1 = GATED ? w1.global[e] : 0.0f;
+  using WF = WeightFmt<FMT>;
+  constexpr int SB = WF::kScaleBytes;  // scale bytes per lane and K unit
+  const float ep_g0 = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
+  const float ep_g1 = !GATED ? 0.0f : FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_src, p.a_bytes);
 
   // weight streams: expert e's tensors through buffer resources; offsets past
@@ -704,13 +710,13 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
     const int nt = nt0 + (GATED ? i % NP : i);
     rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
-    rs[i] = make_rsrc(w.scales + (size_t)e * N * (K / 16), (uint32_t)((size_t)N * (K / 16)));
+    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
     vw[i] = (uint32_t)nt * 16 * (K / 2) + lane * 16;
-    vs[i] = (uint32_t)nt * K + lane * 2;
+    vs[i] = (uint32_t)nt * K * SB / 2 + lane * SB;
   }
   auto load = [&](int u, GemvUnit<NL, NW> &d) {
     const bool kok = u < ue && u * kUnitK + 32 * g < K;
-    const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 128 : kOOB;
+    const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 64 * SB : kOOB;
     // va is kOOB for rows past the tile; kOOB + 256u + 16s stays out of range
     const uint32_t oa = kok ? va + (uint32_t)u * kUnitK * 2 : kOOB;
 #pragma unroll
@@ -718,7 +724,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       d.w[i] = bload16_nt(rw[i], vw[i] + ow);
-      d.s[i] = bload2(rs[i], vs[i] + os);
+      d.s[i] = load_scale<SB>(rs[i], vs[i] + os);
     }
   };
 
@@ -739,16 +745,16 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
         }
       }
     }
-    f16x2 bs[NW];
+    typename WF::Prep bs[NW];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) bs[i] = block_scales_f16(c.s[i]);
+    for (int i = 0; i < NW; ++i) bs[i] = WF::prep(c.s[i]);
     const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // this lane's operand for MFMA j: its chunk j - h NL when that is in range
       const f16x8 aj = NL == 4 ? a[j % NL] : (j / NL == h ? a[j % NL] : zero);
 #pragma unroll
-      for (int i = 0; i < NW; ++i) acc[i] = mfma16x16x32(aj, dequant8(c.w[i][j], bs[i][j >> 1]), acc[i]);
+      for (int i = 0; i < NW; ++i) acc[i] = mfma16x16x32(aj, WF::dequant(c.w[i][j], bs[i], j), acc[i]);
     }
   };
 
@@ -890,7 +896,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 // all of K; KS = 4: the 4 waves share one column group and split K (gate/up
 // always; down for batches with few tiles, where whole-K streams per wave
 // would leave HBM idle).
-template <int ROWS, int NP, bool GATED, int KS>
+template <int ROWS, int NP, bool GATED, int KS, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
 void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets, int E, Nvfp4 w0, Nvfp4 w1) {
   constexpr int NW = GATED ? 2 * NP : NP;
@@ -901,9 +907,9 @@ void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets, int E, Nvfp4
   int e, row0, mrows;
   if (!find_tile(offsets, E, ROWS, blockIdx.y, e, row0, mrows)) return;  // uniform
   // rows per MFMA block: the smallest packing that holds the tile (uniform)
-  if (mrows <= 4) gemv_run<4, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
-  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
-  else gemv_run<16, NP, GATED, KS>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  if (mrows <= 4) gemv_run<4, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else gemv_run<16, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
 }
 
 bool tensor_ok(const nvfp4_tensor *t, int E, int N, int K) {
@@ -956,7 +962,10 @@ int check_common(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I, cons
   return MOE_OK;
 }
 
-bool tensor_null(const nvfp4_tensor *t) { return !t || !t->packed || !t->scales || !t->global; }
+// the global scale is read for NVFP4 only
+bool tensor_null(const nvfp4_tensor *t) {
+  return !t || !t->packed || !t->scales || (t->format == MOE_FORMAT_NVFP4 && !t->global);
+}
 
 constexpr int kGemmGateNP = 2;  // tiled mode: gate/up row-tile pairs per wave
 constexpr int kGemmDownNP = 4;  // tiled mode: down row tiles per wave
@@ -969,22 +978,22 @@ dim3 gemm_grid(int P, int E, int bm, int ncb) {
   return dim3((unsigned)((n + kXcds - 1) / kXcds * kXcds));
 }
 
-template <int MSUB>
+template <int MSUB, int FMT>
 int launch_gate_up(const Ws &w, const int32_t *offsets, const int32_t *sorted_pairs, int T,
                    int top_k, int E, Nvfp4 g, Nvfp4 u, int H, int I, hipStream_t s) {
   const int ncb = (I + 64 * kGemmGateNP - 1) / (64 * kGemmGateNP);
-  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmGateNP, true>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
+  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmGateNP, true, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
              dim3(kThreads), 0, s,
              (const uint16_t *)w.x16, (const int32_t *)w.x_exp, w.a_max, offsets, sorted_pairs,
              top_k, E, ncb, (uint32_t)((size_t)T * H * 2), g, u, H, I, w.a);
   return MOE_OK;
 }
 
-template <int MSUB>
+template <int MSUB, int FMT>
 int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nvfp4 d, int H,
                 int I, uint16_t *y, hipStream_t s) {
   const int ncb = (H + 64 * kGemmDownNP - 1) / (64 * kGemmDownNP);
-  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
+  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
              dim3(kThreads), 0, s, (const uint16_t *)w.a, (const int32_t *)nullptr, w.a_max, offsets,
              (const int32_t *)nullptr, top_k, E, ncb, (uint32_t)((size_t)T * top_k * I * 2), d, d,
              I, H, y);
@@ -1021,21 +1030,13 @@ extern "C" int nvfp4_expert_prep_rmsnorm(const uint16_t *x, const uint16_t *norm
   return MOE_OK;
 }
 
-extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor *up,
-                                    const int32_t *expert_offsets, const int32_t *sorted_pairs,
-                                    int32_t T, int32_t top_k, int32_t H, int32_t I,
-                                    void *workspace, size_t ws_bytes, void *stream) {
-  if (tensor_null(gate) || tensor_null(up) || !expert_offsets || (T > 0 && !sorted_pairs))
-    return MOE_ERR_NULL;
-  const int E = gate->E;
-  if (!tensor_ok(gate, E, I, H) || !tensor_ok(up, E, I, H)) return MOE_ERR_SHAPE;
-  if (gate->layout != MOE_LAYOUT_TILED || up->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
-  int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
-  if (st != MOE_OK || T == 0) return st;
-  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
-  Nvfp4 g{gate->packed, gate->scales, gate->global};
-  Nvfp4 u{up->packed, up->scales, up->global};
-  hipStream_t s = (hipStream_t)stream;
+namespace moe {
+namespace {
+
+// the gate/up and down launches of one weight format (arguments checked)
+template <int FMT>
+int gate_up_fmt(const Ws &w, const int32_t *expert_offsets, const int32_t *sorted_pairs, int T,
+                int top_k, int E, int H, int I, Nvfp4 g, Nvfp4 u, hipStream_t s) {
   if (gemv_mode(T, top_k, E)) {
     const int rows = gemv_rows(T, top_k, E);
     // the 4 waves of a workgroup split K for one column group of kGateNP row tiles
@@ -1043,29 +1044,19 @@ extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor
     const GemvArgs a{w.x16, w.x_exp, w.a_max, sorted_pairs, top_k, H, I, T * top_k,
                      (uint32_t)((size_t)T * H * 2), w.a};
     if (rows == 8)
-      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a,
+      MOE_LAUNCH((k_expert_gemv<8, kGateNP, true, 4, FMT>), grid, dim3(kThreads), 0, s, a,
                  expert_offsets, E, g, u);
     else
-      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true, 4>), grid, dim3(kThreads), 0, s, a,
+      MOE_LAUNCH((k_expert_gemv<16, kGateNP, true, 4, FMT>), grid, dim3(kThreads), 0, s, a,
                  expert_offsets, E, g, u);
     return MOE_OK;
   }
-  return launch_gate_up<4>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
+  return launch_gate_up<4, FMT>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
 }
 
-extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets,
-                                 int32_t T, int32_t top_k, int32_t H, int32_t I,
-                                 uint16_t *y_sorted, void *workspace, size_t ws_bytes,
-                                 void *stream) {
-  if (tensor_null(down) || !expert_offsets || (T > 0 && !y_sorted)) return MOE_ERR_NULL;
-  const int E = down->E;
-  if (!tensor_ok(down, E, H, I)) return MOE_ERR_SHAPE;
-  if (down->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
-  int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
-  if (st != MOE_OK || T == 0) return st;
-  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
-  Nvfp4 d{down->packed, down->scales, down->global};
-  hipStream_t s = (hipStream_t)stream;
+template <int FMT>
+int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E, int H, int I,
+             Nvfp4 d, uint16_t *y_sorted, hipStream_t s) {
   if (gemv_mode(T, top_k, E)) {
     const int rows = gemv_rows(T, top_k, E);
     const int np = rows == 16 ? kDownNPWide : kDownNP;
@@ -1074,9 +1065,9 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
     const dim3 grid(split ? (H + 16 * np - 1) / (16 * np) : gx, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
-#define MOE_GEMV_DN(ROWS, NP, KS)                                                         \
-  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS>), grid, dim3(kThreads), 0, s, a, expert_offsets, \
-             E, d, d)
+#define MOE_GEMV_DN(ROWS, NP, KS)                                                               \
+  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS, FMT>), grid, dim3(kThreads), 0, s, a,          \
+             expert_offsets, E, d, d)
     if (rows == 8) {
       if (split) MOE_GEMV_DN(8, kDownNP, 4); else MOE_GEMV_DN(8, kDownNP, 1);
     } else {
@@ -1085,7 +1076,63 @@ extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert
 #undef MOE_GEMV_DN
     return MOE_OK;
   }
-  return launch_down<4>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
+  return launch_down<4, FMT>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
+}
+
+bool format_known(int f) { return f >= MOE_FORMAT_NVFP4 && f <= MOE_FORMAT_AFF4; }
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int nvfp4_expert_gate_up(const nvfp4_tensor *gate, const nvfp4_tensor *up,
+                                    const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                    int32_t T, int32_t top_k, int32_t H, int32_t I,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+  using namespace moe;
+  if (tensor_null(gate) || tensor_null(up) || !expert_offsets || (T > 0 && !sorted_pairs))
+    return MOE_ERR_NULL;
+  const int E = gate->E;
+  if (!tensor_ok(gate, E, I, H) || !tensor_ok(up, E, I, H)) return MOE_ERR_SHAPE;
+  if (gate->layout != MOE_LAYOUT_TILED || up->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
+  if (!format_known(gate->format) || gate->format != up->format) return MOE_ERR_UNSUPPORTED;
+  int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
+  Nvfp4 g{gate->packed, gate->scales, gate->global};
+  Nvfp4 u{up->packed, up->scales, up->global};
+  hipStream_t s = (hipStream_t)stream;
+  switch (gate->format) {
+    case MOE_FORMAT_Q4_0:
+      return gate_up_fmt<MOE_FORMAT_Q4_0>(w, expert_offsets, sorted_pairs, T, top_k, E, H, I, g, u, s);
+    case MOE_FORMAT_AFF4:
+      return gate_up_fmt<MOE_FORMAT_AFF4>(w, expert_offsets, sorted_pairs, T, top_k, E, H, I, g, u, s);
+    default:
+      return gate_up_fmt<MOE_FORMAT_NVFP4>(w, expert_offsets, sorted_pairs, T, top_k, E, H, I, g, u, s);
+  }
+}
+
+extern "C" int nvfp4_expert_down(const nvfp4_tensor *down, const int32_t *expert_offsets,
+                                 int32_t T, int32_t top_k, int32_t H, int32_t I,
+                                 uint16_t *y_sorted, void *workspace, size_t ws_bytes,
+                                 void *stream) {
+  using namespace moe;
+  if (tensor_null(down) || !expert_offsets || (T > 0 && !y_sorted)) return MOE_ERR_NULL;
+  const int E = down->E;
+  if (!tensor_ok(down, E, H, I)) return MOE_ERR_SHAPE;
+  if (down->layout != MOE_LAYOUT_TILED || !format_known(down->format)) return MOE_ERR_UNSUPPORTED;
+  int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
+  Nvfp4 d{down->packed, down->scales, down->global};
+  hipStream_t s = (hipStream_t)stream;
+  switch (down->format) {
+    case MOE_FORMAT_Q4_0:
+      return down_fmt<MOE_FORMAT_Q4_0>(w, expert_offsets, T, top_k, E, H, I, d, y_sorted, s);
+    case MOE_FORMAT_AFF4:
+      return down_fmt<MOE_FORMAT_AFF4>(w, expert_offsets, T, top_k, E, H, I, d, y_sorted, s);
+    default:
+      return down_fmt<MOE_FORMAT_NVFP4>(w, expert_offsets, T, top_k, E, H, I, d, y_sorted, s);
+  }
 }
 
 extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate,
@@ -1102,6 +1149,9 @@ extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *ga
     return MOE_ERR_SHAPE;
   if (gate->layout != MOE_LAYOUT_TILED || up->layout != MOE_LAYOUT_TILED ||
       down->layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_UNSUPPORTED;
+  if (!moe::format_known(gate->format) || gate->format != up->format ||
+      !moe::format_known(down->format))
     return MOE_ERR_UNSUPPORTED;
   int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
   if (st != MOE_OK || T == 0) return st;

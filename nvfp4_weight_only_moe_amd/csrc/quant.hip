@@ -119,50 +119,79 @@ __global__ void k_write_global(const uint32_t *__restrict__ amax_bits, int E,
 }
 
 // Byte offsets of element (n, k) (k % 8 == 0) of one expert tensor in the
-// tiled layout: its packed dword and its scale byte.  Lane l = 16 g + r of
-// unit u of row tile t holds row 16t + r, k = 128u + 32g .. +31.
-__device__ __forceinline__ void tiled_offsets(size_t n, size_t k, int K, size_t *pw, size_t *ps) {
+// tiled layout: its packed dword and the first byte of its lane's scale data
+// (SB bytes per lane and unit).  Lane l = 16 g + r of unit u of row tile t
+// holds row 16t + r, k = 128u + 32g .. +31.
+__device__ __forceinline__ void tiled_offsets(size_t n, size_t k, int K, int SB, size_t *pw,
+                                              size_t *ps) {
   const size_t t = n / 16, r = n % 16, u = k / 128, g = (k % 128) / 32, w = (k % 32) / 8;
   const size_t lane = 16 * g + r;
   *pw = t * 16 * (size_t)(K / 2) + u * 1024 + lane * 16 + w * 4;
-  *ps = t * (size_t)K + u * 128 + lane * 2 + (k % 32) / 16;
+  *ps = t * (size_t)K * SB / 2 + u * 64 * SB + lane * SB;
+}
+// the canonical offset of the lane scale data of element (n, k): NVFP4 the
+// two block codes of k's 32 elements, int4 the fp16 d or (s, b) of k's block
+template <int FMT>
+__device__ __forceinline__ size_t canonical_scale_offset(size_t n, size_t k, int K) {
+  constexpr int SB = WeightFmt<FMT>::kScaleBytes;
+  return FMT == MOE_FORMAT_NVFP4 ? n * (K / 16) + (k / 32) * 2 : (n * (K / 32) + k / 32) * SB;
 }
 
-// canonical -> tiled, one thread per 16-byte lane slot
+// canonical -> tiled, one thread per 16-byte lane slot (int4 formats: the
+// nibbles of each dword in the tiled order)
+template <int FMT>
 __global__ __launch_bounds__(256) void k_repack(const uint8_t *__restrict__ packed,
                                                 const uint8_t *__restrict__ scales, int N, int K,
                                                 size_t nslots, uint8_t *__restrict__ tp,
                                                 uint8_t *__restrict__ ts) {
+  constexpr int SB = WeightFmt<FMT>::kScaleBytes;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // (expert, row, 32-k slice)
   if (i >= nslots) return;
   const size_t per_e = (size_t)N * (K / 32);
   const size_t e = i / per_e, rem = i % per_e;
   const size_t n = rem / (K / 32), k = (rem % (K / 32)) * 32;
   size_t pw, ps;
-  tiled_offsets(n, k, K, &pw, &ps);
+  tiled_offsets(n, k, K, SB, &pw, &ps);
   const uint8_t *src = packed + e * N * (K / 2) + n * (K / 2) + k / 2;
-  *(u32x4 *)(tp + e * N * (K / 2) + pw) = *(const u32x4 *)src;
-  const uint8_t *ssrc = scales + e * N * (K / 16) + n * (K / 16) + k / 16;
-  uint8_t *sdst = ts + e * N * (K / 16) + ps;
-  sdst[0] = ssrc[0];
-  sdst[1] = ssrc[1];
+  u32x4 v = *(const u32x4 *)src;
+  if (FMT != MOE_FORMAT_NVFP4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = int4_tile_dword(v[q]);
+  }
+  *(u32x4 *)(tp + e * N * (K / 2) + pw) = v;
+  const size_t sbytes = (size_t)N * K * SB / 32;  // per expert
+  const uint8_t *ssrc = scales + e * sbytes + canonical_scale_offset<FMT>(n, k, K);
+  uint8_t *sdst = ts + e * sbytes + ps;
+#pragma unroll
+  for (int b = 0; b < SB; ++b) sdst[b] = ssrc[b];
 }
 
-// one thread per 8 elements: the expert kernels' decode, widened to bf16 (exact)
+// one thread per 8 elements: the expert kernels' decode (WeightFmt), as f16
+// bit patterns; BF16: NVFP4 only, widened to bf16 (exact)
+template <int FMT, bool BF16>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ packed,
                                                  const uint8_t *__restrict__ scales, int N, int K,
                                                  int tiled, uint16_t *__restrict__ out) {
+  constexpr int SB = WeightFmt<FMT>::kScaleBytes;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // dword index
   if (i >= (size_t)N * K / 8) return;
   const size_t n = i / (K / 8), k = (i % (K / 8)) * 8;
-  size_t pw = n * (K / 2) + k / 2, ps = n * (K / 16) + k / 16;
-  if (tiled) tiled_offsets(n, k, K, &pw, &ps);
-  const uint32_t wv = *(const uint32_t *)(packed + pw);
-  const f16x8 h = dequant8(wv, block_scales_f16(scales[ps])[0]);
-  u32x4 o;
+  size_t pw = n * (K / 2) + k / 2, ps = canonical_scale_offset<FMT>(n, k, K);
+  if (tiled) tiled_offsets(n, k, K, SB, &pw, &ps);
+  uint32_t wv = *(const uint32_t *)(packed + pw);
+  if (FMT != MOE_FORMAT_NVFP4 && !tiled) wv = int4_tile_dword(wv);
+  uint32_t raw = scales[ps] | ((uint32_t)scales[ps + 1] << 8);
+  if (SB == 4) raw |= ((uint32_t)scales[ps + 2] << 16) | ((uint32_t)scales[ps + 3] << 24);
+  const f16x8 h = WeightFmt<FMT>::dequant(wv, WeightFmt<FMT>::prep(raw), (int)((k % 32) / 8));
+  // f16: the vector's bytes as they are (a bit_cast of a single vector
+  // element h[i] would read element 0 with this compiler, so the whole
+  // vector is cast)
+  u32x4 o = __builtin_bit_cast(u32x4, h);
+  if (BF16) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = (uint32_t)f32_to_bf16((float)h[2 * q]) | ((uint32_t)f32_to_bf16((float)h[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)f32_to_bf16((float)h[2 * q]) | ((uint32_t)f32_to_bf16((float)h[2 * q + 1]) << 16);
+  }
   *(u32x4 *)(out + n * K + k) = o;
 }
 
@@ -196,23 +225,61 @@ extern "C" int nvfp4_repack(const nvfp4_tensor *src, uint8_t *packed_tiled, uint
   if (src->E <= 0 || src->N <= 0 || src->N % 16 || src->K <= 0 || src->K % 32) return MOE_ERR_SHAPE;
   if (src->layout != MOE_LAYOUT_CANONICAL) return MOE_ERR_UNSUPPORTED;
   const size_t nslots = (size_t)src->E * src->N * (src->K / 32);
-  MOE_LAUNCH(k_repack, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
-             src->packed, src->scales, src->N, src->K, nslots, packed_tiled, scales_tiled);
+  const dim3 grid((unsigned)((nslots + 255) / 256));
+  hipStream_t s = (hipStream_t)stream;
+  switch (src->format) {
+    case MOE_FORMAT_NVFP4:
+      MOE_LAUNCH(k_repack<MOE_FORMAT_NVFP4>, grid, dim3(256), 0, s, src->packed, src->scales,
+                 src->N, src->K, nslots, packed_tiled, scales_tiled);
+      break;
+    case MOE_FORMAT_Q4_0:
+      MOE_LAUNCH(k_repack<MOE_FORMAT_Q4_0>, grid, dim3(256), 0, s, src->packed, src->scales,
+                 src->N, src->K, nslots, packed_tiled, scales_tiled);
+      break;
+    case MOE_FORMAT_AFF4:
+      MOE_LAUNCH(k_repack<MOE_FORMAT_AFF4>, grid, dim3(256), 0, s, src->packed, src->scales,
+                 src->N, src->K, nslots, packed_tiled, scales_tiled);
+      break;
+    default: return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
-extern "C" int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream) {
+namespace {
+int dequant_checked(const nvfp4_tensor *w, int32_t e, uint16_t *out, bool bf16, void *stream) {
   using namespace moe;
   if (!w || !out || !w->packed || !w->scales) return MOE_ERR_NULL;
   if (w->N <= 0 || w->K <= 0 || w->K % 32 || e < 0 || e >= w->E) return MOE_ERR_SHAPE;
   if (w->layout != MOE_LAYOUT_CANONICAL && w->layout != MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
+  if (w->format < MOE_FORMAT_NVFP4 || w->format > MOE_FORMAT_AFF4) return MOE_ERR_UNSUPPORTED;
+  if (bf16 && w->format != MOE_FORMAT_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (w->layout == MOE_LAYOUT_TILED && w->N % 16) return MOE_ERR_SHAPE;
   const size_t n8 = (size_t)w->N * w->K / 8;
+  const int sb = w->format == MOE_FORMAT_AFF4 ? 4 : 2;
   const uint8_t *p = w->packed + (size_t)e * w->N * (w->K / 2);
-  const uint8_t *sc = w->scales + (size_t)e * w->N * (w->K / 16);
-  MOE_LAUNCH(k_dequant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, (hipStream_t)stream, p,
-             sc, w->N, w->K, (int)(w->layout == MOE_LAYOUT_TILED), out);
+  const uint8_t *sc = w->scales + (size_t)e * w->N * w->K * sb / 32;
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  hipStream_t s = (hipStream_t)stream;
+  const int tiled = w->layout == MOE_LAYOUT_TILED;
+  if (bf16) {
+    MOE_LAUNCH((k_dequant<MOE_FORMAT_NVFP4, true>), grid, dim3(256), 0, s, p, sc, w->N, w->K, tiled, out);
+  } else if (w->format == MOE_FORMAT_NVFP4) {
+    MOE_LAUNCH((k_dequant<MOE_FORMAT_NVFP4, false>), grid, dim3(256), 0, s, p, sc, w->N, w->K, tiled, out);
+  } else if (w->format == MOE_FORMAT_Q4_0) {
+    MOE_LAUNCH((k_dequant<MOE_FORMAT_Q4_0, false>), grid, dim3(256), 0, s, p, sc, w->N, w->K, tiled, out);
+  } else {
+    MOE_LAUNCH((k_dequant<MOE_FORMAT_AFF4, false>), grid, dim3(256), 0, s, p, sc, w->N, w->K, tiled, out);
+  }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" int nvfp4_dequant_bf16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream) {
+  return dequant_checked(w, e, out, true, stream);
+}
+
+extern "C" int moe_dequant_f16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *stream) {
+  return dequant_checked(w, e, out, false, stream);
 }
 
 extern "C" const char *moe_status_str(int status) {
@@ -227,4 +294,4 @@ extern "C" const char *moe_status_str(int status) {
   }
 }
 
-extern "C" int moe_abi_version(void) { return (1 << 16) | 0; }
+extern "C" int moe_abi_version(void) { return (2 << 16) | 0; }

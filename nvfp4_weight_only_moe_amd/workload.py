@@ -1,5 +1,6 @@
 """Device-resident synthetic workloads: seeded bf16 inputs from ``moe_synth``,
-uploaded once, expert weights quantised on the GPU by ``nvfp4_quantize``."""
+uploaded once, expert weights quantised on the GPU by ``nvfp4_quantize`` (or,
+for the int4 formats, uploaded as drawn and repacked)."""
 import numpy as np
 import torch
 
@@ -58,6 +59,32 @@ def build_small_layer(case, top_k, device="cuda"):
     g = quantize_stack_on_gpu(case["gate"], device)
     u = quantize_stack_on_gpu(case["up"], device)
     d = quantize_stack_on_gpu(case["down"], device)
+    return MoeLayer(wr, sc, pes, bias, g, u, d, top_k=top_k)
+
+
+def int4_to_device(fmt, packed, scales, device="cuda", tiled=True):
+    """An int4 stack (``moe_synth`` arrays: packed [E, N, K/2] u8, scale bytes
+    [E, N, ...] u8) as Nvfp4Weights of format ``fmt`` ("q4_0" or "aff4")."""
+    w = _lib.Nvfp4Weights(torch.from_numpy(np.ascontiguousarray(packed)).to(device),
+                          torch.from_numpy(np.ascontiguousarray(scales)).to(device), None,
+                          _lib.LAYOUT_CANONICAL, _lib.FORMATS[fmt])
+    return _lib.nvfp4_repack(w) if tiled else w
+
+
+def build_int4_layer(fmt, layer=0, zipf=False, device="cuda", seed=S.SEED, h=S.H, i=S.I, e=S.E,
+                     k=S.TOP_K):
+    """One model-shaped layer with int4 expert stacks of format ``fmt``."""
+    wr, sc, pes, bias = router_to_device(S.router_params(layer, seed, h, e, zipf), device)
+    stacks = [int4_to_device(fmt, *S.int4_stack(fmt, layer, proj, seed, h, i, e), device=device)
+              for proj in (S.GATE, S.UP, S.DOWN)]
+    torch.cuda.synchronize()
+    return MoeLayer(wr, sc, pes, bias, stacks[0], stacks[1], stacks[2], k)
+
+
+def build_small_int4_layer(case, fmt, top_k, device="cuda"):
+    """A ``moe_synth.small_int4_case`` dict on the device."""
+    wr, sc, pes, bias = router_to_device(case["router"], device)
+    g, u, d = (int4_to_device(fmt, *case[n], device=device) for n in ("gate", "up", "down"))
     return MoeLayer(wr, sc, pes, bias, g, u, d, top_k=top_k)
 
 

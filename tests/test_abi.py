@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for st in (0, -1, -2, -3, -4, -5):
         assert L.moe_status_str(st)
-    assert L.moe_abi_version() >> 16 == 1
+    assert L.moe_abi_version() >> 16 == 2
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -96,9 +96,9 @@ def test_route_bucket_rejects(L):
     assert L.moe_route_bucket(*a) == -2
 
 
-def _tensor(E, N, K, layout=1):
+def _tensor(E, N, K, layout=1, fmt=0, glob=0x3000):
     from nvfp4_weight_only_moe_amd._lib import Nvfp4TensorC
-    return Nvfp4TensorC(0x1000, 0x2000, 0x3000, E, N, K, layout)
+    return Nvfp4TensorC(0x1000, 0x2000, glob, E, N, K, layout, fmt)
 
 
 def test_expert_mlp_rejects(L):
@@ -187,3 +187,37 @@ def test_workspace_sizes_cover_buffers(L):
     assert ws >= T * H * 2 + P * I * 2 + P * 4 + T * 4
     assert L.moe_workspace_bytes(0, k, E, H, I) > 0
     assert L.moe_bucket_workspace_bytes(T, k, E) >= 256
+
+
+def test_weight_format_checks(L):
+    """Formats: unknown ones are rejected, gate and up must agree, the FP32
+    global may be NULL for the int4 formats only (T = 0: nothing launched)."""
+    T, k, E, H, I = 64, 8, 128, 2816, 704
+    ws = L.moe_workspace_bytes(T, k, E, H, I)
+    R = ctypes.byref
+    for fmt in (1, 2):
+        g, u, d = (_tensor(E, I, H, fmt=fmt, glob=None), _tensor(E, I, H, fmt=fmt, glob=None),
+                   _tensor(E, H, I, fmt=fmt, glob=None))
+        assert L.nvfp4_expert_gate_up(R(g), R(u), FAKE, FAKE, 0, k, H, I, FAKE, ws, NULL) == 0
+        assert L.nvfp4_expert_down(R(d), FAKE, 0, k, H, I, FAKE, FAKE, ws, NULL) == 0
+        assert L.nvfp4_expert_mlp(FAKE, R(g), R(u), R(d), FAKE, FAKE, 0, k, H, I, FAKE, FAKE, ws,
+                                  NULL) == 0
+    g0 = _tensor(E, I, H, fmt=0, glob=None)                      # NVFP4 needs its global
+    assert L.nvfp4_expert_gate_up(R(g0), R(g0), FAKE, FAKE, 0, k, H, I, FAKE, ws, NULL) == -1
+    q, a = _tensor(E, I, H, fmt=1), _tensor(E, I, H, fmt=2)
+    assert L.nvfp4_expert_gate_up(R(q), R(a), FAKE, FAKE, T, k, H, I, FAKE, ws, NULL) == -4
+    assert L.nvfp4_expert_mlp(FAKE, R(q), R(a), R(_tensor(E, H, I, fmt=1)), FAKE, FAKE, T, k, H,
+                              I, FAKE, FAKE, ws, NULL) == -4
+    bad = _tensor(E, I, H, fmt=3)
+    assert L.nvfp4_expert_gate_up(R(bad), R(bad), FAKE, FAKE, T, k, H, I, FAKE, ws, NULL) == -4
+    assert L.nvfp4_expert_down(R(_tensor(E, H, I, fmt=-1)), FAKE, T, k, H, I, FAKE, FAKE, ws,
+                               NULL) == -4
+    # mixed formats across gate/up and down are allowed (T = 0)
+    assert L.nvfp4_expert_mlp(FAKE, R(q), R(q), R(_tensor(E, H, I, fmt=2)), FAKE, FAKE, 0, k, H,
+                              I, FAKE, FAKE, ws, NULL) == 0
+    # dequant / repack
+    assert L.moe_dequant_f16(R(_tensor(2, 16, 64, fmt=3)), 0, FAKE, NULL) == -4
+    assert L.moe_dequant_f16(R(_tensor(2, 16, 64, fmt=1, glob=None)), 2, FAKE, NULL) == -2
+    assert L.moe_dequant_f16(R(_tensor(2, 16, 64, fmt=2, glob=None)), 0, NULL, NULL) == -1
+    assert L.nvfp4_dequant_bf16(R(_tensor(2, 16, 64, fmt=1)), 0, FAKE, NULL) == -4
+    assert L.nvfp4_repack(R(_tensor(2, 16, 64, layout=0, fmt=4)), FAKE, FAKE, NULL) == -4

@@ -60,3 +60,33 @@ def test_round_f16_ties_to_even():
     x = np.random.default_rng(2).standard_normal(1000)
     r = Q.round_f16(x)
     assert np.all(np.abs(r - x) <= np.abs(x) * 2.0 ** -11 + 2.0 ** -25)
+
+
+def test_synthetic_int4_stacks_follow_their_recipe():
+    """The seeded int4 inputs: deterministic per (format, layer, projection,
+    expert), stored shapes, fp16 scales inside the drawn ranges, and decoded
+    weights of the size of the bf16 N(0, 0.02) weights."""
+    import moe_synth as S
+    for fmt in ("q4_0", "aff4"):
+        p, s = S.int4_expert(fmt, 0, S.GATE, 5)
+        p2, s2 = S.int4_expert(fmt, 0, S.GATE, 5)
+        assert np.array_equal(p, p2) and np.array_equal(s, s2)
+        assert not np.array_equal(p, S.int4_expert(fmt, 0, S.GATE, 6)[0])
+        assert p.shape == (S.I, S.H // 2) and p.dtype == np.uint8
+        assert s.shape == (S.I, S.H // 32 * S.INT4_SCALE_BYTES[fmt])
+        bits = s.view(np.uint16)
+        if fmt == "q4_0":
+            d = Q.f16_bits_to_f64(bits)
+            assert d.min() >= 0.004 - 1e-5 and d.max() <= 0.008 + 1e-5
+            w = Q.decode_q4_0(p, bits)
+        else:
+            sb = Q.f16_bits_to_f64(bits.reshape(S.I, -1, 2))
+            assert sb[..., 0].min() >= 0.004 - 1e-5 and sb[..., 0].max() <= 0.008 + 1e-5
+            assert sb[..., 1].min() >= -0.06 - 1e-4 and sb[..., 1].max() <= -0.035 + 1e-4
+            w = Q.decode_aff4(p, bits.reshape(S.I, -1, 2))
+        assert 0.015 < w.std() < 0.045
+        # every code appears, with roughly uniform frequency
+        cnt = np.bincount(Q.unpack_codes(p).ravel(), minlength=16)
+        assert cnt.min() > 0.9 * cnt.mean()
+    c = S.small_int4_case(3, "aff4", 5, 128, 64, 8, 2)
+    assert c["gate"][0].shape == (8, 64, 64) and c["down"][1].shape == (8, 128, 64 // 32 * 4)
