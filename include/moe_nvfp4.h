@@ -95,7 +95,8 @@ extern "C" {
  * weight may come out as +0 where the exact product is -0).  Scales and
  * biases must be finite, and for Q4_0 |d| <= 8188 (so that 8d is finite).  Tiled
  * int4 stacks use the same tiles, with the 8 nibbles of every packed dword
- * permuted so that nibble p holds element 2p (p < 4) or 2(p - 4) + 1, and the
+ * (elements j = 0..7, canonical bits 4j..4j+3) permuted so that byte b holds
+ * element b in its low nibble and element b + 4 in its high nibble, and the
  * scales of lane l of unit u of tile t at byte t*K*SB/2 + 64*SB*u + SB*l
  * (SB = 2 for Q4_0, 4 for AFF4).
  */

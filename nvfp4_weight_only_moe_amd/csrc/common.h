@@ -61,22 +61,28 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16 s) {
 }
 
 // ---- int4 weight formats --------------------------------------------------
-// Tiled int4 dwords hold their 8 nibbles permuted: nibble p is element 2p
-// (p < 4) or 2(p - 4) + 1, so that pair i = (nibble i, nibble 4 + i) is
-// (element 2i, element 2i + 1).  OR-ing a code into the mantissa of the f16
-// 1024 gives 1024 + q exactly; subtracting 1024 leaves q.
-__device__ __forceinline__ f16x2 int4_pair(uint32_t w, int i) {
-  const uint32_t h = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-  const f16x2 base = {(f16)1024.0f, (f16)1024.0f};
-  return __builtin_bit_cast(f16x2, h) - base;
+// An E4M3 byte with value 0..15 encodes exactly q * 2^-9 (subnormals m * 2^-9
+// for q < 8, exponent 1 for 8 <= q < 16), linear in q.  So masking each code
+// into a byte of its own and running the hardware FP8 -> f16 conversion with
+// scale 2^9 gives q as an exact f16, two codes per conversion.  Tiled int4
+// dwords hold their nibbles in the order this wants: byte b has element b in
+// its low nibble and element b + 4 in its high nibble.
+__device__ __forceinline__ void int4_codes_f16(uint32_t w, f16x2 &e01, f16x2 &e23, f16x2 &e45,
+                                               f16x2 &e67) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  e01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+  e23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+  e45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+  e67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
 }
-// the tiled nibble order of a canonical dword (weight preparation and checks)
+// the tiled nibble order of a canonical dword (element j in bits 4j):
+// element j < 4 moves to bits 8j, element j >= 4 to bits 8(j - 4) + 4
 __device__ __forceinline__ uint32_t int4_tile_dword(uint32_t c) {
   uint32_t t = 0;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int el = p < 4 ? 2 * p : 2 * (p - 4) + 1;
-    t |= ((c >> (4 * el)) & 15u) << (4 * p);
+  for (int j = 0; j < 8; ++j) {
+    const int pos = j < 4 ? 8 * j : 8 * (j - 4) + 4;
+    t |= ((c >> (4 * j)) & 15u) << pos;
   }
   return t;
 }
@@ -110,14 +116,13 @@ struct WeightFmt<MOE_FORMAT_Q4_0> {
     return {f16x2{d, d}, f16x2{nb, nb}};
   }
   static __device__ __forceinline__ f16x8 dequant(uint32_t w, const Prep &p, int) {
-    f16x8 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2 v = __builtin_elementwise_fma(int4_pair(w, i), p.d, p.nb);
-      o[2 * i] = v[0];
-      o[2 * i + 1] = v[1];
-    }
-    return o;
+    f16x2 a, b, c, d;
+    int4_codes_f16(w, a, b, c, d);
+    a = __builtin_elementwise_fma(a, p.d, p.nb);
+    b = __builtin_elementwise_fma(b, p.d, p.nb);
+    c = __builtin_elementwise_fma(c, p.d, p.nb);
+    d = __builtin_elementwise_fma(d, p.d, p.nb);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
 };
 template <>
@@ -132,14 +137,13 @@ struct WeightFmt<MOE_FORMAT_AFF4> {
     return {f16x2{s, s}, f16x2{b, b}};
   }
   static __device__ __forceinline__ f16x8 dequant(uint32_t w, const Prep &p, int) {
-    f16x8 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2 v = __builtin_elementwise_fma(int4_pair(w, i), p.s, p.b);
-      o[2 * i] = v[0];
-      o[2 * i + 1] = v[1];
-    }
-    return o;
+    f16x2 a, b, c, d;
+    int4_codes_f16(w, a, b, c, d);
+    a = __builtin_elementwise_fma(a, p.s, p.b);
+    b = __builtin_elementwise_fma(b, p.s, p.b);
+    c = __builtin_elementwise_fma(c, p.s, p.b);
+    d = __builtin_elementwise_fma(d, p.s, p.b);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
 };
 

@@ -48,19 +48,16 @@ def _oracle_fns(fmt, stacks):
 def _tiled_int4_reference(packed, scales, sb):
     """numpy statement of the tiled int4 layout (header: nvfp4_tensor): the
     NVFP4 tile order of the packed bytes, the 8 nibbles of each dword
-    reordered (nibble p <- element 2p for p < 4, element 2(p - 4) + 1 above),
-    and the scales of lane l of unit u of tile t at t*K*SB/2 + 64*SB*u + SB*l."""
+    reordered (byte b <- element b in the low nibble, element b + 4 in the
+    high one), and the scales of lane l of unit u of tile t at
+    t*K*SB/2 + 64*SB*u + SB*l."""
     E, N, K2 = packed.shape
     K = 2 * K2
     codes = np.empty((E, N, K), dtype=np.uint8)
     codes[..., 0::2] = packed & 15
     codes[..., 1::2] = packed >> 4
-    perm = np.empty_like(codes)
     c8 = codes.reshape(E, N, K // 8, 8)
-    p8 = perm.reshape(E, N, K // 8, 8)
-    for p in range(8):
-        p8[..., p] = c8[..., 2 * p] if p < 4 else c8[..., 2 * (p - 4) + 1]
-    rebyte = (perm[..., 0::2] | (perm[..., 1::2] << 4)).astype(np.uint8)
+    rebyte = (c8[..., 0:4] | (c8[..., 4:8] << 4)).astype(np.uint8).reshape(E, N, K // 2)
     tp = np.zeros_like(packed).reshape(E, -1)
     ts = np.zeros_like(scales).reshape(E, -1)
     for n in range(N):
