@@ -461,13 +461,15 @@ def profiled_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary of this workload, or None when there is none or when the kernel
     source has changed since the counters were taken (the summary records
-    the sha256 of the source file it was taken with)."""
+    the sha256 of mlp.hip followed by common.h as they were then)."""
     import hashlib
     path = os.path.join(HERE, "profiles", f"hbm_traffic__{workload}.txt")
-    src = os.path.join(HERE, "nvfp4_weight_only_moe_amd", "csrc", "mlp.hip")
     if not os.path.exists(path):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in ("mlp.hip", "common.h"):     # the expert kernels and their decode
+        h.update(open(os.path.join(HERE, "nvfp4_weight_only_moe_amd", "csrc", f), "rb").read())
+    digest = h.hexdigest()
     rec = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
