@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--prep-branch", action="store_true",
+                    help="run the expert-input prep on a parallel graph branch (forked and "
+                         "joined per layer) instead of first on the one stream")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter scaling reference)")
     return ap.parse_args()
@@ -286,20 +289,27 @@ def main():
     fork_join = [(hip.event(), hip.event()) for _ in range(args.steps * n_layers)]
 
     def queue_steps():
-        """K steps; per layer the prep runs on `side`, forked after the
-        previous layer's combine and joined before the gate/up GEMM."""
+        """K steps on one stream: per layer prep, route + bucket, gate/up,
+        down, combine.  With --prep-branch the prep runs on `side` instead,
+        forked after the previous layer's combine and joined before the
+        gate/up GEMM (a dependency across queues costs more than the prep)."""
         n = 0
         for layers in step_plan:
             for li, layer in enumerate(layers):
-                route_bucket, prep, gate_up, down, combine = stage_calls(layer, side, li)
-                fork, join = fork_join[n]
-                n += 1
-                hip.record(fork, hs, False)
-                hip.wait(hside, fork)
-                prep()
-                hip.record(join, hside, False)
-                route_bucket()
-                hip.wait(hs, join)
+                route_bucket, prep, gate_up, down, combine = stage_calls(
+                    layer, side if args.prep_branch else None, li)
+                if args.prep_branch:
+                    fork, join = fork_join[n]
+                    n += 1
+                    hip.record(fork, hs, False)
+                    hip.wait(hside, fork)
+                    prep()
+                    hip.record(join, hside, False)
+                    route_bucket()
+                    hip.wait(hs, join)
+                else:
+                    prep()
+                    route_bucket()
                 gate_up()
                 down()
                 combine()
@@ -310,7 +320,7 @@ def main():
     if not args.eager:
         try:
             graph = hip.instantiate(hip.capture_graph(hs, queue_steps))
-            mode = "hip_graph (prep on a parallel branch)"
+            mode = "hip_graph (prep on a parallel branch)" if args.prep_branch else "hip_graph (one stream)"
             hip.launch(graph, hs)            # one untimed replay
             stream.synchronize()
         except Exception as exc:

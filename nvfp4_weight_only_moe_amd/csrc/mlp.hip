@@ -642,6 +642,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 constexpr int kGemvPD = 1;
 constexpr int kGateNP = 2;       // gate/up row-tile pairs per wave (K split)
 constexpr int kDownNP = 2;       // down row tiles per wave (8-row tiles)
+constexpr int kDownNPMany = 4;   // ... when there are many tiles (P >= 3E)
 constexpr int kDownNPWide = 4;   // ... with 16-row tiles
 // down takes the K split when the unsplit grid would have fewer workgroups
 constexpr int kGemvSplitBelow = 1024;
@@ -1059,7 +1060,10 @@ int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E
              Nvfp4 d, uint16_t *y_sorted, hipStream_t s) {
   if (gemv_mode(T, top_k, E)) {
     const int rows = gemv_rows(T, top_k, E);
-    const int np = rows == 16 ? kDownNPWide : kDownNP;
+    // more row tiles per wave halves the activation loads per weight byte
+    // but also the waves; it pays once the tiles alone fill the chip
+    const bool many = (long long)T * top_k >= 3LL * E;
+    const int np = rows == 16 ? kDownNPWide : many ? kDownNPMany : kDownNP;
     const int gx = (H + 64 * np - 1) / (64 * np);
     const bool split = gx * w.L.max_tiles < kGemvSplitBelow;
     const dim3 grid(split ? (H + 16 * np - 1) / (16 * np) : gx, w.L.max_tiles);
@@ -1068,7 +1072,9 @@ int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E
 #define MOE_GEMV_DN(ROWS, NP, KS)                                                               \
   MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS, FMT>), grid, dim3(kThreads), 0, s, a,          \
              expert_offsets, E, d, d)
-    if (rows == 8) {
+    if (rows == 8 && many) {
+      if (split) MOE_GEMV_DN(8, kDownNPMany, 4); else MOE_GEMV_DN(8, kDownNPMany, 1);
+    } else if (rows == 8) {
       if (split) MOE_GEMV_DN(8, kDownNP, 4); else MOE_GEMV_DN(8, kDownNP, 1);
     } else {
       if (split) MOE_GEMV_DN(16, kDownNPWide, 4); else MOE_GEMV_DN(16, kDownNPWide, 1);
