@@ -37,7 +37,8 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
-STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
+STAGES = ("route_bucket_prep", "gate_up", "down", "combine")
+SEPARATE_STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
 
 
 def parse():
@@ -60,9 +61,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--separate-prep", action="store_true",
+                    help="queue moe_route_bucket and the expert-input prep as two calls instead "
+                         "of one moe_route_bucket_prep")
     ap.add_argument("--prep-branch", action="store_true",
-                    help="run the expert-input prep on a parallel graph branch (forked and "
-                         "joined per layer) instead of first on the one stream")
+                    help="with --separate-prep: run the prep on a parallel graph branch (forked "
+                         "and joined per layer) instead of first on the one stream")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter scaling reference)")
     return ap.parse_args()
@@ -256,12 +260,14 @@ def main():
     hs, hside = ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side.cuda_stream)
     from nvfp4_weight_only_moe_amd import _lib as C
 
+    separate = args.separate_prep or args.prep_branch
+    stages = SEPARATE_STAGES if separate else STAGES
+
     def stage_calls(layer, prep_stream=None, li=0):
-        """The five stage calls of one block pass (layer li of the step), in
-        STAGES order."""
+        """The stage calls of one block pass (layer li of the step), by name."""
         x_in = xs[li] if chain else x
+        nm = norms[li] if chain else None
         if chain:
-            nm = norms[li]
             prep = lambda: C.nvfp4_expert_prep_rmsnorm(x_in, nm.pre, nm.eps, E, I, K, buf.ws,
                                                        prep_stream or stream)
             combine = lambda: C.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank,
@@ -271,48 +277,55 @@ def main():
             prep = lambda: C.nvfp4_expert_prep(x_in, E, I, K, buf.ws, prep_stream or stream)
             combine = lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out,
                                             stream)
-        return [
-            lambda: C.moe_route_bucket(x_in, layer.w_router, layer.router_scale,
-                                       layer.per_expert_scale, layer.logit_bias, K, layer.eps,
-                                       buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
-                                       buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
-                                       buf.bucket_ws, stream),
-            prep,
-            lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
-                                           buf.sorted_pairs, T, K, H, buf.ws, stream),
-            lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K, buf.y_sorted,
-                                        buf.ws, stream),
-            combine,
-        ]
+        return {
+            "route_bucket_prep": lambda: C.moe_route_bucket_prep(
+                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
+                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
+                nm.pre if chain else None, nm.eps if chain else 0.0, I, buf.ws, stream),
+            "route_bucket": lambda: C.moe_route_bucket(
+                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
+                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
+                stream),
+            "prep": prep,
+            "gate_up": lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
+                                                      buf.sorted_pairs, T, K, H, buf.ws, stream),
+            "down": lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K,
+                                                buf.y_sorted, buf.ws, stream),
+            "combine": combine,
+        }
 
     step_plan = [step_layers[(args.warmup + s) % len(step_layers)] for s in range(args.steps)]
     fork_join = [(hip.event(), hip.event()) for _ in range(args.steps * n_layers)]
 
     def queue_steps():
-        """K steps on one stream: per layer prep, route + bucket, gate/up,
-        down, combine.  With --prep-branch the prep runs on `side` instead,
-        forked after the previous layer's combine and joined before the
-        gate/up GEMM (a dependency across queues costs more than the prep)."""
+        """K steps on one stream: per layer route + bucket + prep (one call),
+        gate/up, down, combine.  --separate-prep: prep, then route + bucket,
+        as two calls; --prep-branch: the prep on `side` instead, forked after
+        the previous layer's combine and joined before the gate/up GEMM (a
+        dependency across queues costs more than the prep)."""
         n = 0
         for layers in step_plan:
             for li, layer in enumerate(layers):
-                route_bucket, prep, gate_up, down, combine = stage_calls(
-                    layer, side if args.prep_branch else None, li)
+                c = stage_calls(layer, side if args.prep_branch else None, li)
                 if args.prep_branch:
                     fork, join = fork_join[n]
                     n += 1
                     hip.record(fork, hs, False)
                     hip.wait(hside, fork)
-                    prep()
+                    c["prep"]()
                     hip.record(join, hside, False)
-                    route_bucket()
+                    c["route_bucket"]()
                     hip.wait(hs, join)
+                elif separate:
+                    c["prep"]()
+                    c["route_bucket"]()
                 else:
-                    prep()
-                    route_bucket()
-                gate_up()
-                down()
-                combine()
+                    c["route_bucket_prep"]()
+                c["gate_up"]()
+                c["down"]()
+                c["combine"]()
 
     # ---- timed region: the K steps as one graph, replayed once
     mode, graph = "eager", None
@@ -320,7 +333,9 @@ def main():
     if not args.eager:
         try:
             graph = hip.instantiate(hip.capture_graph(hs, queue_steps))
-            mode = "hip_graph (prep on a parallel branch)" if args.prep_branch else "hip_graph (one stream)"
+            mode = ("hip_graph (prep on a parallel branch)" if args.prep_branch else
+                    "hip_graph (one stream, route + prep as two calls)" if separate else
+                    "hip_graph (one stream)")
             hip.launch(graph, hs)            # one untimed replay
             stream.synchronize()
         except Exception as exc:
@@ -342,7 +357,8 @@ def main():
     calls = []
     for layers in step_plan:
         for li, layer in enumerate(layers):
-            calls += stage_calls(layer, None, li)
+            c = stage_calls(layer, None, li)
+            calls += [c[n] for n in stages]
     bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
     if not args.eager:
         timed_graph = hip.timed_chain(hs, calls, bounds)
@@ -361,7 +377,7 @@ def main():
     # back (the same routing and buffers, the layers of the step plan in
     # turn, so the weights stream from HBM as in the steps) between two
     # timing events on the launch stream; the event cost spreads over R
-    gu_calls = [stage_calls(layers[li], None, li)[2]
+    gu_calls = [stage_calls(layers[li], None, li)["gate_up"]
                 for layers in step_plan for li in range(len(layers))]
     reps_gu = max(20, len(gu_calls))
     gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
@@ -379,13 +395,13 @@ def main():
     stream.synchronize()
     gu_kernel_us = 1e3 * hip.elapsed(gu_ev[0], gu_ev[1]) / reps_gu
 
-    stage_ms = {n: [] for n in STAGES}
+    stage_ms = {n: [] for n in stages}
     gpu_step_ms = []
-    per_step = n_layers * len(STAGES)
+    per_step = n_layers * len(stages)
     for s in range(args.steps):
         b = bounds[s * per_step:(s + 1) * per_step + 1]
         for j in range(per_step):
-            stage_ms[STAGES[j % len(STAGES)]].append(hip.elapsed(b[j], b[j + 1]))
+            stage_ms[stages[j % len(stages)]].append(hip.elapsed(b[j], b[j + 1]))
         gpu_step_ms.append(hip.elapsed(b[0], b[-1]))
     stage_avg_us = {n: 1e3 * float(np.mean(v)) for n, v in stage_ms.items()}
 

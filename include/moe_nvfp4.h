@@ -13,7 +13,8 @@
  *
  * The hot path is four calls, in this order, on one stream:
  *     moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine
- * (moe_route_bucket may replace the first two).
+ * (moe_route_bucket may replace the first two; moe_route_bucket_prep the
+ * first two and the expert MLP's prep stage).
  *
  * Conventions for every entry point
  *   - Every pointer is a device pointer owned by the caller (for example
@@ -184,6 +185,31 @@ int moe_route_bucket(const uint16_t *x, const uint16_t *w_router, const uint16_t
                      float *topk_w, float *topk_w_raw, float *logits, int32_t *expert_offsets,
                      int32_t *sorted_pairs, int32_t *pair_rank, void *workspace, size_t ws_bytes,
                      void *stream);
+
+/*
+ * moe_route_bucket_prep -- moe_route_bucket followed by the expert MLP's
+ * first stage on the same x: nvfp4_expert_prep(x) when norm_weight is NULL,
+ * else nvfp4_expert_prep_rmsnorm(x, norm_weight, norm_eps) (the learned norm
+ * of the expert input, "Gemma 4 26B-A4B (MoE) - Core AI", Architecture code
+ * sketch).  Same arguments as those calls and the same output bytes,
+ * including the expert workspace's f16 rows; queue nvfp4_expert_gate_up and
+ * nvfp4_expert_down after it.  For decode batches (moe_route_bucket's
+ * one-launch path) the logits kernel's expert-0 workgroups, which read every
+ * token row anyway, also write the expert input: one launch fewer.
+ *   bucket_ws, bucket_ws_bytes   as moe_route_bucket's workspace
+ *   norm_weight [H] bf16 or NULL; norm_eps >= 0 (read with norm_weight)
+ *   I, expert_ws, expert_ws_bytes   as nvfp4_expert_prep's (I, workspace)
+ * Errors: those of moe_route_bucket and of nvfp4_expert_prep(_rmsnorm),
+ * checked before any work is queued.
+ */
+int moe_route_bucket_prep(const uint16_t *x, const uint16_t *w_router,
+                          const uint16_t *router_scale, const uint16_t *per_expert_scale,
+                          const float *logit_bias, int32_t T, int32_t H, int32_t E, int32_t top_k,
+                          float eps, int32_t *topk_idx, float *topk_w, float *topk_w_raw,
+                          float *logits, int32_t *expert_offsets, int32_t *sorted_pairs,
+                          int32_t *pair_rank, void *bucket_ws, size_t bucket_ws_bytes,
+                          const uint16_t *norm_weight, float norm_eps, int32_t I,
+                          void *expert_ws, size_t expert_ws_bytes, void *stream);
 
 /*
  * nvfp4_expert_mlp -- every routed (token, expert) pair through its expert:

@@ -17,7 +17,7 @@ MOE_OK = 0
 _ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
            -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_LAUNCH"}
 
-EXPORTED = ("moe_route", "moe_route_bucket", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
+EXPORTED = ("moe_route", "moe_route_bucket", "moe_route_bucket_prep", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
             "moe_workspace_bytes", "moe_combine", "nvfp4_expert_prep_rmsnorm",
             "moe_combine_rmsnorm", "nvfp4_quantize", "nvfp4_repack",
@@ -65,6 +65,9 @@ def lib(path=None):
         "moe_bucket_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_route_bucket": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp,
                                             vp, vp, vp, vp, vp, sz, vp]),
+        "moe_route_bucket_prep": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp,
+                                                 vp, vp, vp, vp, vp, vp, sz, vp, f32, i32, vp, sz,
+                                                 vp]),
         "nvfp4_expert_mlp": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
         "nvfp4_expert_prep": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_gate_up": (ctypes.c_int, [P, P, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
@@ -201,6 +204,32 @@ def moe_route_bucket(x, w_router, router_scale, per_expert_scale, logit_bias, to
         _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("moe_route_bucket", st)
+
+
+def moe_route_bucket_prep(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps,
+                          topk_idx, topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs,
+                          pair_rank, bucket_ws, norm_weight, norm_eps, I, expert_ws, stream=None):
+    """moe_route_bucket, then nvfp4_expert_prep(x) (norm_weight None) or
+    nvfp4_expert_prep_rmsnorm(x, norm_weight, norm_eps) into expert_ws."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    st = lib().moe_route_bucket_prep(
+        _ptr(x, _B16, (T, H), "x"), _ptr(w_router, _B16, (E, H), "w_router"),
+        _ptr(router_scale, _B16, (H,), "router_scale"),
+        _ptr(per_expert_scale, _B16, (E,), "per_expert_scale"),
+        _ptr(logit_bias, torch.float32, (E,), "logit_bias"), T, H, E, top_k, float(eps),
+        _ptr(topk_idx, torch.int32, (T, top_k), "topk_idx"),
+        _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
+        _ptr(topk_w_raw, torch.float32, (T, top_k), "topk_w_raw"),
+        _ptr(logits, torch.float32, (T, E), "logits"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"),
+        _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"),
+        _ptr(bucket_ws, None, None, "bucket_ws"), bucket_ws.numel() * bucket_ws.element_size(),
+        _ptr(norm_weight, _B16, (H,), "norm_weight"), float(norm_eps), I,
+        _ptr(expert_ws, None, None, "expert_ws"), expert_ws.numel() * expert_ws.element_size(),
+        _stream(stream))
+    _check("moe_route_bucket_prep", st)
 
 
 def moe_bucket_workspace_bytes(T, top_k, E):

@@ -1,8 +1,10 @@
 """One MoE expert block as the sequence of the four C-ABI calls.
 
 ``MoeLayer`` holds one layer's device weights, ``MoeBuffers`` the caller-owned
-outputs and workspaces for a token count, ``forward`` queues
-moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine on one stream.
+outputs and workspaces for a token count, ``forward`` queues the block on one
+stream: moe_route_bucket_prep (router, bucketing and the expert-input prep of
+the same x) -> nvfp4_expert_gate_up -> nvfp4_expert_down -> moe_combine, the
+same results as moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine.
 Nothing here computes: it only allocates device memory and passes pointers.
 """
 from dataclasses import dataclass
@@ -76,6 +78,19 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
     record timing events around each stage."""
     xe = x if x_expert is None else x_expert
     mark = marks or (lambda name: None)
+    if marks is None and x_expert is None:
+        # the router and the expert-input prep read the same x: one call
+        _lib.moe_route_bucket_prep(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                                   layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx,
+                                   buf.topk_w, buf.topk_w_raw, buf.logits, buf.expert_offsets,
+                                   buf.sorted_pairs, buf.pair_rank, buf.bucket_ws, None, 0.0,
+                                   layer.I, buf.ws, stream)
+        _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs,
+                                  buf.T, layer.top_k, layer.H, buf.ws, stream)
+        _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,
+                               buf.ws, stream)
+        _lib.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out, stream)
+        return buf.out
     if marks is None:
         _lib.moe_route_bucket(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
                               layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx, buf.topk_w,
@@ -122,12 +137,11 @@ def forward_branch(layer: MoeLayer, residual, buf: MoeBuffers, norms: BranchNorm
     experts read rmsnorm(residual, pre), and buf.out = (residual +
     rmsnorm(sum_k w_k y_k, post)) * layer_scalar (no residual when
     ``norms.add_residual`` is false)."""
-    _lib.moe_route_bucket(residual, layer.w_router, layer.router_scale, layer.per_expert_scale,
-                          layer.logit_bias, layer.top_k, layer.eps, buf.topk_idx, buf.topk_w,
-                          buf.topk_w_raw, buf.logits, buf.expert_offsets, buf.sorted_pairs,
-                          buf.pair_rank, buf.bucket_ws, stream)
-    _lib.nvfp4_expert_prep_rmsnorm(residual, norms.pre, norms.eps, layer.E, layer.I, layer.top_k,
-                                   buf.ws, stream)
+    _lib.moe_route_bucket_prep(residual, layer.w_router, layer.router_scale,
+                               layer.per_expert_scale, layer.logit_bias, layer.top_k, layer.eps,
+                               buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
+                               buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
+                               norms.pre, norms.eps, layer.I, buf.ws, stream)
     _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs, buf.T,
                               layer.top_k, layer.H, buf.ws, stream)
     _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,

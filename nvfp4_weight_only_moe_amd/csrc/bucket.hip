@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_select_bucket_last(
     const float *__restrict__ logits, const uint16_t *__restrict__ pes, int T, int E, int K,
     int32_t *topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ rank,
-    int32_t *__restrict__ err, int32_t *__restrict__ arrive) {
+    int32_t *__restrict__ err, int32_t *__restrict__ arrive, PrepArgs pa) {
   __shared__ int s_last;
   const int t = blockIdx.x * (kBucketThreads / kWave) + (threadIdx.x >> 6);
   if (t < T) select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
@@ -157,6 +157,18 @@ __global__ __launch_bounds__(kBucketThreads) void k_select_bucket_last(
     s_last = last;
   }
   __syncthreads();
+  // the expert-input prep of this workgroup's tokens (moe_route_bucket_prep),
+  // after the arrival so that it never delays the bucketing workgroup's start
+  if (pa.x16) {
+    for (int i = blockIdx.x * kBucketThreads + threadIdx.x; i < pa.P; i += gridDim.x * kBucketThreads)
+      pa.a_max[i] = 0u;
+    if (t < T) {
+      if (pa.norm_w)
+        prep_row<true>(pa.x, pa.norm_w, pa.norm_eps, pa.H, t, pa.x16, pa.x_exp);
+      else
+        prep_row<false>(pa.x, nullptr, 0.0f, pa.H, t, pa.x16, pa.x_exp);
+    }
+  }
   if (!s_last) return;  // uniform
   bucket_small<kBucketThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
 }
@@ -239,11 +251,11 @@ __attribute__((visibility("hidden"))) int launch_select_bucket(
                          const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, hipStream_t s) {
+                         void *workspace, const PrepArgs &pa, hipStream_t s) {
   int32_t *err = (int32_t *)workspace;
   MOE_LAUNCH(k_select_bucket_last, dim3((T + kBucketWaves - 1) / kBucketWaves),
              dim3(kBucketThreads), 0, s, logits, pes, T, E, top_k, topk_idx, topk_w, topk_w_raw,
-             expert_offsets, sorted_pairs, pair_rank, err, err + 1);
+             expert_offsets, sorted_pairs, pair_rank, err, err + 1, pa);
   return MOE_OK;
 }
 }  // namespace moe

@@ -91,107 +91,18 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
 }
 
 // ---------------------------------------------------------------- prep ----
-// One wave per token: row maximum -> exponent -> f16 row scaled by
-// 2^(14 - exponent), row-major [T][H]; the other threads clear the per-row
-// maximum of A.  A lane keeps its (up to kPrepV) 16-byte pieces of the row in
-// registers between the two passes, so the row is read once.
-constexpr int kPrepV = 8;  // H <= 64 * 8 * kPrepV; longer rows take a second read
-
-// NORM: the expert input is the learned RMSNorm of x, y = x / sqrt(mean(x^2)
-// + eps) * norm_w, computed in fp32 from the kept row (sum of squares in a
-// fixed order) and rescaled to f16 like a plain row.
+// One wave per token (prep_row, shared with the decode selection kernel); the
+// other threads clear the per-row maximum of A.
 template <bool NORM>
 __global__ __launch_bounds__(kThreads) void k_prep(const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ norm_w, float eps,
                                                    int T, int H, int P, uint16_t *__restrict__ x16,
                                                    int32_t *__restrict__ x_exp,
                                                    uint32_t *__restrict__ a_max) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = blockIdx.x * kThreads + tid; i < P; i += gridDim.x * kThreads) a_max[i] = 0u;
   const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const uint16_t *row = x + (size_t)t * H;
-  u32x4 keep[kPrepV], gkeep[kPrepV];
-#pragma unroll
-  for (int v = 0; v < kPrepV; ++v) {
-    const int k = (v * kWave + lane) * 8;
-    keep[v] = k < H ? *(const u32x4 *)(row + k) : u32x4{0, 0, 0, 0};
-    if (NORM) gkeep[v] = k < H ? *(const u32x4 *)(norm_w + k) : u32x4{0, 0, 0, 0};
-  }
-  // 1 / rms of the row (NORM)
-  float inv = 1.0f;
-  if (NORM) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kPrepV; ++v)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(keep[v][i] << 16), hi = __uint_as_float(keep[v][i] & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-    for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {  // rows longer than kept
-      const u32x4 v = *(const u32x4 *)(row + k);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-    }
-    ss = wave_sum(ss);
-    inv = 1.0f / sqrtf(ss / (float)H + eps);
-  }
-  // the 8 expert-input values of a 16-byte piece (bf16 x, and norm_w when NORM)
-  auto values = [&](const u32x4 &xv, const u32x4 &gv, float (&y)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[2 * i] = __uint_as_float(xv[i] << 16);
-      y[2 * i + 1] = __uint_as_float(xv[i] & 0xFFFF0000u);
-      if (NORM) {
-        y[2 * i] = y[2 * i] * inv * __uint_as_float(gv[i] << 16);
-        y[2 * i + 1] = y[2 * i + 1] * inv * __uint_as_float(gv[i] & 0xFFFF0000u);
-      }
-    }
-  };
-  auto gload = [&](int k) { return NORM ? *(const u32x4 *)(norm_w + k) : u32x4{0, 0, 0, 0}; };
-  float amax = 0.0f;
-  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8) {
-    float y[8];
-    values(*(const u32x4 *)(row + k), gload(k), y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
-  }
-#pragma unroll
-  for (int v = 0; v < kPrepV; ++v) {
-    float y[8];
-    values(keep[v], gkeep[v], y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
-  }
-  amax = wave_max(amax);
-  const int ex = row_exponent(amax);
-  const float f = __builtin_ldexpf(1.0f, 14 - ex);
-  auto convert = [&](const u32x4 &xv, const u32x4 &gv) {
-    float y[8];
-    values(xv, gv, y);
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16 lo = (f16)(y[2 * i] * f);
-      const f16 hi = (f16)(y[2 * i + 1] * f);
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    return o;
-  };
-#pragma unroll
-  for (int v = 0; v < kPrepV; ++v) {
-    const int k = (v * kWave + lane) * 8;
-    if (k < H) *(u32x4 *)(x16 + (size_t)t * H + k) = convert(keep[v], gkeep[v]);
-  }
-  for (int k = (kPrepV * kWave + lane) * 8; k < H; k += kWave * 8)
-    *(u32x4 *)(x16 + (size_t)t * H + k) = convert(*(const u32x4 *)(row + k), gload(k));
-  if (lane == 0) x_exp[t] = ex;
+  if (t < T) prep_row<NORM>(x, norm_w, eps, H, t, x16, x_exp);
 }
 
 // gelu_tanh(g) = 0.5 g (1 + tanh(u)), u = sqrt(2/pi) (g + 0.044715 g^3), in the
@@ -1002,6 +913,19 @@ int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nv
 }
 
 }  // namespace
+
+namespace moe {
+int expert_prep_buffers(int T, int top_k, int E, int H, int I, void *workspace, size_t ws_bytes,
+                        uint16_t **x16, int32_t **x_exp, uint32_t **a_max) {
+  const int st = check_common(T, top_k, E, H, I, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  const Ws w = ws_ptrs(workspace, ws_layout(T, top_k, E, H, I));
+  *x16 = w.x16;
+  *x_exp = w.x_exp;
+  *a_max = w.a_max;
+  return MOE_OK;
+}
+}  // namespace moe
 
 extern "C" int nvfp4_expert_prep(const uint16_t *x_expert, int32_t T, int32_t top_k, int32_t E,
                                  int32_t H, int32_t I, void *workspace, size_t ws_bytes,

@@ -283,7 +283,7 @@ constexpr int kFusedMaxT = 64;
 int launch_select_bucket(const float *logits, const uint16_t *pes, int T, int E, int top_k,
                          int32_t *topk_idx, float *topk_w, float *topk_w_raw,
                          int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
-                         void *workspace, hipStream_t s);
+                         void *workspace, const PrepArgs &pa, hipStream_t s);
 }
 
 extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -318,15 +318,14 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
   return MOE_OK;
 }
 
-extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
-                                const uint16_t *router_scale, const uint16_t *per_expert_scale,
-                                const float *logit_bias, int32_t T, int32_t H, int32_t E,
-                                int32_t top_k, float eps, int32_t *topk_idx, float *topk_w,
-                                float *topk_w_raw, float *logits, int32_t *expert_offsets,
-                                int32_t *sorted_pairs, int32_t *pair_rank, void *workspace,
-                                size_t ws_bytes, void *stream) {
-  using namespace moe;
-  // the checks of moe_route and moe_bucket, before anything is queued
+namespace moe {
+namespace {
+// the checks of moe_route and moe_bucket, before anything is queued
+int route_bucket_checks(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+                        const uint16_t *per_expert_scale, int32_t T, int32_t H, int32_t E,
+                        int32_t top_k, int32_t *topk_idx, float *topk_w, float *logits,
+                        int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+                        void *workspace, size_t ws_bytes) {
   if (!w_router || !router_scale || !per_expert_scale || !expert_offsets || !workspace)
     return MOE_ERR_NULL;
   if (T > 0 && (!x || !topk_idx || !topk_w || !logits || !sorted_pairs || !pair_rank))
@@ -335,18 +334,22 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
   if (E > MOE_MAX_EXPERTS || E % 16 || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   if (ws_bytes < moe_bucket_workspace_bytes(T, top_k, E)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// true: the decode path, logits then one selection + bucketing launch
+bool fused_route(int T, int H, int top_k) {
   const int nv = (H + 511) / 512;
-  if (T > kFusedMaxT || nv > kFewMaxV || T * top_k > 4096) {
-    const int st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
-                             top_k, eps, topk_idx, topk_w, topk_w_raw, logits, stream);
-    if (st != MOE_OK) return st;
-    return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
-                      ws_bytes, stream);
-  }
-  if (T == 0)  // empty batch: the offsets are all zero, as moe_bucket writes them
-    return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
-                      ws_bytes, stream);
-  hipStream_t s = (hipStream_t)stream;
+  return T > 0 && T <= kFusedMaxT && nv <= kFewMaxV && T * top_k <= 4096;
+}
+
+int route_bucket_fused(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+                       const uint16_t *per_expert_scale, const float *logit_bias, int32_t T,
+                       int32_t H, int32_t E, int32_t top_k, float eps, int32_t *topk_idx,
+                       float *topk_w, float *topk_w_raw, float *logits, int32_t *expert_offsets,
+                       int32_t *sorted_pairs, int32_t *pair_rank, void *workspace,
+                       const PrepArgs &pa, hipStream_t s) {
+  const int nv = (H + 511) / 512;
   // the arrival counter of the selection kernel: word 1 of the workspace,
   // zeroed by the logits kernel of this call
   int32_t *arrive = (int32_t *)workspace + 1;
@@ -361,5 +364,71 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
 #undef MOE_FEW
   }
   return launch_select_bucket(logits, per_expert_scale, T, E, top_k, topk_idx, topk_w, topk_w_raw,
-                              expert_offsets, sorted_pairs, pair_rank, workspace, s);
+                              expert_offsets, sorted_pairs, pair_rank, workspace, pa, s);
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
+                                const uint16_t *router_scale, const uint16_t *per_expert_scale,
+                                const float *logit_bias, int32_t T, int32_t H, int32_t E,
+                                int32_t top_k, float eps, int32_t *topk_idx, float *topk_w,
+                                float *topk_w_raw, float *logits, int32_t *expert_offsets,
+                                int32_t *sorted_pairs, int32_t *pair_rank, void *workspace,
+                                size_t ws_bytes, void *stream) {
+  using namespace moe;
+  int st = route_bucket_checks(x, w_router, router_scale, per_expert_scale, T, H, E, top_k,
+                               topk_idx, topk_w, logits, expert_offsets, sorted_pairs, pair_rank,
+                               workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (!fused_route(T, H, top_k)) {
+    // T == 0 included: the offsets are all zero, as moe_bucket writes them
+    if (T > 0) {
+      st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k,
+                     eps, topk_idx, topk_w, topk_w_raw, logits, stream);
+      if (st != MOE_OK) return st;
+    }
+    return moe_bucket(topk_idx, T, top_k, E, expert_offsets, sorted_pairs, pair_rank, workspace,
+                      ws_bytes, stream);
+  }
+  return route_bucket_fused(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
+                            top_k, eps, topk_idx, topk_w, topk_w_raw, logits, expert_offsets,
+                            sorted_pairs, pair_rank, workspace, PrepArgs{}, (hipStream_t)stream);
+}
+
+extern "C" int moe_route_bucket_prep(
+    const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+    const uint16_t *per_expert_scale, const float *logit_bias, int32_t T, int32_t H, int32_t E,
+    int32_t top_k, float eps, int32_t *topk_idx, float *topk_w, float *topk_w_raw, float *logits,
+    int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank, void *bucket_ws,
+    size_t bucket_ws_bytes, const uint16_t *norm_weight, float norm_eps, int32_t I,
+    void *expert_ws, size_t expert_ws_bytes, void *stream) {
+  using namespace moe;
+  int st = route_bucket_checks(x, w_router, router_scale, per_expert_scale, T, H, E, top_k,
+                               topk_idx, topk_w, logits, expert_offsets, sorted_pairs, pair_rank,
+                               bucket_ws, bucket_ws_bytes);
+  if (st != MOE_OK) return st;
+  if (norm_weight && !(norm_eps >= 0.0f)) return MOE_ERR_SHAPE;
+  PrepArgs pa{};
+  st = expert_prep_buffers(T, top_k, E, H, I, expert_ws, expert_ws_bytes, &pa.x16, &pa.x_exp,
+                           &pa.a_max);
+  if (st != MOE_OK) return st;
+  if (!fused_route(T, H, top_k)) {
+    st = moe_route_bucket(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k,
+                          eps, topk_idx, topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs,
+                          pair_rank, bucket_ws, bucket_ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return norm_weight ? nvfp4_expert_prep_rmsnorm(x, norm_weight, norm_eps, T, top_k, E, H, I,
+                                                   expert_ws, expert_ws_bytes, stream)
+                       : nvfp4_expert_prep(x, T, top_k, E, H, I, expert_ws, expert_ws_bytes,
+                                           stream);
+  }
+  pa.x = x;
+  pa.norm_w = norm_weight;
+  pa.norm_eps = norm_eps;
+  pa.H = H;
+  pa.P = T * top_k;
+  return route_bucket_fused(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E,
+                            top_k, eps, topk_idx, topk_w, topk_w_raw, logits, expert_offsets,
+                            sorted_pairs, pair_rank, bucket_ws, pa, (hipStream_t)stream);
 }

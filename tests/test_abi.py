@@ -221,3 +221,28 @@ def test_weight_format_checks(L):
     assert L.moe_dequant_f16(R(_tensor(2, 16, 64, fmt=2, glob=None)), 0, NULL, NULL) == -1
     assert L.nvfp4_dequant_bf16(R(_tensor(2, 16, 64, fmt=1)), 0, FAKE, NULL) == -4
     assert L.nvfp4_repack(R(_tensor(2, 16, 64, layout=0, fmt=4)), FAKE, FAKE, NULL) == -4
+
+
+def test_route_bucket_prep_rejects(L):
+    T, k, E, H, I = 64, 8, 128, 2816, 704
+    wsb = L.moe_bucket_workspace_bytes(T, k, E)
+    wse = L.moe_workspace_bytes(T, k, E, H, I)
+    # (x, w, scale, pes, bias, T, H, E, k, eps, idx, w, w_raw, logits, off, sp, pr,
+    #  bucket_ws, bucket_ws_bytes, norm_w, norm_eps, I, expert_ws, expert_ws_bytes, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, NULL, T, H, E, k, 1e-6, FAKE, FAKE, NULL, FAKE, FAKE, FAKE,
+          FAKE, FAKE, wsb, NULL, 0.0, I, FAKE, wse, NULL]
+    a = list(ok); a[18] = wsb - 1
+    assert L.moe_route_bucket_prep(*a) == -3                 # bucket workspace
+    a = list(ok); a[23] = wse - 1
+    assert L.moe_route_bucket_prep(*a) == -3                 # expert workspace
+    a = list(ok); a[22] = NULL
+    assert L.moe_route_bucket_prep(*a) == -1
+    a = list(ok); a[19], a[20] = FAKE, -1.0
+    assert L.moe_route_bucket_prep(*a) == -2                 # norm eps < 0
+    a = list(ok); a[21] = I + 32
+    a[23] = L.moe_workspace_bytes(T, k, E, H, I + 32)
+    assert L.moe_route_bucket_prep(*a) == -4                 # I % 64
+    a = list(ok); a[0] = NULL
+    assert L.moe_route_bucket_prep(*a) == -1                 # x NULL with T > 0
+    a = list(ok); a[7] = 120
+    assert L.moe_route_bucket_prep(*a) == -4                 # E % 16

@@ -293,6 +293,51 @@ def test_route_bucket_matches_oracle_and_separate_calls(T, H, E, k):
         assert len(differ) <= max(1, T // 200)
 
 
+@pytest.mark.parametrize("T,H,E,k,I", [(0, 2816, 128, 8, 704), (1, 2816, 128, 8, 704),
+                                       (5, 2816, 128, 8, 704), (64, 2816, 128, 8, 704),
+                                       (65, 2816, 128, 8, 704), (300, 2816, 128, 8, 704),
+                                       (9, 192, 16, 3, 64), (64, 4096, 256, 16, 128),
+                                       (30, 4160, 32, 4, 64)])
+@pytest.mark.parametrize("norm", [False, True])
+def test_route_bucket_prep_equals_separate_calls(T, H, E, k, I, norm):
+    """moe_route_bucket_prep: every output byte, the whole expert workspace
+    included (filled with garbage first, so that the clearing of the row
+    maxima is checked), equal to moe_route_bucket followed by
+    nvfp4_expert_prep (or nvfp4_expert_prep_rmsnorm)."""
+    router = S.router_params(3, h=H, e=E)
+    x = S.activations(94, T, h=H)
+    x[:min(T, 2)] = S.f32_to_bf16_bits(S.bf16_bits_to_f32(x[:min(T, 2)]) * np.float32(3e4))
+    wr, sc, pes, bias = W.router_to_device(router)
+    xd = _bits(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    nw = _bits(S.norm_weights(2, h=H)[0]) if norm else None
+    wsb = moe.moe_bucket_workspace_bytes(T, k, E)
+    wse = moe.moe_workspace_bytes(T, k, E, H, I)
+
+    def outs():
+        return dict(idx=torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+                    w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                    w_raw=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                    lg=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+                    off=torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+                    sp=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+                    pr=torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+                    ws=torch.full((wsb,), 0x55, dtype=torch.uint8, device="cuda"),
+                    ews=torch.full((wse,), 0xA7, dtype=torch.uint8, device="cuda"))
+    a, b = outs(), outs()
+    moe.moe_route_bucket_prep(xd, wr, sc, pes, bias, k, 1e-6, a["idx"], a["w"], a["w_raw"],
+                              a["lg"], a["off"], a["sp"], a["pr"], a["ws"], nw, 1e-6, I, a["ews"])
+    moe.moe_route_bucket(xd, wr, sc, pes, bias, k, 1e-6, b["idx"], b["w"], b["w_raw"], b["lg"],
+                         b["off"], b["sp"], b["pr"], b["ws"])
+    if norm:
+        moe.nvfp4_expert_prep_rmsnorm(xd, nw, 1e-6, E, I, k, b["ews"])
+    else:
+        moe.nvfp4_expert_prep(xd, E, I, k, b["ews"])
+    torch.cuda.synchronize()
+    for n in ("idx", "w", "w_raw", "lg", "off", "sp", "pr", "ews"):
+        assert torch.equal(a[n].view(torch.uint8), b[n].view(torch.uint8)), n
+    assert int(a["ws"][:4].view(torch.int32)[0]) == 0
+
+
 # ---------------------------------------------------------------- experts
 def _expert_case(T, k, E, H, I, seed):
     c = S.small_case(seed, T, H, I, E, k)
