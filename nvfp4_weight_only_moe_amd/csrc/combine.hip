@@ -4,7 +4,7 @@
 // accumulation, one bf16 rounding.  Workgroup (t, c) covers token t's columns
 // 1024c .. 1024c + 1023; each thread owns 8 consecutive outputs (16-byte
 // loads and stores), so even a decode batch spreads over many workgroups.
-#include "common.h"
+#include "combine_row.h"
 
 namespace moe {
 namespace {
@@ -16,135 +16,23 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t *__r
                                                  const int32_t *__restrict__ rank, int T, int K,
                                                  int H, uint16_t *__restrict__ out) {
   const int t = blockIdx.x;
-  const int P = T * K;
-  // ranks and weights first, then every row load issued before any is used,
-  // so the loads of the K rows overlap instead of queueing one by one
-  int rk[MOE_MAX_TOPK];
-  float wk[MOE_MAX_TOPK];
-  uint32_t valid = 0;  // bit j: slot j has a rank inside [0, P)
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rk[j] = 0;
-    wk[j] = 0.0f;
-    if (j < K) {
-      const int rr = rank[(size_t)t * K + j];
-      if (rr >= 0 && rr < P) {
-        rk[j] = rr;
-        wk[j] = w[(size_t)t * K + j];
-        valid |= 1u << j;
-      }
-    }
-  }
+  // ranks and weights first, then every row load issued before any is used
+  const TokenPairs tp = token_pairs(w, rank, t, K, T * K);
   const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
-  if (c < H) {
-    u32x4 v[MOE_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if ((valid >> j) & 1u) v[j] = *(const u32x4 *)(y + (size_t)rk[j] * H + c);
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if ((valid >> j) & 1u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(wk[j], __uint_as_float(v[j][i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(wk[j], __uint_as_float(v[j][i] & 0xFFFF0000u), acc[2 * i + 1]);
-        }
-      }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = f32x2_to_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    *(u32x4 *)(out + (size_t)t * H + c) = o;
-  }
+  if (c < H) combine_chunk(y, tp, H, t, c, out);
 }
 
-// The combine followed by the learned RMSNorm of the summed row ("Gemma 4
-// 26B-A4B (MoE) - Core AI", Architecture sketch: post_feedforward_layernorm_2
-// of the weighted sum, then the residual add and layer_scalar):
-//   s = sum_j w[t][j] * Y[rank(t, j)]            (fp32, order j = 0, 1, ...)
-//   out[t] = (residual[t] + s / sqrt(mean(s^2) + eps) * norm_w) * layer_scalar
-// rounded once to bf16.  One workgroup per token (the norm needs the whole
-// row): thread i owns columns 8(i + 256 q), q < kNormPieces, kept in
+// The combine followed by the learned RMSNorm of the summed row: one
+// workgroup per token (the norm needs the whole row), the row kept in
 // registers between the sum of squares and the output.
-constexpr int kNormThreads = 256;
-constexpr int kNormPieces = 4;  // H <= 8 * 256 * 4 = 8192
-
 __global__ __launch_bounds__(kNormThreads) void k_combine_rmsnorm(
     const uint16_t *__restrict__ y, const float *__restrict__ w, const int32_t *__restrict__ rank,
     const uint16_t *__restrict__ norm_w, float eps, const uint16_t *residual, float layer_scalar,
     int T, int K, int H, uint16_t *out) {
   __shared__ float s_ss[kNormThreads / kWave];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int P = T * K;
-  int rk[MOE_MAX_TOPK];
-  float wk[MOE_MAX_TOPK];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rk[j] = 0;
-    wk[j] = 0.0f;
-    if (j < K) {
-      const int rr = rank[(size_t)t * K + j];
-      if (rr >= 0 && rr < P) {
-        rk[j] = rr;
-        wk[j] = w[(size_t)t * K + j];
-        valid |= 1u << j;
-      }
-    }
-  }
-  float acc[kNormPieces][8];
-  float ss = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kNormPieces; ++q) {
-    const int c = (q * kNormThreads + tid) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[q][i] = 0.0f;
-    if (c < H) {
-      u32x4 v[MOE_MAX_TOPK];
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j)
-        if ((valid >> j) & 1u) v[j] = *(const u32x4 *)(y + (size_t)rk[j] * H + c);
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        if ((valid >> j) & 1u) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[q][2 * i] = fmaf(wk[j], __uint_as_float(v[j][i] << 16), acc[q][2 * i]);
-            acc[q][2 * i + 1] = fmaf(wk[j], __uint_as_float(v[j][i] & 0xFFFF0000u), acc[q][2 * i + 1]);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(acc[q][i], acc[q][i], ss);
-    }
-  }
-  // sum of squares of the row: waves, then the 4 wave sums in order
-  ss = wave_sum(ss);
-  if ((tid & (kWave - 1)) == 0) s_ss[tid / kWave] = ss;
-  __syncthreads();
-  float tot = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kNormThreads / kWave; ++i) tot += s_ss[i];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-#pragma unroll
-  for (int q = 0; q < kNormPieces; ++q) {
-    const int c = (q * kNormThreads + tid) * 8;
-    if (c >= H) continue;
-    const u32x4 g = *(const u32x4 *)(norm_w + c);
-    u32x4 r = {0, 0, 0, 0};
-    if (residual) r = *(const u32x4 *)(residual + (size_t)t * H + c);
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = (__uint_as_float(r[i] << 16) + acc[q][2 * i] * inv * __uint_as_float(g[i] << 16)) * layer_scalar;
-      const float hi = (__uint_as_float(r[i] & 0xFFFF0000u) +
-                        acc[q][2 * i + 1] * inv * __uint_as_float(g[i] & 0xFFFF0000u)) * layer_scalar;
-      o[i] = f32x2_to_bf16x2(lo, hi);
-    }
-    *(u32x4 *)(out + (size_t)t * H + c) = o;
-  }
+  const int t = blockIdx.x;
+  const TokenPairs tp = token_pairs(w, rank, t, K, T * K);
+  combine_rmsnorm_row(y, tp, norm_w, eps, residual, layer_scalar, H, t, out, s_ss);
 }
 
 }  // namespace
