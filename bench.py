@@ -2,22 +2,21 @@
 """Throughput of the NVFP4 weight-only Gemma-4-26B-A4B MoE expert block on one
 MI355X.
 
-A step is one pass of the whole hot path -- routing and bucketing (one
-moe_route_bucket call), the expert MLP (prep, gate/up, down) and moe_combine --
-over one batch of seeded synthetic
-tokens, with inputs and weights already resident in HBM.  The default workload
-is one model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts,
-top-8, expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
+A step is one pass of the whole hot path -- routing, bucketing and the expert
+input's prep (one moe_route_bucket_prep call), the expert MLP's gate/up and
+down projections, and moe_combine -- over one batch of seeded synthetic tokens,
+with inputs and weights already resident in HBM.  The default workload is one
+model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts, top-8,
+expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
 
-Timing: W warm-up steps, then K steps captured in one HIP graph and replayed
-once, bracketed by synchronisations (ms_per_step is wall clock / K).  In the
-graph the activation prep of each step runs on a parallel branch beside the
-router and the bucketing (it does not depend on them).  The per-kernel
-durations used for the roofline of the dominant kernel (the gate/up GEMV/GEMM)
-come from a second graph of the same K steps in which every stage call is a
-child graph bracketed by timing-event nodes on the launch stream.  Consecutive
-steps read different, byte-identical copies of the expert weights so that each
-step streams its experts from HBM instead of the 256 MB last-level cache.
+Timing: W warm-up steps, then K steps captured in one HIP graph on one stream
+and replayed once, bracketed by synchronisations (ms_per_step is wall clock /
+K).  The dominant kernel (the gate/up GEMV/GEMM) is timed by HIP events around
+back-to-back launches of its stage call on the same stream; per-stage
+durations come from a second graph of the K steps in which every stage call is
+a child graph between timing-event nodes.  Consecutive steps read different,
+byte-identical copies of the expert weights so that each step streams its
+experts from HBM instead of the 256 MB last-level cache.
 
 Prints one JSON line (rank 0).
 """

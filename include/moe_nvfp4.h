@@ -253,8 +253,8 @@ size_t moe_workspace_bytes(int32_t T, int32_t top_k, int32_t E, int32_t H, int32
  * want to time or overlap them; queued in this order with the same workspace
  * they give the same bytes as nvfp4_expert_mlp.
  *   nvfp4_expert_prep:    per-token power-of-two rescale of x_expert to f16
- *                         (for few rows per expert stored transposed), and
- *                         clears the per-row max of A.  It does not read the
+ *                         ([T][H] in the workspace), and clears the per-row
+ *                         max of A.  It does not read the
  *                         routing, so it may run concurrently with moe_route
  *                         and moe_bucket (on another stream or graph branch),
  *                         as long as it completes before nvfp4_expert_gate_up.
