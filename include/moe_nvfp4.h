@@ -385,7 +385,7 @@ int moe_dequant_f16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *strea
 /* Text of a status code (static storage). */
 const char *moe_status_str(int status);
 
-/* ABI version of this header: (major << 16) | minor. */
+/* ABI version of this header: (major << 16) | minor (2.1: moe_route_bucket_prep). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus
