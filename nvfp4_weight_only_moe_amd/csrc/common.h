@@ -16,6 +16,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kWave = 64;
+constexpr int kXcds = 8;  // XCDs of the MI355X: workgroup b runs on XCD b % 8
 
 // ---- bf16 <-> f32 (bit patterns) -----------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -137,7 +137,6 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 // reuse a column block's weights then run side by side on one XCD and hit
 // its L2 instead of HBM.
 constexpr int kUnitK = 128;
-constexpr int kXcds = 8;
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts, then the
 // row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
