@@ -242,6 +242,58 @@ def test_graph_replay_matches_eager(layer0):
         assert torch.equal(buf.sorted_pairs, eager.sorted_pairs)
 
 
+def test_graph_replay_matches_eager_prefill(layer0_zipf):
+    """The prefill path in a graph (wide router, multi-kernel bucketing,
+    tiled GEMMs): every replay, with eager work between them, equals eager."""
+    x = W.to_device_bf16(S.activations(2, 2048))
+    eager = moe.MoeBuffers(2048, layer0_zipf.H, layer0_zipf.I, layer0_zipf.E, 8)
+    moe.forward(layer0_zipf, x, eager)
+    buf = moe.MoeBuffers(2048, layer0_zipf.H, layer0_zipf.I, layer0_zipf.E, 8)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(layer0_zipf, x, buf)     # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(layer0_zipf, x, buf)
+    for _ in range(3):
+        buf.out.zero_()
+        buf.expert_offsets.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.out, eager.out)
+        assert torch.equal(buf.expert_offsets, eager.expert_offsets)
+        assert torch.equal(buf.sorted_pairs, eager.sorted_pairs)
+
+
+@pytest.mark.parametrize("T", [5, 300])
+def test_separate_expert_input(T):
+    """forward with an expert input other than the router's x (moe_route_bucket
+    + nvfp4_expert_mlp + moe_combine): the experts read x_expert, the router x."""
+    T, k, E, H, I = T, 4, 16, 192, 128
+    c = S.small_case(40 + T, T, H, I, E, k)
+    xe_bits = S.small_case(41 + T, T, H, I, E, k)["x"]
+    layer = W.build_small_layer(c, k)
+    buf = moe.MoeBuffers(T, H, I, E, k)
+    moe.forward(layer, W.to_device_bf16(c["x"]), buf, x_expert=W.to_device_bf16(xe_bits))
+    torch.cuda.synchronize()
+    r = router_f64(c["router"])
+    xs, xe = F.bf16_bits_to_f64(c["x"]), F.bf16_bits_to_f64(xe_bits)
+    ref_r = M.route(xs, r["w_router"], r["scale"], r["per_expert_scale"], k, r["bias"])
+    gidx = buf.topk_idx.cpu().numpy()
+    check_route(gidx, buf.topk_w.cpu().numpy(), buf.topk_w_raw.cpu().numpy(), ref_r,
+                r["per_expert_scale"])
+    q = {n: quantize_experts(F.bf16_bits_to_f64(c[n])) for n in ("gate", "up", "down")}
+    fns = {n: M.nvfp4_weights(*q[n]) for n in q}
+    ref = M.moe_block(xs, xe, r, fns["gate"], fns["up"], fns["down"], k=k, ids=gidx)["out"]
+    got = buf.out.float().cpu().numpy()
+    assert rel_frob(got, ref) <= REL_FROB_TOL
+    # and not what the router's x would have given
+    wrong = M.moe_block(xs, xs, r, fns["gate"], fns["up"], fns["down"], k=k, ids=gidx)["out"]
+    assert rel_frob(got, wrong) > 0.5
+
+
 @pytest.mark.parametrize("T,k,E,H,I,zipf", [(1, 2, 16, 128, 64, False), (3, 2, 16, 128, 64, False),
                                             (5, 4, 32, 192, 128, True), (50, 8, 16, 256, 64, True)])
 def test_small_block_odd_shapes(T, k, E, H, I, zipf):
