@@ -43,8 +43,8 @@ SEPARATE_STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
                     help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
                          "3: 30-layer decode sweep")

@@ -146,31 +146,40 @@ __global__ __launch_bounds__(kBucketThreads) void k_select_bucket_last(
     int32_t *topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ rank,
     int32_t *__restrict__ err, int32_t *__restrict__ arrive, PrepArgs pa) {
-  __shared__ int s_last;
-  const int t = blockIdx.x * (kBucketThreads / kWave) + (threadIdx.x >> 6);
+  __shared__ int s_arr;
+  constexpr int kTPB = kBucketThreads / kWave;  // tokens per workgroup (a wave each)
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kTPB + wave;
   if (t < T) select_token(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
   __syncthreads();  // every wave's stores have left for L2
   if (threadIdx.x == 0) {
     __threadfence();  // release: this workgroup's selections, visible device-wide
-    const bool last = atomicAdd(arrive, 1) == (int)gridDim.x - 1;
-    if (last) __threadfence();  // acquire: every workgroup's selections
-    s_last = last;
+    const int arr = atomicAdd(arrive, 1);
+    if (arr == (int)gridDim.x - 1) __threadfence();  // acquire: every workgroup's selections
+    s_arr = arr;
   }
   __syncthreads();
-  // the expert-input prep of this workgroup's tokens (moe_route_bucket_prep),
-  // after the arrival so that it never delays the bucketing workgroup's start
+  const int arr = s_arr, G = (int)gridDim.x;
+  const bool last = arr == G - 1;  // uniform
+  if (last) bucket_small<kBucketThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
+  // the expert-input prep (moe_route_bucket_prep) by arrival order: the
+  // workgroup that arrived a-th preps token block a, except that the last one
+  // (busy bucketing, on the critical path) leaves its block to the first one;
+  // a single workgroup does both, bucketing first
   if (pa.x16) {
-    for (int i = blockIdx.x * kBucketThreads + threadIdx.x; i < pa.P; i += gridDim.x * kBucketThreads)
+    for (int i = blockIdx.x * kBucketThreads + threadIdx.x; i < pa.P; i += G * kBucketThreads)
       pa.a_max[i] = 0u;
-    if (t < T) {
+    auto prep_block = [&](int blk) {
+      const int tp = blk * kTPB + wave;
+      if (tp >= T) return;
       if (pa.norm_w)
-        prep_row<true>(pa.x, pa.norm_w, pa.norm_eps, pa.H, t, pa.x16, pa.x_exp);
+        prep_row<true>(pa.x, pa.norm_w, pa.norm_eps, pa.H, tp, pa.x16, pa.x_exp);
       else
-        prep_row<false>(pa.x, nullptr, 0.0f, pa.H, t, pa.x16, pa.x_exp);
-    }
+        prep_row<false>(pa.x, nullptr, 0.0f, pa.H, tp, pa.x16, pa.x_exp);
+    };
+    if (!last || G == 1) prep_block(arr);
+    if (arr == 0 && G > 1) prep_block(G - 1);
   }
-  if (!s_last) return;  // uniform
-  bucket_small<kBucketThreads>(topk_idx, T * K, E, offsets, sorted, rank, err);
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket_hist(const int32_t *__restrict__ idx,
