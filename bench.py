@@ -43,8 +43,10 @@ SEPARATE_STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; 10 for the 30-layer sweep)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 20; 3 for the 30-layer sweep)")
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
                     help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
                          "3: 30-layer decode sweep")
@@ -68,7 +70,12 @@ def parse():
                          "and joined per layer) instead of first on the one stream")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter scaling reference)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10 if args.workload == 3 else 200
+    if args.warmup is None:
+        args.warmup = 3 if args.workload == 3 else 20
+    return args
 
 
 class HipRuntime:
