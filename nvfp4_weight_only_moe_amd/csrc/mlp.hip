@@ -124,19 +124,25 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 // staged once in LDS as f16 (double-buffered) and shared by the 4 waves; each
 // lane loads its 16 bytes of every weight row tile it owns (one contiguous
 // kilobyte per wave in the tiled layout), dequantises them in registers and
-// runs MSUB x NW x 4 MFMAs 16x16x32, so one LDS fragment feeds NW MFMAs and
-// one dequantised weight fragment feeds MSUB.  The weights of unit u+1 are
-// in flight while unit u is multiplied; the activations of unit u+2 while
-// unit u+1 is staged.  16-row blocks past the end of a partial block skip
-// their MFMAs (a workgroup-uniform branch).
+// runs Q x NW x 4 MFMAs 16x16x32, so one LDS fragment feeds NW MFMAs and
+// one dequantised weight fragment feeds Q.  Q is the number of 16-row groups
+// of the block that hold rows (a partial block at the end of an expert's
+// bucket has fewer): the kernel picks the instantiation per workgroup, so
+// empty groups are neither staged nor multiplied.  Waves whose columns lie
+// past N stage activations for the others but issue no MFMAs.  The weights
+// of unit u+1 are in flight while unit u is multiplied; the activations of
+// unit u+2 while unit u+1 is staged.
 //
 // Order of the workgroups: a 1-D grid, a multiple of the 8 XCDs.  Hardware
 // hands workgroup b to XCD b % 8; b is mapped to the logical index
 // (b % 8) * (grid / 8) + b / 8 so that each XCD walks one contiguous range of
-// the logical order (expert, column block, row block).  The row blocks that
-// reuse a column block's weights then run side by side on one XCD and hit
-// its L2 instead of HBM.
+// the logical order: expert, then groups of kRowGroup row blocks, and in a
+// group column block, then row block.  The row blocks that reuse a column
+// block's weights run side by side on one XCD and hit its L2 instead of HBM,
+// and so do the column blocks that reuse a group's activations.
 constexpr int kUnitK = 128;
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts, then the
 // row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
@@ -153,8 +159,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
-// Logical block `L` of the order (expert e, column block cb, row block m):
-// expert e holds ceil(M_e / bm) * ncb consecutive blocks.  Lane l takes
+// Row blocks per group of the block order (below).
+constexpr int kRowGroup = 8;
+
+// Logical block `L` of the block order: expert e holds ceil(M_e / bm) * ncb
+// consecutive blocks (row block m0 / bm, column block cb).  Lane l takes
 // experts PER*l .. PER*l + PER - 1; one DPP prefix sum over the lanes
 // (scalar results).  False past the last block.
 __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int ncb, int L,
@@ -190,8 +199,13 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
   e = __builtin_amdgcn_readlane(ee, src);
   rem = __builtin_amdgcn_readlane(rem, src);
   nb = __builtin_amdgcn_readlane(nb, src);
-  cb = rem / nb;  // scalar
-  m0 = (rem - cb * nb) * bm;
+  // expert e's blocks in groups of kRowGroup row blocks (the last group may
+  // be smaller), each group column-block major: gsz row blocks x ncb columns
+  const int gi = rem / (kRowGroup * ncb);  // scalar
+  const int gsz = min(kRowGroup, nb - gi * kRowGroup);
+  const int r2 = rem - gi * kRowGroup * ncb;
+  cb = r2 / gsz;
+  m0 = (gi * kRowGroup + r2 - cb * gsz) * bm;
   return true;
 }
 
@@ -209,41 +223,43 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
 // Register budget of the K loop: weight register sets of the LDS-direct
 // (gate/up) pipeline (3: weights two units ahead; 2: one unit ahead) and
 // activation fragment sets (2: the next step's fragments are read from LDS
-// while this step multiplies; 1: read just before use).
+// while this step multiplies; 1: read just before use).  LDS activation
+// buffers of that pipeline: kGemmLdsBufs - 1 units in flight.
 constexpr int kGemmWeightSets = 3;
+constexpr int kGemmLdsBufs = 3;
+
 constexpr int kGemmAFragSets = 2;
 // dequantise the next K step's weights while this step's MFMAs run
 constexpr bool kGemmPipeDequant = true;
 
+// LDS activation buffers of the tiled-mode kernels
+template <bool GATED>
+constexpr int gemm_lds_bufs() { return GATED ? kGemmLdsBufs : 2; }
+
+// One block of the tiled mode: rows row0 .. row0 + mrows - 1 (mrows <= 16 Q)
+// of expert e, column block cb.  Q: the 16-row groups holding rows; only
+// those are staged, multiplied and stored.  s_a: the LDS activation buffers
+// [gemm_lds_bufs][16 MSUB * kUnitK]; s_rowscale: [16 MSUB].
 // DIRECT: the activations are f16 in memory (gate/up): buffer loads write
 // them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
 // through registers and are converted to f16 with the row's power of two.
-template <int MSUB, int NP, bool GATED, int FMT>
+template <int MSUB, int Q, int NP, bool GATED, int FMT>
 __device__ __forceinline__ void gemm_run(
     const uint16_t *__restrict__ a_src, const int32_t *__restrict__ x_exp,
-    uint32_t *__restrict__ a_max, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ sorted_pairs, int top_k, int E, int ncb, uint32_t a_bytes,
-    const Nvfp4 &w0, const Nvfp4 &w1, int K, int N, uint16_t *__restrict__ out) {
+    uint32_t *__restrict__ a_max, const int32_t *__restrict__ sorted_pairs, int top_k,
+    uint32_t a_bytes, const Nvfp4 &w0, const Nvfp4 &w1, int K, int N, uint16_t *__restrict__ out,
+    int e, int row0, int mrows, int cb, uint16_t (*s_a)[kBM * MSUB * kUnitK], float *s_rowscale) {
   constexpr bool DIRECT = GATED;
   constexpr int BM = kBM * MSUB;
   constexpr int NW = GATED ? 2 * NP : NP;  // weight row tiles streamed by a wave
   using WF = WeightFmt<FMT>;
   constexpr int SB = WF::kScaleBytes;       // scale bytes per lane and K unit
-  constexpr int NBUF = DIRECT ? 3 : 2;  // LDS activation buffers
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[NBUF][BM * kUnitK];
-  __shared__ float s_rowscale[BM];
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  int e, m0, cb;
-  if (!find_block(offsets, E, BM, ncb, L, e, m0, cb)) return;  // uniform over the workgroup
-  const int row0 = offsets[e] + m0;
-  const int mrows = min(BM, offsets[e + 1] - row0);
-  const int nq = (mrows + kBM - 1) / kBM;  // 16-row blocks holding rows
+  constexpr int NBUF = gemm_lds_bufs<GATED>();  // LDS activation buffers
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (K + kUnitK - 1) / kUnitK;
   const int nt0 = (cb * 4 + wave) * NP;          // first output row tile of this wave
-  const bool wave_on = nt0 * 16 < N;             // waves past the last column stage only
+  const bool wave_on = nt0 * 16 < N;  // waves past the last column stage only (no MFMAs)
 
   // ---- staging map.  DIRECT: load q of wave w fills rows 16q + 4w + lane/16,
   // LDS chunk positions lane%16 (one contiguous kilobyte per load); the lane
@@ -252,10 +268,10 @@ __device__ __forceinline__ void gemm_run(
   // K, read hardware zeros (offset out of range).
   const int st_row = DIRECT ? 4 * wave + (lane >> 4) : (tid >> 4);  // row within each 16
   const int st_c = DIRECT ? ((lane & 15) ^ st_row) : (tid & 15);      // K chunk of this lane
-  uint32_t st_off[MSUB];
-  float st_scale[MSUB];
+  uint32_t st_off[Q];
+  float st_scale[Q];
 #pragma unroll
-  for (int q = 0; q < MSUB; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int m = q * kBM + st_row;
     const bool ok = m < mrows;
     const int prow = ok ? row0 + m : row0;
@@ -282,19 +298,19 @@ __device__ __forceinline__ void gemm_run(
   // DIRECT staging of unit u into buffer b
   auto load_a_lds = [&](int u, int b) {
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q)
+    for (int q = 0; q < Q; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void *)&s_a[b][(q * kBM + 4 * wave) * kUnitK], 16,
           a_offset(u, q), 0, 0, 0);
   };
   // register staging
-  auto load_a = [&](int u, u32x4 (&v)[MSUB]) {
+  auto load_a = [&](int u, u32x4 (&v)[Q]) {
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q) v[q] = bload16(ra, a_offset(u, q));
+    for (int q = 0; q < Q; ++q) v[q] = bload16(ra, a_offset(u, q));
   };
-  auto store_a = [&](int b, const u32x4 (&v)[MSUB]) {
+  auto store_a = [&](int b, const u32x4 (&v)[Q]) {
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q) {
+    for (int q = 0; q < Q; ++q) {
       u32x4 o = v[q];
       if (!GATED) {  // bf16 -> f16 with the row's power of two (exact)
         const float f = st_scale[q];
@@ -332,9 +348,9 @@ __device__ __forceinline__ void gemm_run(
     }
   };
 
-  f32x4 acc[MSUB][NW];
+  f32x4 acc[Q][NW];
 #pragma unroll
-  for (int q = 0; q < MSUB; ++q)
+  for (int q = 0; q < Q; ++q)
 #pragma unroll
     for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
 
@@ -349,40 +365,40 @@ __device__ __forceinline__ void gemm_run(
     if (kGemmPipeDequant) {
       // the weights of step j + 1 are dequantised while the MFMAs of step j
       // run (two register sets), one MFMA between every two VALU ops
-      f16x8 a[MSUB], b[2][NW];
+      f16x8 a[Q], b[2][NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) b[0][i] = WF::dequant(wv[i][0], bs[i], 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int q = 0; q < MSUB; ++q)
+        for (int q = 0; q < Q; ++q)
           a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
         if (j < 3) {
 #pragma unroll
           for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = WF::dequant(wv[i][j + 1], bs[i], j + 1);
         }
 #pragma unroll
-        for (int q = 0; q < MSUB; ++q)
+        for (int q = 0; q < Q; ++q)
 #pragma unroll
           for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[q], b[j & 1][i], acc[q][i]);
-        __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
         if (j < 3) {
 #pragma unroll
-          for (int m = 0; m < MSUB * NW; ++m) {
+          for (int m = 0; m < Q * NW; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (8 * NW) / (MSUB * NW), 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (8 * NW) / (Q * NW), 0);
           }
         } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, MSUB * NW, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, Q * NW, 0);
         }
       }
       return;
     }
     constexpr int NA = kGemmAFragSets;
-    f16x8 a[NA][MSUB];
-    auto read_a = [&](int j, f16x8 (&dst)[MSUB]) {
+    f16x8 a[NA][Q];
+    auto read_a = [&](int j, f16x8 (&dst)[Q]) {
 #pragma unroll
-      for (int q = 0; q < MSUB; ++q)
+      for (int q = 0; q < Q; ++q)
         dst[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
     };
     if (NA == 2) read_a(0, a[0]);
@@ -394,13 +410,13 @@ __device__ __forceinline__ void gemm_run(
 #pragma unroll
       for (int i = 0; i < NW; ++i) b[i] = WF::dequant(wv[i][j], bs[i], j);
 #pragma unroll
-      for (int q = 0; q < MSUB; ++q)
+      for (int q = 0; q < Q; ++q)
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[j % NA][q], b[i], acc[q][i]);
       // order: LDS reads (of the next step with two fragment sets), dequantisation, MFMAs
-      if (NA == 1 || j < 3) __builtin_amdgcn_sched_group_barrier(0x100, MSUB, 0);
+      if (NA == 1 || j < 3) __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 8 * NW, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MSUB * NW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, Q * NW, 0);
     }
   };
 
@@ -415,26 +431,33 @@ __device__ __forceinline__ void gemm_run(
   u32x4 wv[WS][NW];
   uint32_t sv[WS][NW];
   if (DIRECT) {
-    // weights WS - 1 units ahead (WS register sets); the loop is unrolled
-    // by a multiple of the 3 LDS buffers and of WS, and the steps past the
-    // last unit skip their MFMAs (a uniform branch)
-    constexpr int UNR = WS == 3 ? 3 : 6;
-    constexpr int AHEAD = MSUB + 2 * NW * (WS - 1);  // loads issued after a unit's activations
-    load_a_lds(0, 0);
-    load_a_lds(1, 1);
+    // activations NBUF - 1 units ahead (a ring of NBUF LDS buffers), weights
+    // WS - 1 units ahead (WS register sets); the loop is unrolled by a
+    // multiple of NBUF and of WS, and the steps past the last unit skip
+    // their MFMAs (a uniform branch).  Every iteration issues Q
+    // activation loads, then 2 NW weight and scale loads, all unconditional
+    // (past the end they read zeros), so the vector-memory counter waits
+    // below are exact: after the activations of a unit come the NBUF - 2
+    // later units' activation loads and, before it is needed, at least
+    // min(NBUF - 1, WS) groups of weight loads.
+    constexpr int UNR = NBUF * WS / gcd_c(NBUF, WS);
+    constexpr int PRE = (NBUF - 2) * Q + (WS - 1) * 2 * NW;  // after unit 0's activations
+    constexpr int AHEAD = (NBUF - 2) * Q + (NBUF - 1 < WS ? NBUF - 1 : WS) * 2 * NW;
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load_a_lds(i, i);
 #pragma unroll
     for (int i = 0; i < WS - 1; ++i) load_w(i, wv[i], sv[i]);
-    MOE_WAIT_VMCNT(AHEAD);  // unit 0 of the activations has landed
+    MOE_WAIT_VMCNT(PRE);  // unit 0 of the activations has landed
     __syncthreads();
     const int nuu = (nunits + UNR - 1) / UNR * UNR;
     for (int u0 = 0; u0 < nuu; u0 += UNR) {
 #pragma unroll
       for (int d = 0; d < UNR; ++d) {
-        const int u = u0 + d;  // LDS ring buffer of unit u: u % 3 = d % 3
-        load_a_lds(u + 2, (d + 2) % 3);
+        const int u = u0 + d;  // LDS ring buffer of unit u: u % NBUF = d % NBUF
+        load_a_lds(u + NBUF - 1, (d + NBUF - 1) % NBUF);
         load_w(u + WS - 1, wv[(d + WS - 1) % WS], sv[(d + WS - 1) % WS]);
         __builtin_amdgcn_sched_barrier(0);
-        if (u < nunits) compute(s_a[d % 3], wv[d % WS], sv[d % WS]);
+        if (u < nunits && wave_on) compute(s_a[d % NBUF], wv[d % WS], sv[d % WS]);
         __builtin_amdgcn_sched_barrier(0);
         MOE_WAIT_VMCNT(AHEAD);  // unit u+1 of the activations has landed
         __syncthreads();
@@ -442,7 +465,7 @@ __device__ __forceinline__ void gemm_run(
     }
   } else {
     const int nu = (nunits + 1) & ~1;
-    u32x4 av[2][MSUB];
+    u32x4 av[2][Q];
     load_a(0, av[0]);
     load_w(0, wv[0], sv[0]);
     load_a(1, av[1]);
@@ -455,7 +478,7 @@ __device__ __forceinline__ void gemm_run(
         const int u = u0 + d;
         load_w(u + 1, wv[d ^ 1], sv[d ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(s_a[d], wv[d], sv[d]);
+        if (wave_on) compute(s_a[d], wv[d], sv[d]);
         __builtin_amdgcn_sched_barrier(0);
         store_a(d ^ 1, av[d ^ 1]);
         load_a(u + 3, av[d ^ 1]);
@@ -470,8 +493,7 @@ __device__ __forceinline__ void gemm_run(
     const float gg = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
     const float gu = FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q) {
-      if (q >= nq) break;
+    for (int q = 0; q < Q; ++q) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int m = q * kBM + 4 * g + jj;
@@ -492,8 +514,7 @@ __device__ __forceinline__ void gemm_run(
   } else {
     const float gd = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
 #pragma unroll
-    for (int q = 0; q < MSUB; ++q) {
-      if (q >= nq) break;
+    for (int q = 0; q < Q; ++q) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int m = q * kBM + 4 * g + jj;
@@ -519,8 +540,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int E, int ncb, uint32_t a_bytes,
     Nvfp4 w0, Nvfp4 w1,                  // GATED: gate, up; else w0 = down
     int K, int N, uint16_t *__restrict__ out) {
-  gemm_run<MSUB, NP, GATED, FMT>(a_src, x_exp, a_max, offsets, sorted_pairs, top_k, E, ncb, a_bytes, w0,
-                            w1, K, N, out);
+  static_assert(MSUB == 4, "one instantiation per 16-row group count below");
+  constexpr int BM = kBM * MSUB;
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[gemm_lds_bufs<GATED>()][BM * kUnitK];
+  __shared__ float s_rowscale[BM];
+  const int per_xcd = gridDim.x / kXcds;
+  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  int e, m0, cb;
+  if (!find_block(offsets, E, BM, ncb, L, e, m0, cb)) return;  // uniform over the workgroup
+  const int row0 = offsets[e] + m0;
+  const int mrows = min(BM, offsets[e + 1] - row0);  // >= 1: a block holds rows
+#define MOE_GEMM_RUN(Q)                                                                          \
+  gemm_run<MSUB, Q, NP, GATED, FMT>(a_src, x_exp, a_max, sorted_pairs, top_k, a_bytes, w0, w1, K, \
+                                    N, out, e, row0, mrows, cb, s_a, s_rowscale)
+  // the 16-row groups holding rows (uniform)
+  if (mrows > 3 * kBM) MOE_GEMM_RUN(4);
+  else if (mrows > 2 * kBM) MOE_GEMM_RUN(3);
+  else if (mrows > kBM) MOE_GEMM_RUN(2);
+  else MOE_GEMM_RUN(1);
+#undef MOE_GEMM_RUN
 }
 
 // ------------------------------------------------------- GEMV mode ----
