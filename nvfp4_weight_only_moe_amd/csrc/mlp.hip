@@ -593,7 +593,9 @@ constexpr int kDownNP = 2;       // down row tiles per wave (8-row tiles)
 constexpr int kDownNPMany = 4;   // ... when there are many tiles (P >= 3E)
 constexpr int kDownNPWide = 4;   // ... with 16-row tiles
 // down takes the K split when the unsplit grid would have fewer workgroups
-constexpr int kGemvSplitBelow = 1024;
+// (T = 1: 198 workgroups unsplit, the split slightly faster; T = 4: 792, the
+// unsplit grid faster)
+constexpr int kGemvSplitBelow = 512;
 
 template <int NL, int NW>
 struct GemvUnit {
