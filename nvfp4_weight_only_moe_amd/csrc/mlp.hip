@@ -167,7 +167,7 @@ constexpr int kRowGroup = 8;
 // experts PER*l .. PER*l + PER - 1; one DPP prefix sum over the lanes
 // (scalar results).  False past the last block.
 __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int ncb, int L,
-                           int &e, int &m0, int &cb) {
+                           int grp, int &e, int &m0, int &cb) {
   constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4u);
@@ -199,13 +199,13 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
   e = __builtin_amdgcn_readlane(ee, src);
   rem = __builtin_amdgcn_readlane(rem, src);
   nb = __builtin_amdgcn_readlane(nb, src);
-  // expert e's blocks in groups of kRowGroup row blocks (the last group may
-  // be smaller), each group column-block major: gsz row blocks x ncb columns
-  const int gi = rem / (kRowGroup * ncb);  // scalar
-  const int gsz = min(kRowGroup, nb - gi * kRowGroup);
-  const int r2 = rem - gi * kRowGroup * ncb;
+  // expert e's blocks in groups of grp row blocks (the last group may be
+  // smaller), each group column-block major: gsz row blocks x ncb columns
+  const int gi = rem / (grp * ncb);  // scalar
+  const int gsz = min(grp, nb - gi * grp);
+  const int r2 = rem - gi * grp * ncb;
   cb = r2 / gsz;
-  m0 = (gi * kRowGroup + r2 - cb * gsz) * bm;
+  m0 = (gi * grp + r2 - cb * gsz) * bm;
   return true;
 }
 
@@ -259,7 +259,7 @@ __device__ __forceinline__ void gemm_run(
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (K + kUnitK - 1) / kUnitK;
   const int nt0 = (cb * 4 + wave) * NP;          // first output row tile of this wave
-  const bool wave_on = nt0 * 16 < N;  // waves past the last column stage only (no MFMAs)
+  const bool wave_on = nt0 * 16 < N;  // waves past the last column stage only (gate/up: no MFMAs)
 
   // ---- staging map.  DIRECT: load q of wave w fills rows 16q + 4w + lane/16,
   // LDS chunk positions lane%16 (one contiguous kilobyte per load); the lane
@@ -478,7 +478,7 @@ __device__ __forceinline__ void gemm_run(
         const int u = u0 + d;
         load_w(u + 1, wv[d ^ 1], sv[d ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (wave_on) compute(s_a[d], wv[d], sv[d]);
+        compute(s_a[d], wv[d], sv[d]);  // no branch: it would split the pipelined loop
         __builtin_amdgcn_sched_barrier(0);
         store_a(d ^ 1, av[d ^ 1]);
         load_a(u + 3, av[d ^ 1]);
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int per_xcd = gridDim.x / kXcds;
   const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   int e, m0, cb;
-  if (!find_block(offsets, E, BM, ncb, L, e, m0, cb)) return;  // uniform over the workgroup
+  if (!find_block(offsets, E, BM, ncb, L, kRowGroup, e, m0, cb)) return;  // uniform over the workgroup
   const int row0 = offsets[e] + m0;
   const int mrows = min(BM, offsets[e + 1] - row0);  // >= 1: a block holds rows
 #define MOE_GEMM_RUN(Q)                                                                          \
