@@ -151,27 +151,33 @@ __global__ __launch_bounds__(256) void k_route_logits_few(
     logits[(size_t)t * E + e] = d * (1.0f / sqrtf(q2 / (float)H + eps) * hs) + b;
 }
 
-// ---- many tokens: 64 tokens x 32 experts per workgroup (16 x 32 per wave),
-// so that even 2048 tokens give 128 workgroups.  K in chunks of 128 staged in
-// LDS by coalesced row loads (16 threads per row); the next chunk is loaded
-// into registers while the current one is multiplied.  The split is taken on
-// the activation side when staging: x*scale = hi + lo (both bf16, exact).
+// ---- many tokens: 64 tokens x EXP experts per workgroup (16 x EXP per wave;
+// EXP = 16 or 32, the smaller tile doubling the workgroups of mid-sized
+// batches at the cost of staging each token chunk twice as often).  K in
+// chunks of 128 staged in LDS by coalesced row loads (16 threads per row); the
+// next chunk is loaded into registers while the current one is multiplied.
+// The split is taken on the activation side when staging: x*scale = hi + lo
+// (both bf16, exact).
 constexpr int kWideKC = 128;
 constexpr int kWideTok = 64;
-constexpr int kWideExp = 32;
 constexpr int kWideLd = kWideKC + 8;  // bf16 per LDS row (padding spreads banks)
+// below this many tokens the 16-expert tile (T = 128: step 130 -> 127 us,
+// T = 512: 232 -> 228 us; T = 2048 unchanged, T = 16384 slower)
+constexpr int kWideExp16Below = 2048;
 
+template <int EXP>
 __global__ __launch_bounds__(256) void k_route_logits_wide(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
     float eps, float *__restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t s_xh[kWideTok * kWideLd];
   __shared__ __attribute__((aligned(16))) uint16_t s_xl[kWideTok * kWideLd];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[kWideExp * kWideLd];
+  constexpr int NF = EXP / 16;  // 16-expert MFMA column tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[EXP * kWideLd];
   __shared__ float s_ss[kWideTok];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * kWideExp;
+  const int e0 = blockIdx.x * EXP;
   const int t0 = blockIdx.y * kWideTok;
   // staging map: 16 threads per row, rows srow + 16h
   const int srow = tid >> 4, scol = (tid & 15) * 8;
@@ -183,15 +189,15 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
     xok[h] = t < T;
     xrow[h] = x + (size_t)(xok[h] ? t : 0) * H;
   }
-  const uint16_t *wrow[2];
-  bool wok[2];
+  const uint16_t *wrow[NF];
+  bool wok[NF];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NF; ++h) {
     const int ee = e0 + srow + 16 * h;
     wok[h] = ee < E;
     wrow[h] = w + (size_t)(wok[h] ? ee : 0) * H;
   }
-  u32x4 xv[4], wv[2], sv;
+  u32x4 xv[4], wv[NF], sv;
   auto load = [&](int kc) {
     const bool kok = kc + scol < H;  // chunks past the end (H % 128 = 64, or the last prefetch) read zeros
     const u32x4 s0 = *(const u32x4 *)(scale + (kok ? kc + scol : 0));
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
       xv[h] = (xok[h] && kok) ? v : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NF; ++h) {
       const u32x4 v = *(const u32x4 *)(wrow[h] + (kok ? kc + scol : 0));
       wv[h] = (wok[h] && kok) ? v : u32x4{0, 0, 0, 0};
     }
@@ -218,9 +224,11 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
       *(bf16x8 *)(s_xl + (srow + 16 * h) * kWideLd + scol) = lo;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) *(u32x4 *)(s_w + (srow + 16 * h) * kWideLd + scol) = wv[h];
+    for (int h = 0; h < NF; ++h) *(u32x4 *)(s_w + (srow + 16 * h) * kWideLd + scol) = wv[h];
   };
-  f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0, 0, 0, 0};
   load(0);
   for (int kc = 0; kc < H; kc += kWideKC) {
     store();
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
       const bf16x8 ah = *(const bf16x8 *)(s_xh + (wave * 16 + r) * kWideLd + k);
       const bf16x8 al = *(const bf16x8 *)(s_xl + (wave * 16 + r) * kWideLd + k);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < NF; ++f) {
         const bf16x8 b = *(const bf16x8 *)(s_w + (f * 16 + r) * kWideLd + k);
         acc[f] = mfma_bf16(ah, b, acc[f]);
         acc[f] = mfma_bf16(al, b, acc[f]);
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
   __syncthreads();
   const float hs = 1.0f / sqrtf((float)H);
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const int e = e0 + f * 16 + r;
     if (e >= E) continue;
     const float b = bias ? bias[e] : 0.0f;
@@ -310,8 +318,12 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
 #undef MOE_FEW
     }
   } else {
-    MOE_LAUNCH(k_route_logits_wide, dim3((E + kWideExp - 1) / kWideExp, (T + kWideTok - 1) / kWideTok),
-               dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+    if (T < kWideExp16Below)
+      MOE_LAUNCH(k_route_logits_wide<16>, dim3(E / 16, (T + kWideTok - 1) / kWideTok), dim3(256), 0,
+                 s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+    else
+      MOE_LAUNCH(k_route_logits_wide<32>, dim3((E + 31) / 32, (T + kWideTok - 1) / kWideTok),
+                 dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
   }
   MOE_LAUNCH(k_route_select, dim3((T + 3) / 4), dim3(256), 0, s, logits, per_expert_scale,
                      T, E, top_k, topk_idx, topk_w, topk_w_raw);
