@@ -196,7 +196,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
-              "multi-GPU path is a design note, not part of this build.", file=sys.stderr)
+              "multi-GPU path is described, not implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
     import moe_synth as S

@@ -45,10 +45,10 @@ extern "C" {
 #define MOE_ERR_NULL (-1)        /* a required pointer is NULL                */
 #define MOE_ERR_SHAPE (-2)       /* a size is out of range or inconsistent    */
 #define MOE_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than required   */
-#define MOE_ERR_UNSUPPORTED (-4) /* valid shape this build does not handle    */
+#define MOE_ERR_UNSUPPORTED (-4) /* valid shape this library does not handle  */
 #define MOE_ERR_LAUNCH (-5)      /* a kernel launch failed (hipGetLastError)  */
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define MOE_MAX_EXPERTS 256 /* E                                   */
 #define MOE_MAX_TOPK 16     /* top_k                               */
 

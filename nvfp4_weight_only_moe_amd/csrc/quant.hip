@@ -288,7 +288,7 @@ extern "C" const char *moe_status_str(int status) {
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
     case MOE_ERR_WORKSPACE: return "workspace NULL or smaller than required";
-    case MOE_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by this library";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
