@@ -376,6 +376,25 @@ def test_expert_mlp_skewed_gemv_mode():
     _check_expert_mlp(c, idx, T, k, E, H, I)
 
 
+def test_expert_mlp_gemm_every_row_group():
+    # LDS-tiled GEMM mode (64-row blocks) with bucket sizes chosen so that
+    # blocks hold 1..16, 17..32, 33..48 and 49..64 rows (each count of 16-row
+    # groups the kernels specialise on), full and ragged, an expert of 10 row
+    # blocks (block groups of 8 with a shorter last group) and empty experts;
+    # H = 192 leaves half a K unit and down waves past N, I = 64 leaves gate/up
+    # waves past N
+    sizes = [1, 16, 17, 33, 48, 49, 64, 130, 600]
+    k, E, H, I = 1, 16, 192, 64
+    T = sum(sizes)
+    c = S.small_case(2024, T, H, I, E, k)
+    rng = np.random.default_rng(11)
+    experts = rng.permutation(E)[:len(sizes)]
+    idx = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in zip(experts, sizes)])
+    idx = idx[rng.permutation(T)].reshape(T, k)
+    assert sorted(np.bincount(idx.ravel(), minlength=E)[experts]) == sorted(sizes)
+    _check_expert_mlp(c, idx, T, k, E, H, I)
+
+
 def _check_expert_mlp(c, idx, T, k, E, H, I):
     layer = W.build_small_layer(c, k)
     off, sp, pr, _ = _bucket_gpu(idx, E)
