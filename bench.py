@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "q4_0", "aff4"],
                     help="expert weight format (the int4 ones: seeded codes and fp16 scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64,
+                    help="tokens of the workload the fp64 oracle baseline runs (about 10-20 s)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--separate-prep", action="store_true",
                     help="queue moe_route_bucket and the expert-input prep as two calls instead "
