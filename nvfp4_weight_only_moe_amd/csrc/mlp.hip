@@ -121,17 +121,19 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 // tiles of 16 outputs (gated: NP gate tiles and the same NP up tiles).
 //
 // K advances in units of 128.  Per unit the activation block [rows][128] is
-// staged once in LDS as f16 (double-buffered) and shared by the 4 waves; each
-// lane loads its 16 bytes of every weight row tile it owns (one contiguous
-// kilobyte per wave in the tiled layout), dequantises them in registers and
-// runs Q x NW x 4 MFMAs 16x16x32, so one LDS fragment feeds NW MFMAs and
-// one dequantised weight fragment feeds Q.  Q is the number of 16-row groups
-// of the block that hold rows (a partial block at the end of an expert's
-// bucket has fewer): the kernel picks the instantiation per workgroup, so
-// empty groups are neither staged nor multiplied.  Waves whose columns lie
-// past N stage activations for the others but issue no MFMAs.  The weights
-// of unit u+1 are in flight while unit u is multiplied; the activations of
-// unit u+2 while unit u+1 is staged.
+// staged once in LDS as f16 (gate/up: a ring of three buffers filled by
+// direct buffer-to-LDS loads; down: double-buffered through registers) and
+// shared by the 4 waves; each lane loads its 16 bytes of every weight row
+// tile it owns (one contiguous kilobyte per wave in the tiled layout),
+// dequantises them in registers and runs Q x NW x 4 MFMAs 16x16x32, so one
+// LDS fragment feeds NW MFMAs and one dequantised weight fragment feeds Q.
+// Q is the number of 16-row groups of the block that hold rows (a partial
+// block at the end of an expert's bucket has fewer): the kernel picks the
+// instantiation per workgroup, so empty groups are neither staged nor
+// multiplied.  Gate/up waves whose columns lie past N stage activations for
+// the others but issue no MFMAs.  Gate/up keeps the weights of two units and
+// the activations of two units in flight while a unit is multiplied; down
+// one unit of weights and two of activations.
 //
 // Order of the workgroups: a 1-D grid, a multiple of the 8 XCDs.  Hardware
 // hands workgroup b to XCD b % 8; b is mapped to the logical index
@@ -420,13 +422,12 @@ __device__ __forceinline__ void gemm_run(
     }
   };
 
-  // ---- pipeline, one barrier per unit; unrolled by two so that register
-  // buffers have static indices (an odd unit count runs one unit of zeros).
-  // Weights: double-buffered in registers, unit u+1 issued before unit u is
-  // multiplied.  Activations are fetched two units ahead.  DIRECT: a ring of
-  // three LDS buffers, unit u+2 issued before unit u is multiplied and
-  // waited for one unit later; otherwise two register sets, unit u+3 loaded
-  // when unit u+1 has been converted into the LDS double buffer.
+  // ---- pipeline, one barrier per unit; unrolled so that register buffers
+  // have static indices (steps past the last unit multiply nothing or
+  // zeros).  DIRECT (gate/up): below.  Otherwise (down): weights
+  // double-buffered in registers, unit u+1 issued before unit u is
+  // multiplied; activations in two register sets, unit u+3 loaded when unit
+  // u+1 has been converted into the LDS double buffer.
   constexpr int WS = DIRECT ? kGemmWeightSets : 2;  // weight register sets
   u32x4 wv[WS][NW];
   uint32_t sv[WS][NW];
