@@ -194,8 +194,8 @@ int moe_route_bucket(const uint16_t *x, const uint16_t *w_router, const uint16_t
  * sketch).  Same arguments as those calls and the same output bytes,
  * including the expert workspace's f16 rows; queue nvfp4_expert_gate_up and
  * nvfp4_expert_down after it.  For decode batches (moe_route_bucket's
- * one-launch path) the logits kernel's expert-0 workgroups, which read every
- * token row anyway, also write the expert input: one launch fewer.
+ * one-launch path) the selection kernel's waves also write the expert input,
+ * one token row each, beside the bucketing: one launch fewer.
  *   bucket_ws, bucket_ws_bytes   as moe_route_bucket's workspace
  *   norm_weight [H] bf16 or NULL; norm_eps >= 0 (read with norm_weight)
  *   I, expert_ws, expert_ws_bytes   as nvfp4_expert_prep's (I, workspace)
