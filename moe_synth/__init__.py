@@ -40,7 +40,7 @@ GROUP = 16
 SEED = 0
 
 # key tags
-_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER, _NORM, _INT4 = range(9)
+_W, _ROUTER_W, _ROUTER_SCALE, _PES, _ZIPF, _X, _OUTLIER, _NORM, _INT4, _H1 = range(10)
 GATE, UP, DOWN = 0, 1, 2
 
 WORKLOADS = {
@@ -125,11 +125,19 @@ def router_params(layer, seed=SEED, h=H, e=E, zipf=False):
 
 
 def norm_weights(layer, seed=SEED, h=H):
-    """The two learned norm weights around the sparse branch of one layer
-    (pre- and post-norm), bf16 bits [h] each ~ U(0.5, 1.5)."""
-    pre = _rng(seed, (_NORM, layer, 0)).uniform(0.5, 1.5, h)
-    post = _rng(seed, (_NORM, layer, 1)).uniform(0.5, 1.5, h)
-    return f32_to_bf16_bits(pre.astype(np.float32)), f32_to_bf16_bits(post.astype(np.float32))
+    """The three learned norm weights of one layer's step after the sparse
+    branch, bf16 bits [h] each ~ U(0.5, 1.5): pre_feedforward_layernorm_2 (the
+    expert input), post_feedforward_layernorm_2 (the weighted expert sum) and
+    post_feedforward_layernorm (the sum of the dense and sparse branches)."""
+    return tuple(f32_to_bf16_bits(_rng(seed, (_NORM, layer, j)).uniform(0.5, 1.5, h).astype(np.float32))
+                 for j in range(3))
+
+
+def dense_branch_output(workload, t, seed=SEED, h=H):
+    """A stand-in for the dense branch's normed output h1 [T, H] (the dense MLP
+    is outside the block): bf16 bits ~ N(0, 1)."""
+    a = _rng(seed, (_H1, workload, t)).standard_normal(t * h, dtype=np.float32).reshape(t, h)
+    return f32_to_bf16_bits(a)
 
 
 def activations(workload, t, seed=SEED, h=H, outliers=False):

@@ -22,13 +22,14 @@ Readings (the pages leave these open):
   the result (compared as sets).
 * The bucket order is (expert, token, slot); the routing weight multiplies the
   expert output after the down projection.
-* The learned norms around the branch (``pre_feedforward_layernorm_2`` on the
-  expert input, ``post_feedforward_layernorm_2`` on the weighted sum) are
-  RMSNorms with a multiplicative per-channel weight and the same epsilon; a
-  checkpoint that stores the weight as an offset from 1 passes 1 + w.  The
-  layer's residual add and ``layer_scalar`` follow the branch; its dense MLP
-  and the outer ``post_feedforward_layernorm`` are not part of the block, so
-  ``sparse_branch`` gives residual + branch (times layer_scalar) without them.
+* The learned norms of the layer step (``pre_feedforward_layernorm_2`` on the
+  expert input, ``post_feedforward_layernorm_2`` on the weighted sum,
+  ``post_feedforward_layernorm`` on the sum of the dense branch's h1 and the
+  sparse branch's h2) are RMSNorms with a multiplicative per-channel weight and
+  the same epsilon; a checkpoint that stores the weight as an offset from 1
+  passes 1 + w.  The layer's dense MLP is not part of the block: its output h1
+  (after ``post_feedforward_layernorm_1``) is an input of ``sparse_branch``
+  (zero when absent).
 """
 import numpy as np
 
@@ -221,17 +222,26 @@ def rms_norm(x, weight, eps=1e-6):
     return x * inv * np.asarray(weight, np.float64)
 
 
-def sparse_branch(residual, router, pre_norm, post_norm, gate, up, down, k=8, eps=1e-6,
-                  ids=None, layer_scalar=1.0, add_residual=True):
-    """The sparse branch of a layer with its two learned norms (float64), same
-    page and sketch: the router reads the raw residual, the experts read
-    rms_norm(residual, pre_norm), and the weighted sum of the routed outputs
-    passes through rms_norm(., post_norm).  Returns dict(out, branch, x_expert,
-    block): out = (residual + branch) * layer_scalar (without the residual when
-    ``add_residual`` is false)."""
+def sparse_branch(residual, router, pre_norm2, post_norm2, gate, up, down, k=8, eps=1e-6,
+                  ids=None, post_norm=None, h1=None, layer_scalar=1.0):
+    """The sparse branch and the layer step that follows it (float64), same
+    page, Architecture code sketch:
+
+        w, idx = router(residual)                      # the RAW residual
+        h2 = experts(rms_norm(residual, pre_norm2), idx)
+        h2 = rms_norm(sum_k w_k h2_k, post_norm2)
+        x  = residual + rms_norm(h1 + h2, post_norm)   # h1: the dense branch
+        x  = x * layer_scalar
+
+    ``h1`` is the dense branch's output (None: zero).  Without ``post_norm``
+    the layer step is not taken and ``out`` is None.  Returns dict(out, h2,
+    x_expert, block)."""
     res = np.asarray(residual, np.float64)
-    x_expert = rms_norm(res, pre_norm, eps)
+    x_expert = rms_norm(res, pre_norm2, eps)
     blk = moe_block(res, x_expert, router, gate, up, down, k, eps, ids)
-    branch = rms_norm(blk["out"], post_norm, eps)
-    out = ((res + branch) if add_residual else branch) * layer_scalar
-    return dict(out=out, branch=branch, x_expert=x_expert, block=blk)
+    h2 = rms_norm(blk["out"], post_norm2, eps)
+    out = None
+    if post_norm is not None:
+        u = h2 if h1 is None else np.asarray(h1, np.float64) + h2
+        out = (res + rms_norm(u, post_norm, eps)) * layer_scalar
+    return dict(out=out, h2=h2, x_expert=x_expert, block=blk)

@@ -115,3 +115,31 @@ def test_products_exact_in_bf16_and_f16():
     t = torch.from_numpy(prod)
     assert torch.equal(t.to(torch.bfloat16).to(torch.float64), t)
     assert torch.equal(t.to(torch.float16).to(torch.float64), t)
+
+
+def test_dequantize_no_global_hand_computed():
+    """E2M1 x E4M3 with the group of 16 along K ("Gemma-4-26B-A4B-NVFP4-mlx",
+    Notes), values worked by hand.  Row 0: codes k % 16, block scales 1.0
+    (0x38) and 2.0 (0x40); row 1: the same codes, scales 0.5 (0x30) and 0."""
+    codes = np.tile(np.arange(32) % 16, (2, 1)).astype(np.uint8)
+    packed = F.pack_nibbles(codes)
+    assert packed[0, 0] == 0x10 and packed[0, 7] == 0xFE   # low nibble = even k
+    scales = np.array([[0x38, 0x40], [0x30, 0x00]], dtype=np.uint8)
+    d = F.dequantize_no_global(packed, scales)
+    assert d.shape == (2, 32)
+    hand = {(0, 0): 0.0, (0, 1): 0.5, (0, 7): 6.0, (0, 9): -0.5, (0, 15): -6.0,
+            (0, 17): 1.0, (0, 23): 12.0, (0, 29): -6.0, (1, 5): 1.5, (1, 7): 3.0,
+            (1, 9): -0.25, (1, 14): -2.0, (1, 16): 0.0, (1, 23): 0.0}
+    for (n, k), v in hand.items():
+        assert d[n, k] == v, (n, k, d[n, k], v)
+    # with the tensor scale: the same products times g (same multiplication order)
+    g = 0.0078125 * 3
+    assert np.array_equal(F.dequantize(packed, scales, g), d * g)
+
+
+def test_dequantize_no_global_times_g_is_dequantize():
+    rng = np.random.default_rng(9)
+    packed = rng.integers(0, 256, (8, 64), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (8, 8), dtype=np.uint8)
+    g = float(np.float32(0.0123))
+    assert np.array_equal(F.dequantize_no_global(packed, scales) * g, F.dequantize(packed, scales, g))

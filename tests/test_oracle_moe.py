@@ -199,22 +199,108 @@ def test_rms_norm_closed_forms():
     assert np.all(M.rms_norm(np.zeros((1, 64)), w, 1e-6) == 0.0)
 
 
-def test_sparse_branch_composition():
-    c = S.small_case(11, 4, 32, 16, 8, 2)
-    r = {k: (F.bf16_bits_to_f64(v) if v is not None and k != "bias" else v)
-         for k, v in c["router"].items()}
+def _branch_case(seed=11, t=4, h=32, i=16, e=8, k=2):
+    c = S.small_case(seed, t, h, i, e, k)
+    r = {n: (F.bf16_bits_to_f64(v) if v is not None and n != "bias" else v)
+         for n, v in c["router"].items()}
     x = F.bf16_bits_to_f64(c["x"])
-    fn = {n: (lambda m: (lambda e: F.bf16_bits_to_f64(m[e])))(c[n]) for n in ("gate", "up", "down")}
-    pre = np.linspace(0.5, 1.5, 32)
-    post = np.linspace(1.5, 0.5, 32)
-    sb = M.sparse_branch(x, r, pre, post, fn["gate"], fn["up"], fn["down"], k=2, layer_scalar=0.75)
-    # by definition: the block on the normed expert input, then the post-norm, residual, scalar
-    blk = M.moe_block(x, M.rms_norm(x, pre), r, fn["gate"], fn["up"], fn["down"], k=2)
-    assert np.array_equal(sb["out"], (x + M.rms_norm(blk["out"], post)) * 0.75)
-    # the routing depends on the raw residual only: the pre-norm weight does not change it
-    sb2 = M.sparse_branch(x, r, 3.0 * pre, post, fn["gate"], fn["up"], fn["down"], k=2)
-    assert np.array_equal(sb2["block"]["route"]["idx"], sb["block"]["route"]["idx"])
-    # a zero post-norm weight leaves the residual times the scalar
-    z = M.sparse_branch(x, r, pre, np.zeros(32), fn["gate"], fn["up"], fn["down"], k=2,
-                        layer_scalar=2.0)
-    assert np.array_equal(z["out"], 2.0 * x)
+    fn = {n: (lambda m: (lambda ex: F.bf16_bits_to_f64(m[ex])))(c[n]) for n in ("gate", "up", "down")}
+    return x, r, fn
+
+
+def test_layer_step_outer_norm_sees_h1_plus_h2():
+    """"Gemma 4 26B-A4B (MoE) - Core AI", Architecture code sketch: the layer
+    adds the residual to post_feedforward_layernorm(h1 + h2), then scales by
+    layer_scalar.  Special cases with eps = 0, where the norms have closed
+    forms, each failing for a plausible wrong composition."""
+    x, r, fn = _branch_case()
+    h, ones = x.shape[1], np.ones(x.shape[1])
+
+    def step(**kw):
+        base = dict(pre_norm2=ones, post_norm2=ones, post_norm=ones, eps=0.0)
+        base.update(kw)
+        # the expert input here is rms_norm(x, 1) (pre-norm weight one), not x
+        return M.sparse_branch(x, r, base.pop("pre_norm2"), base.pop("post_norm2"), fn["gate"],
+                               fn["up"], fn["down"], k=2, **base)
+
+    # the pre-norm of the expert input is scale-free, so feed the block x / rms(x)
+    s_n = M.moe_block(x, x / np.sqrt(np.mean(x * x, axis=1, keepdims=True)), r, fn["gate"],
+                      fn["up"], fn["down"], k=2, eps=0.0)["out"]
+    unit = s_n / np.sqrt(np.mean(s_n * s_n, axis=1, keepdims=True))
+    # h1 = 0, outer weight 2: the outer norm of a unit-RMS row is 2x the row
+    # (a missing outer norm, or the old residual + post_norm_2(sum), gives 1x)
+    got = step(post_norm=np.full(h, 2.0))["out"]
+    assert np.allclose(got, x + 2.0 * unit, rtol=0, atol=1e-12)
+    # h1 = h2 (both unit RMS): norm(2 h2) = h2, so out = x + w * h2; adding h1
+    # after the outer norm instead would give x + h2 + w * h2
+    w = np.linspace(0.5, 1.5, h)
+    got = step(post_norm=w, h1=unit)["out"]
+    assert np.allclose(got, x + w * unit, rtol=0, atol=1e-12)
+    # h1 = -h2 (the branch's own h2): the outer norm sees zero and the
+    # residual passes alone, scaled (eps > 0 keeps the zero row finite)
+    h2 = step(post_norm=None, eps=1e-6)["h2"]
+    got = step(h1=-h2, layer_scalar=0.75, eps=1e-6)["out"]
+    assert np.array_equal(got, 0.75 * x)
+    # any h1: (out / scalar - residual) / w has RMS exactly 1 in every row
+    h1 = np.random.default_rng(5).standard_normal(x.shape)
+    got = step(post_norm=w, h1=h1, layer_scalar=0.5)["out"]
+    v = (got / 0.5 - x) / w
+    assert np.allclose(np.sqrt(np.mean(v * v, axis=1)), 1.0, rtol=1e-12)
+    # the layer scalar multiplies the whole step (a power of two: exact)
+    a = step(post_norm=w, h1=h1, layer_scalar=1.0)["out"]
+    assert np.array_equal(step(post_norm=w, h1=h1, layer_scalar=0.25)["out"], 0.25 * a)
+    # without the outer norm weight the step is not taken: h2 alone
+    b = step(post_norm=None)
+    assert b["out"] is None and np.allclose(b["h2"], unit, rtol=0, atol=1e-12)
+
+
+def test_routing_reads_the_raw_residual_and_experts_the_normed_one():
+    """Same sketch: router(residual) on the raw residual, the experts on
+    pre_feedforward_layernorm_2(residual).  A per-channel pre-norm weight that
+    reroutes the normed input shows which one the router read."""
+    x, r, fn = _branch_case(seed=12, t=6, e=8, k=2)
+    h = x.shape[1]
+    pre = np.where(np.arange(h) % 2 == 0, 0.05, 4.0)
+    raw = M.route(x, r["w_router"], r["scale"], r["per_expert_scale"], 2)["idx"]
+    normed = M.route(M.rms_norm(x, pre), r["w_router"], r["scale"], r["per_expert_scale"], 2)["idx"]
+    assert not np.array_equal(np.sort(raw, 1), np.sort(normed, 1))   # the pin can fail
+    sb = M.sparse_branch(x, r, pre, np.ones(h), fn["gate"], fn["up"], fn["down"], k=2,
+                         post_norm=np.ones(h))
+    assert np.array_equal(np.sort(sb["block"]["route"]["idx"], 1), np.sort(raw, 1))
+    # the experts read a scale-free norm of the residual: 4x (exact in fp64)
+    # gives the same branch output h2 (eps = 0); the GELU-gated experts on
+    # the raw residual would not be homogeneous in it
+    a = M.sparse_branch(x, r, pre, np.ones(h), fn["gate"], fn["up"], fn["down"], k=2, eps=0.0)
+    b = M.sparse_branch(4.0 * x, r, pre, np.ones(h), fn["gate"], fn["up"], fn["down"], k=2, eps=0.0)
+    assert np.allclose(a["h2"], b["h2"], rtol=0, atol=1e-12)
+    raw_in = M.moe_block(4.0 * x, 4.0 * x, r, fn["gate"], fn["up"], fn["down"], k=2, eps=0.0)["out"]
+    raw_in1 = M.moe_block(x, x, r, fn["gate"], fn["up"], fn["down"], k=2, eps=0.0)["out"]
+    assert not np.allclose(M.rms_norm(raw_in, np.ones(h), 0.0), M.rms_norm(raw_in1, np.ones(h), 0.0),
+                           rtol=0, atol=1e-6)
+
+
+def test_weights_for_ids_hand_computed():
+    """Softmax probabilities at the given ids, renormalised over them, times
+    per_expert_scale ("Gemma 4 26B-A4B (MoE) - Core AI", router description).
+    logits ln(1, 2, 3, 4, 6): probabilities 1/16 .. 6/16; ids (4, 1) take
+    6/16 and 2/16 -> 3/4 and 1/4 (renormalising the logits instead would give
+    ln 6 / ln 12 = 0.72)."""
+    logits = np.log(np.array([[1.0, 2.0, 3.0, 4.0, 6.0], [5.0, 5.0, 5.0, 5.0, 5.0]]))
+    pes = np.array([1.0, 0.5, 2.0, 1.0, 1.5])
+    ids = np.array([[4, 1], [2, 0]])
+    w, w_raw = M.weights_for_ids(logits, pes, ids)
+    assert np.allclose(w_raw, [[0.75, 0.25], [0.5, 0.5]], rtol=0, atol=1e-15)
+    assert np.allclose(w, [[1.125, 0.125], [1.0, 0.5]], rtol=0, atol=1e-15)
+
+
+def test_weights_for_ids_agrees_with_route():
+    p = S.router_params(0)
+    x = _f64(S.activations(1, 16))
+    wr, sc, pes = _f64(p["w_router"]), _f64(p["scale"]), _f64(p["per_expert_scale"])
+    r = M.route(x, wr, sc, pes, k=8)
+    w, w_raw = M.weights_for_ids(r["logits"], pes, r["idx"])
+    assert np.array_equal(w, r["w"]) and np.array_equal(w_raw, r["w_raw"])
+    # a permutation of the ids permutes the weights
+    perm = r["idx"][:, ::-1]
+    w2, _ = M.weights_for_ids(r["logits"], pes, perm)
+    assert np.allclose(w2, r["w"][:, ::-1], rtol=1e-15, atol=0)
