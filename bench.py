@@ -3,22 +3,34 @@
 MI355X.
 
 A step is one pass of the whole hot path -- routing, bucketing and the expert
-input's prep (one moe_route_bucket_prep call), the expert MLP's gate/up and
-down projections, and moe_combine -- over one batch of seeded synthetic tokens,
-with inputs and weights already resident in HBM.  The default workload is one
-model-shaped layer at decode batch T = 64 (hidden 2816, 128 experts, top-8,
-expert intermediate 704, NVFP4 experts from bf16 N(0, 0.02)).
+input's prep, the expert MLP's gate/up and down projections, and the weighted
+combine -- over one batch of seeded synthetic tokens, with inputs and weights
+already resident in HBM.  Model shapes: hidden 2816, 128 experts, top-8,
+expert intermediate 704, NVFP4 experts quantised on the GPU from bf16
+N(0, 0.02).
+
+Workloads (--workload):
+  0  one layer, decode T = 4
+  1  one layer, decode T = 64 (the headline line)
+  2  one layer, prefill T = 2048, Zipf(1.2) expert popularity
+  3  the 30-layer stack (12.85 GB of NVFP4 experts), one decode sweep through
+     all 30 layers per step, T = 1 or 8 (--sweep-T)
+  4  one layer, prefill T = 16384, Zipf(1.2) + 1% outlier rows x20
+Without --workload every one of them is measured: the JSON line is workload
+1's, and detail.workloads holds each workload's own figures (T = 1 and T = 8
+for workload 3).
 
 Timing: W warm-up steps, then K steps captured in one HIP graph on one stream
-and replayed once, bracketed by synchronisations (ms_per_step is wall clock /
-K).  The dominant kernel (the gate/up GEMV/GEMM) is timed by HIP events around
-back-to-back launches of its stage call on the same stream; per-stage
-durations come from a second graph of the K steps in which every stage call is
-a child graph between timing-event nodes.  Consecutive steps read different,
-byte-identical copies of the expert weights so that each step streams its
-experts from HBM instead of the 256 MB last-level cache.
+and replayed once.  ms_per_step is the GPU time of that replay from HIP events
+recorded on the same stream around the graph launch, divided by K (the host
+wall clock around launch and synchronisation is reported beside it).  The
+dominant kernel (the gate/up projection) is timed by HIP events around
+back-to-back launches of its stage call on the same stream.  Consecutive steps
+of a single-layer workload read different, byte-identical copies of the expert
+weights, so that each step streams its experts from HBM instead of the 256 MB
+last-level cache.
 
-Prints one JSON line (rank 0).
+Prints one JSON line.
 """
 import argparse
 import ctypes
@@ -38,22 +50,25 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
 STAGES = ("route_bucket_prep", "gate_up", "down", "combine")
 SEPARATE_STAGES = ("route_bucket", "prep", "gate_up", "down", "combine")
+METRIC = "MoE layer tokens/s; decode NVFP4 weight GB/s; prefill TFLOP/s (1 MI355X)"
+# the workloads of the default run, in order: (workload, tokens per layer)
+ALL_RUNS = ((1, 64), (0, 4), (2, 2048), (4, 16384), (3, 1), (3, 8))
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 200; 10 for the 30-layer sweep)")
+                    help="timed steps (default 200 for one layer, 20 for the 30-layer sweep)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default 20; 3 for the 30-layer sweep)")
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
-                    help="0: T=4, 1: T=64 (default), 2: T=2048 Zipf, 4: T=16384 Zipf+outliers, "
-                         "3: 30-layer decode sweep")
-    ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3 (1 or 8)")
+                    help="untimed warm-up steps (default 20 for one layer, 3 for the sweep)")
+    ap.add_argument("--workload", type=int, default=None, choices=[0, 1, 2, 3, 4],
+                    help="measure one workload only (default: all, workload 1 as the headline)")
+    ap.add_argument("--sweep-T", type=int, default=8, help="tokens per layer for workload 3")
     ap.add_argument("--chain", action="store_true",
                     help="workload 3: chain the layers through the residual (each layer's sparse "
-                         "branch with its learned norms reads the previous layer's output)")
+                         "branch with its learned norms and the layer step reads the previous "
+                         "layer's output)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the token count of workload 0, 1, 2 or 4 (a size sweep)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies to rotate (0 = auto)")
@@ -61,42 +76,41 @@ def parse():
                     help="expert weight format (the int4 ones: seeded codes and fp16 scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64,
-                    help="tokens of the workload the fp64 oracle baseline runs (about 10-20 s)")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+                    help="tokens of the workload the fp64 oracle baseline runs")
+    ap.add_argument("--stages", action="store_true",
+                    help="also time every stage call (a second graph with event nodes)")
     ap.add_argument("--separate-prep", action="store_true",
                     help="queue moe_route_bucket and the expert-input prep as two calls instead "
                          "of one moe_route_bucket_prep")
-    ap.add_argument("--prep-branch", action="store_true",
-                    help="with --separate-prep: run the prep on a parallel graph branch (forked "
-                         "and joined per layer) instead of first on the one stream")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter scaling reference)")
-    args = ap.parse_args()
-    if args.steps is None:
-        args.steps = 10 if args.workload == 3 else 200
-    if args.warmup is None:
-        args.warmup = 3 if args.workload == 3 else 20
-    return args
+    return ap.parse_args(argv)
+
+
+def step_defaults(workload, steps, warmup):
+    sweep = workload == 3
+    return (steps if steps is not None else (20 if sweep else 200),
+            warmup if warmup is not None else (3 if sweep else 20))
 
 
 class HipRuntime:
-    """The few HIP runtime calls torch does not expose on ROCm: timing events
-    recorded as external nodes of a captured graph, capture and launch of that
-    graph.  Uses the HIP runtime torch has already loaded."""
+    """The few HIP runtime calls torch does not expose on ROCm: events recorded
+    on a raw stream or as nodes of a graph, stream capture, graph launch.
+    Uses the HIP runtime torch has already loaded."""
 
     def __init__(self):
         path = next((l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l),
                     "libamdhip64.so")
         h = ctypes.CDLL(path)
         vp, P = ctypes.c_void_p, ctypes.POINTER
-        for name, args in {"hipEventCreate": [P(vp)], "hipEventRecordWithFlags": [vp, vp, ctypes.c_uint],
-                           "hipEventRecord": [vp, vp], "hipStreamWaitEvent": [vp, vp, ctypes.c_uint],
+        for name, args in {"hipEventCreate": [P(vp)], "hipEventRecord": [vp, vp],
                            "hipEventElapsedTime": [P(ctypes.c_float), vp, vp],
                            "hipStreamBeginCapture": [vp, ctypes.c_int],
                            "hipStreamEndCapture": [vp, P(vp)],
                            "hipGraphInstantiate": [P(vp), vp, vp, ctypes.c_char_p, ctypes.c_size_t],
                            "hipGraphLaunch": [vp, vp], "hipGetErrorString": [ctypes.c_int],
                            "hipGraphCreate": [P(vp), ctypes.c_uint],
+                           "hipGraphExecDestroy": [vp],
                            "hipGraphAddEventRecordNode": [P(vp), vp, P(vp), ctypes.c_size_t, vp],
                            "hipGraphAddChildGraphNode": [P(vp), vp, P(vp), ctypes.c_size_t, vp]}.items():
             f = getattr(h, name)
@@ -113,21 +127,15 @@ class HipRuntime:
         self._ok(self.h.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
         return ev
 
-    def record(self, ev, stream, external):
-        if external:
-            self._ok(self.h.hipEventRecordWithFlags(ev, stream, 1), "hipEventRecordWithFlags")
-        else:
-            self._ok(self.h.hipEventRecord(ev, stream), "hipEventRecord")
-
-    def wait(self, stream, ev):
-        self._ok(self.h.hipStreamWaitEvent(stream, ev, 0), "hipStreamWaitEvent")
+    def record(self, ev, stream):
+        self._ok(self.h.hipEventRecord(ev, stream), "hipEventRecord")
 
     def elapsed(self, a, b):
         ms = ctypes.c_float()
         self._ok(self.h.hipEventElapsedTime(ctypes.byref(ms), a, b), "hipEventElapsedTime")
         return ms.value
 
-    def capture_graph(self, stream, fn):
+    def capture(self, stream, fn):
         """Stream-capture whatever fn() queues on `stream` into a graph."""
         self._ok(self.h.hipStreamBeginCapture(stream, 2), "hipStreamBeginCapture")  # relaxed
         graph = ctypes.c_void_p()
@@ -137,6 +145,15 @@ class HipRuntime:
             rc = self.h.hipStreamEndCapture(stream, ctypes.byref(graph))
         self._ok(rc, "hipStreamEndCapture")
         return graph
+
+    def instantiate(self, g):
+        exe = ctypes.c_void_p()
+        self._ok(self.h.hipGraphInstantiate(ctypes.byref(exe), g, None, None, 0),
+                 "hipGraphInstantiate")
+        return exe
+
+    def launch(self, exe, stream):
+        self._ok(self.h.hipGraphLaunch(exe, stream), "hipGraphLaunch")
 
     def timed_chain(self, stream, calls, events):
         """One graph: event[0], calls[0], event[1], calls[1], ... event[n] as a
@@ -156,7 +173,7 @@ class HipRuntime:
 
         prev = add_event(events[0])
         for call, ev in zip(calls, events[1:]):
-            child = self.capture_graph(stream, call)
+            child = self.capture(stream, call)
             node = ctypes.c_void_p()
             deps = (ctypes.c_void_p * 1)(prev)
             self._ok(self.h.hipGraphAddChildGraphNode(ctypes.byref(node), g, deps, 1, child),
@@ -165,14 +182,18 @@ class HipRuntime:
             prev = add_event(ev)
         return self.instantiate(g)
 
-    def instantiate(self, g):
-        exe = ctypes.c_void_p()
-        self._ok(self.h.hipGraphInstantiate(ctypes.byref(exe), g, None, None, 0),
-                 "hipGraphInstantiate")
-        return exe
-
-    def launch(self, exe, stream):
-        self._ok(self.h.hipGraphLaunch(exe, stream), "hipGraphLaunch")
+    def timed_replay(self, exe, stream, sync):
+        """GPU milliseconds of one replay of `exe` (events on `stream` around
+        the launch) and the host wall-clock milliseconds of launch + sync."""
+        a, b = self.event(), self.event()
+        sync()
+        t0 = time.perf_counter()
+        self.record(a, stream)
+        self.launch(exe, stream)
+        self.record(b, stream)
+        sync()
+        wall = (time.perf_counter() - t0) * 1e3
+        return self.elapsed(a, b), wall
 
 
 # scale bytes per 32 weights: two E4M3 codes (NVFP4), one fp16 d (q4_0), fp16 s and b (aff4)
@@ -188,318 +209,6 @@ def proj_bytes(H, I, fmt="nvfp4"):
 
 def expert_bytes_per_expert(H, I, fmt="nvfp4"):
     return 3 * proj_bytes(H, I, fmt)
-
-
-def main():
-    args = parse()
-    if args.copy_reference:
-        copy_reference(args.copy_reference)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
-              "multi-GPU path is described, not implemented.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import moe_synth as S
-    import nvfp4_weight_only_moe_amd as moe
-    from nvfp4_weight_only_moe_amd import workload as Wl
-
-    torch.cuda.set_device(0)
-    moe.lib()
-    wl = dict(S.WORKLOADS[args.workload])
-    if args.tokens and args.workload != 3:
-        wl["T"] = (args.tokens,)
-        wl["name"] = re.sub(r"_T\d+", f"_T{args.tokens}", wl["name"])
-    H, I, E, K = S.H, S.I, S.E, S.TOP_K
-    t_setup = time.perf_counter()
-
-    fmt = args.format
-    if fmt != "nvfp4":
-        wl["name"] += f"_{fmt}"
-
-    def make_layer(l, zipf):
-        if fmt == "nvfp4":
-            return Wl.build_layer(l, zipf=zipf)
-        return Wl.build_int4_layer(fmt, l, zipf=zipf)
-
-    if args.workload == 3:
-        T = args.sweep_T
-        layers = [make_layer(l, False) for l in range(S.LAYERS)]
-        step_layers = [layers]                       # one step = the 30-layer sweep
-        replicas = 1                                 # 12.85 GB of distinct weights per sweep
-    else:
-        T = wl["T"][0]
-        base = make_layer(0, wl["zipf"])
-        touched = expert_bytes_per_expert(H, I, fmt) * min(E, T * K)
-        replicas = args.replicas or max(2, min(16, math.ceil(1.5 * 2 ** 30 / touched) + 1))
-        reps = Wl.replicate_experts(base, replicas)
-        step_layers = [[r] for r in reps]
-    x = Wl.to_device_bf16(S.activations(args.workload, T, outliers=wl["outliers"]))
-    buf = moe.MoeBuffers(T, H, I, E, K)
-    # chained sweep: layer l reads xs[l] and writes xs[l + 1] (xs[0] = x, so
-    # every step runs the same chain)
-    chain = args.chain and args.workload == 3
-    if chain:
-        wl["name"] += "_chained"
-        norms = [moe.BranchNorms(*[Wl.to_device_bf16(a) for a in S.norm_weights(l)])
-                 for l in range(len(step_layers[0]))]
-        xs = [x] + [torch.empty_like(x) for _ in step_layers[0]]
-    torch.cuda.synchronize()
-    t_setup = time.perf_counter() - t_setup
-
-    def one_step(s, marks=None):
-        for li, layer in enumerate(step_layers[s % len(step_layers)]):
-            if chain:
-                moe.forward_branch(layer, xs[li], buf, norms[li])
-                xs[li + 1].copy_(buf.out)
-            else:
-                moe.forward(layer, x, buf, marks=marks)
-
-    for s in range(args.warmup):
-        one_step(s)
-    torch.cuda.synchronize()
-
-    # K steps, a timing event around every stage call.  With a graph the
-    # events are external event-record nodes of the graph itself.
-    n_layers = len(step_layers[0])
-    hip = HipRuntime()
-    stream, side = torch.cuda.Stream(), torch.cuda.Stream()
-    hs, hside = ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side.cuda_stream)
-    from nvfp4_weight_only_moe_amd import _lib as C
-
-    separate = args.separate_prep or args.prep_branch
-    stages = SEPARATE_STAGES if separate else STAGES
-
-    def stage_calls(layer, prep_stream=None, li=0):
-        """The stage calls of one block pass (layer li of the step), by name."""
-        x_in = xs[li] if chain else x
-        nm = norms[li] if chain else None
-        if chain:
-            prep = lambda: C.nvfp4_expert_prep_rmsnorm(x_in, nm.pre, nm.eps, E, I, K, buf.ws,
-                                                       prep_stream or stream)
-            combine = lambda: C.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank,
-                                                    nm.post, nm.eps, xs[li + 1], x_in,
-                                                    nm.layer_scalar, stream)
-        else:
-            prep = lambda: C.nvfp4_expert_prep(x_in, E, I, K, buf.ws, prep_stream or stream)
-            combine = lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out,
-                                            stream)
-        return {
-            "route_bucket_prep": lambda: C.moe_route_bucket_prep(
-                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
-                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
-                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
-                nm.pre if chain else None, nm.eps if chain else 0.0, I, buf.ws, stream),
-            "route_bucket": lambda: C.moe_route_bucket(
-                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
-                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
-                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
-                stream),
-            "prep": prep,
-            "gate_up": lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
-                                                      buf.sorted_pairs, T, K, H, buf.ws, stream),
-            "down": lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K,
-                                                buf.y_sorted, buf.ws, stream),
-            "combine": combine,
-        }
-
-    step_plan = [step_layers[(args.warmup + s) % len(step_layers)] for s in range(args.steps)]
-    fork_join = [(hip.event(), hip.event()) for _ in range(args.steps * n_layers)]
-
-    def queue_steps():
-        """K steps on one stream: per layer route + bucket + prep (one call),
-        gate/up, down, combine.  --separate-prep: prep, then route + bucket,
-        as two calls; --prep-branch: the prep on `side` instead, forked after
-        the previous layer's combine and joined before the gate/up GEMM (a
-        dependency across queues costs more than the prep)."""
-        n = 0
-        for layers in step_plan:
-            for li, layer in enumerate(layers):
-                c = stage_calls(layer, side if args.prep_branch else None, li)
-                if args.prep_branch:
-                    fork, join = fork_join[n]
-                    n += 1
-                    hip.record(fork, hs, False)
-                    hip.wait(hside, fork)
-                    c["prep"]()
-                    hip.record(join, hside, False)
-                    c["route_bucket"]()
-                    hip.wait(hs, join)
-                elif separate:
-                    c["prep"]()
-                    c["route_bucket"]()
-                else:
-                    c["route_bucket_prep"]()
-                c["gate_up"]()
-                c["down"]()
-                c["combine"]()
-
-    # ---- timed region: the K steps as one graph, replayed once
-    mode, graph = "eager", None
-    torch.cuda.synchronize()
-    if not args.eager:
-        try:
-            graph = hip.instantiate(hip.capture_graph(hs, queue_steps))
-            mode = ("hip_graph (prep on a parallel branch)" if args.prep_branch else
-                    "hip_graph (one stream, route + prep as two calls)" if separate else
-                    "hip_graph (one stream)")
-            hip.launch(graph, hs)            # one untimed replay
-            stream.synchronize()
-        except Exception as exc:
-            print(f"graph build failed ({exc}); timing eager launches", file=sys.stderr)
-            graph = None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graph is not None:
-        hip.launch(graph, hs)
-    else:
-        queue_steps()
-    stream.synchronize()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # ---- per-stage durations: the same K steps with every stage call a
-    # child graph between timing-event nodes (serial order, one stream)
-    calls = []
-    for layers in step_plan:
-        for li, layer in enumerate(layers):
-            c = stage_calls(layer, None, li)
-            calls += [c[n] for n in stages]
-    bounds = [hip.event() for _ in range(len(calls) + 1)]   # event i precedes call i
-    if not args.eager:
-        timed_graph = hip.timed_chain(hs, calls, bounds)
-        hip.launch(timed_graph, hs)
-        events_mode = "hip_graph_with_event_nodes"
-    else:
-        hip.record(bounds[0], hs, False)
-        for call, e in zip(calls, bounds[1:]):
-            call()
-            hip.record(e, hs, False)
-        events_mode = "eager_with_events"
-    stream.synchronize()
-    torch.cuda.synchronize()
-
-    # ---- the dominant kernel alone: the gate/up stage call R times back to
-    # back (the same routing and buffers, the layers of the step plan in
-    # turn, so the weights stream from HBM as in the steps) between two
-    # timing events on the launch stream; the event cost spreads over R
-    gu_calls = [stage_calls(layers[li], None, li)["gate_up"]
-                for layers in step_plan for li in range(len(layers))]
-    reps_gu = max(20, len(gu_calls))
-    gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
-    gu_ev = [hip.event(), hip.event()]
-    if not args.eager:
-        gu_graph = hip.timed_chain(hs, [lambda: [c() for c in gu_seq]], gu_ev)
-        hip.launch(gu_graph, hs)                    # warm
-        stream.synchronize()
-        hip.launch(gu_graph, hs)
-    else:
-        hip.record(gu_ev[0], hs, False)
-        for c in gu_seq:
-            c()
-        hip.record(gu_ev[1], hs, False)
-    stream.synchronize()
-    gu_kernel_us = 1e3 * hip.elapsed(gu_ev[0], gu_ev[1]) / reps_gu
-
-    stage_ms = {n: [] for n in stages}
-    gpu_step_ms = []
-    per_step = n_layers * len(stages)
-    for s in range(args.steps):
-        b = bounds[s * per_step:(s + 1) * per_step + 1]
-        for j in range(per_step):
-            stage_ms[stages[j % len(stages)]].append(hip.elapsed(b[j], b[j + 1]))
-        gpu_step_ms.append(hip.elapsed(b[0], b[-1]))
-    stage_avg_us = {n: 1e3 * float(np.mean(v)) for n, v in stage_ms.items()}
-
-    # work done per step (realised routing)
-    counts = np.diff(buf.expert_offsets.cpu().numpy())
-    U = int((counts > 0).sum())                  # active experts of the last layer run
-    P = T * K
-    if args.workload == 3:
-        U_layers = []
-        for li, layer in enumerate(step_layers[0]):
-            if chain:
-                moe.forward_branch(layer, xs[li], buf, norms[li])
-                xs[li + 1].copy_(buf.out)
-            else:
-                moe.forward(layer, x, buf)
-            torch.cuda.synchronize()
-            U_layers.append(int((np.diff(buf.expert_offsets.cpu().numpy()) > 0).sum()))
-        U_total = sum(U_layers)
-    else:
-        U_layers, U_total = [U], U
-    per_exp = expert_bytes_per_expert(H, I, fmt)
-    gu_w_bytes = 2 * proj_bytes(H, I, fmt)
-    step_s = ms_per_step / 1e3
-    # the back-to-back gate/up launches all ran on the routing still in buf
-    # (the last layer queued before them), whose U is counted above
-    gate_up_alg_bytes = gu_w_bytes * U + T * H * 2 + P * I * 2     # per launch
-    gu_us = gu_kernel_us
-    achieved_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9
-    expert_flops = 2.0 * P * 3 * I * H * n_layers
-    out = {
-        "metric": "MoE layer tokens/s; decode NVFP4 weight GB/s; prefill TFLOP/s (1 MI355X)",
-        "value": T / step_s if args.workload != 3 else T / step_s,
-        "unit": "tokens/s" if args.workload != 3 else "tokens/s (30-layer sweep)",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPES[fmt] + " x bf16 activations; f16 MFMA, fp32 accumulate",
-        "data": DATA[fmt],
-        "config": {"workload": wl["name"], "tokens": T, "hidden": H, "experts": E, "top_k": K,
-                   "moe_intermediate": I, "layers": n_layers, "weight_replicas": replicas,
-                   "timing": mode},
-        "detail": {
-            "stage_timing": events_mode,
-            "chained_layers": bool(chain),
-            "gpu_ms_per_step_with_event_nodes": float(np.mean(gpu_step_ms)),
-            "stage_avg_us": stage_avg_us,
-            "gate_up_kernel_us_back_to_back": gu_kernel_us,
-            "active_experts": U_total,
-            "expert_weight_GBps": per_exp * U_total / step_s / 1e9,
-            "layer_alg_GBps": (per_exp * U_total + n_layers * ((E * H + H + E) * 2 + 2 * T * H * 2)) / step_s / 1e9,
-            "expert_TFLOPs": expert_flops / step_s / 1e12,
-            "max_over_mean_bucket": float(counts.max() / max(counts.mean(), 1e-9)),
-            "setup_s": t_setup,
-        },
-    }
-    # Roofline of the dominant kernel, the gate/up projection: the HBM one for
-    # decode (its algorithmic bytes: the active experts' gate and up tensors,
-    # the f16 activations and A written), the f16 MFMA one for prefill (its
-    # algorithmic flops 2 P 2 I H); the other one is reported beside it.
-    gu_kernel = gate_up_kernel_name(T, K, E, fmt)
-    traffic = profiled_traffic(wl["name"], gu_kernel)   # HBM bytes per launch (counters)
-    hbm = {"kernel": gu_kernel, "bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
-           "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": traffic,
-           "alg_bytes_per_launch": gate_up_alg_bytes, "avg_launch_us": gu_us,
-           "units": f"{U} active experts x {gu_w_bytes} B + {T} x {H} x 2 B + {P} x {I} x 2 B"}
-    gu_flops = 2.0 * P * 2 * I * H
-    tflops = gu_flops / (gu_us * 1e-6) / 1e12
-    mfma = {"kernel": gu_kernel, "bound": "mfma", "achieved": tflops, "peak": F16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": tflops / F16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-            "alg_flops_per_launch": gu_flops, "avg_launch_us": gu_us}
-    if args.workload in (2, 4):
-        out["roofline"], out["roofline_hbm"] = mfma, hbm
-    else:
-        out["roofline"], out["roofline_mfma"] = hbm, mfma
-    if not args.no_cpu_baseline and args.workload != 3:
-        out["cpu_baseline"] = cpu_baseline(args, wl, T)
-    print(json.dumps(out), flush=True)
-
-
-S_I = 704  # expert intermediate size of the workloads
-DTYPES = {"nvfp4": "nvfp4 weights (e2m1 x e4m3 x fp32)",
-          "q4_0": "int4 q4_0 weights ((q - 8) x fp16 d per 32)",
-          "aff4": "int4 affine weights (q x fp16 s + fp16 b per 32)"}
-DATA = {"nvfp4": "synthetic (seeded; bf16 N(0,0.02) experts quantised to NVFP4 on the GPU)",
-        "q4_0": "synthetic (seeded; uniform int4 codes, fp16 d ~ U(0.004, 0.008))",
-        "aff4": "synthetic (seeded; uniform int4 codes, fp16 s ~ U(0.004, 0.008), "
-                "b ~ U(-0.06, -0.035))"}
 
 
 def gate_up_kernel_name(T, K, E, fmt="nvfp4"):
@@ -526,18 +235,328 @@ def profiled_traffic(workload, kernel):
     h = hashlib.sha256()
     for f in ("mlp.hip", "common.h"):     # the expert kernels and their decode
         h.update(open(os.path.join(HERE, "nvfp4_weight_only_moe_amd", "csrc", f), "rb").read())
-    digest = h.hexdigest()
     rec = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != digest or rec.get("kernel") != kernel:
+    if rec.get("source_sha256") != h.hexdigest() or rec.get("kernel") != kernel:
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class Bench:
+    """Device state shared by the workloads of one run: layer 0's expert
+    weights (and their byte-identical replicas) behind either router, the
+    30-layer stack when asked for, the HIP runtime and one stream."""
+
+    def __init__(self, args):
+        import torch
+        import moe_synth as S
+        import nvfp4_weight_only_moe_amd as moe
+        from nvfp4_weight_only_moe_amd import workload as Wl
+        from nvfp4_weight_only_moe_amd import _lib as C
+        self.torch, self.S, self.moe, self.Wl, self.C = torch, S, moe, Wl, C
+        self.args = args
+        self.fmt = args.format
+        self.hip = HipRuntime()
+        self.stream = torch.cuda.Stream()
+        self.hs = ctypes.c_void_p(self.stream.cuda_stream)
+        self.H, self.I, self.E, self.K = S.H, S.I, S.E, S.TOP_K
+        self._base, self._reps, self._stack = None, [], None
+
+    def make_layer(self, l, zipf):
+        if self.fmt == "nvfp4":
+            return self.Wl.build_layer(l, zipf=zipf)
+        return self.Wl.build_int4_layer(self.fmt, l, zipf=zipf)
+
+    def single_layer(self, zipf, replicas):
+        """`replicas` byte-identical copies of layer 0's experts behind the
+        plain or the Zipf-biased router."""
+        S, Wl, moe = self.S, self.Wl, self.moe
+        if self._base is None:
+            self._base = self.make_layer(0, False)
+            self._reps = [self._base]
+        while len(self._reps) < replicas:
+            b = self._base
+            self._reps.append(b.with_experts(b.gate.clone(), b.up.clone(), b.down.clone()))
+        reps = self._reps[:replicas]
+        if zipf:
+            wr, sc, pes, bias = Wl.router_to_device(S.router_params(0, zipf=True))
+            reps = [moe.MoeLayer(wr, sc, pes, bias, r.gate, r.up, r.down, self.K) for r in reps]
+        return reps
+
+    def stack(self):
+        if self._stack is None:
+            self._stack = [self.make_layer(l, False) for l in range(self.S.LAYERS)]
+        return self._stack
+
+
+def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=None):
+    """Measure one workload: K steps in one graph, replayed once, event-timed;
+    the gate/up kernel alone; the work done.  Returns a dict of figures."""
+    torch, S, moe, C, hip = B.torch, B.S, B.moe, B.C, B.hip
+    H, I, E, K, fmt = B.H, B.I, B.E, B.K, B.fmt
+    wl = dict(S.WORKLOADS[workload])
+    name = name or wl["name"]
+    t_setup = time.perf_counter()
+    if workload == 3:
+        step_layers = [B.stack()]
+        replicas = 1
+    else:
+        touched = expert_bytes_per_expert(H, I, fmt) * min(E, T * K)
+        replicas = B.args.replicas or max(2, min(16, math.ceil(1.5 * 2 ** 30 / touched) + 1))
+        step_layers = [[r] for r in B.single_layer(wl["zipf"], replicas)]
+    x = B.Wl.to_device_bf16(S.activations(workload, T, outliers=wl["outliers"]))
+    buf = moe.MoeBuffers(T, H, I, E, K)
+    n_layers = len(step_layers[0])
+    if chain:
+        norms = [moe.BranchNorms(*[B.Wl.to_device_bf16(a) for a in S.norm_weights(l)])
+                 for l in range(n_layers)]
+        xs = [x] + [torch.empty_like(x) for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    hs, stream = B.hs, B.stream
+    separate = B.args.separate_prep
+    stage_names = SEPARATE_STAGES if separate else STAGES
+
+    def stage_calls(layer, li):
+        """The stage calls of one block pass (layer li of the step), by name."""
+        x_in = xs[li] if chain else x
+        nm = norms[li] if chain else None
+        if chain:
+            prep = lambda: C.nvfp4_expert_prep_rmsnorm(x_in, nm.pre2, nm.eps, E, I, K, buf.ws,
+                                                       stream)
+            combine = lambda: C.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank,
+                                                    nm.post2, nm.eps, xs[li + 1],
+                                                    post_norm=nm.post, residual=x_in,
+                                                    layer_scalar=nm.layer_scalar, stream=stream)
+        else:
+            prep = lambda: C.nvfp4_expert_prep(x_in, E, I, K, buf.ws, stream)
+            combine = lambda: C.moe_combine(buf.y_sorted, buf.topk_w, buf.pair_rank, buf.out,
+                                            stream)
+        return {
+            "route_bucket_prep": lambda: C.moe_route_bucket_prep(
+                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
+                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
+                nm.pre2 if chain else None, nm.eps if chain else 0.0, I, buf.ws, stream),
+            "route_bucket": lambda: C.moe_route_bucket(
+                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                layer.logit_bias, K, layer.eps, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
+                buf.logits, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
+                stream),
+            "prep": prep,
+            "gate_up": lambda: C.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets,
+                                                      buf.sorted_pairs, T, K, H, buf.ws, stream),
+            "down": lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K,
+                                                buf.y_sorted, buf.ws, stream),
+            "combine": combine,
+        }
+
+    def queue_step(layers):
+        for li, layer in enumerate(layers):
+            c = stage_calls(layer, li)
+            if separate:
+                c["prep"]()
+                c["route_bucket"]()
+            else:
+                c["route_bucket_prep"]()
+            c["gate_up"]()
+            c["down"]()
+            c["combine"]()
+
+    for s in range(warmup):
+        queue_step(step_layers[s % len(step_layers)])
+    torch.cuda.synchronize()
+    plan = [step_layers[(warmup + s) % len(step_layers)] for s in range(steps)]
+
+    # ---- timed region: the K steps as one graph, replayed once
+    graph = hip.instantiate(hip.capture(hs, lambda: [queue_step(p) for p in plan]))
+    hip.launch(graph, hs)                       # one untimed replay
+    torch.cuda.synchronize()
+    gpu_ms, wall_ms = hip.timed_replay(graph, hs, torch.cuda.synchronize)
+    ms_per_step = gpu_ms / steps
+
+    # ---- the dominant kernel alone: the gate/up stage call R times back to
+    # back (the same routing and buffers, the layers of the step plan in
+    # turn, so the weights stream from HBM as in the steps) between two
+    # events on the launch stream; the event cost spreads over R
+    gu_calls = [stage_calls(layers[li], li)["gate_up"] for layers in plan
+                for li in range(len(layers))]
+    reps_gu = max(20, len(gu_calls))
+    gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
+    gu_graph = hip.instantiate(hip.capture(hs, lambda: [c() for c in gu_seq]))
+    hip.launch(gu_graph, hs)                    # warm
+    gu_ms, _ = hip.timed_replay(gu_graph, hs, torch.cuda.synchronize)
+    gu_us = 1e3 * gu_ms / reps_gu
+
+    stage_avg_us = None
+    if stages:
+        calls = []
+        for layers in plan:
+            for li, layer in enumerate(layers):
+                c = stage_calls(layer, li)
+                calls += [c[n] for n in stage_names]
+        bounds = [hip.event() for _ in range(len(calls) + 1)]
+        tg = hip.timed_chain(hs, calls, bounds)
+        hip.launch(tg, hs)
+        torch.cuda.synchronize()
+        ms = {n: [] for n in stage_names}
+        for j in range(len(calls)):
+            ms[stage_names[j % len(stage_names)]].append(hip.elapsed(bounds[j], bounds[j + 1]))
+        stage_avg_us = {n: 1e3 * float(np.mean(v)) for n, v in ms.items()}
+        hip.h.hipGraphExecDestroy(tg)
+
+    # ---- work done per step (realised routing)
+    counts = np.diff(buf.expert_offsets.cpu().numpy())
+    U_last = int((counts > 0).sum())            # the routing the gate/up launches ran on
+    if n_layers > 1:
+        U_total = 0
+        for li, layer in enumerate(step_layers[0]):
+            stage_calls(layer, li)["route_bucket_prep"]()
+            torch.cuda.synchronize()
+            U_total += int((np.diff(buf.expert_offsets.cpu().numpy()) > 0).sum())
+    else:
+        U_total = U_last
+    P = T * K
+    per_exp = expert_bytes_per_expert(H, I, fmt)
+    gu_w_bytes = 2 * proj_bytes(H, I, fmt)
+    step_s = ms_per_step / 1e3
+    gate_up_alg_bytes = gu_w_bytes * U_last + T * H * 2 + P * I * 2     # per launch
+    gu_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9
+    gu_flops = 2.0 * P * 2 * I * H
+    gu_tflops = gu_flops / (gu_us * 1e-6) / 1e12
+    expert_flops = 2.0 * P * 3 * I * H * n_layers
+    prefill = workload in (2, 4)
+    res = {
+        "workload": name, "tokens": T, "layers": n_layers, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "ms_per_step_wall": wall_ms / steps,
+        "tokens_per_s": T / step_s,
+        "active_experts": U_total,
+        "expert_weight_GBps": per_exp * U_total / step_s / 1e9,
+        "layer_alg_GBps": (per_exp * U_total + n_layers * ((E * H + H + E) * 2 + 2 * T * H * 2))
+                          / step_s / 1e9,
+        "expert_TFLOPs": expert_flops / step_s / 1e12,
+        "max_over_mean_bucket": float(counts.max() / max(counts.mean(), 1e-9)),
+        "weight_replicas": replicas, "setup_s": t_setup,
+        "gate_up_kernel": gate_up_kernel_name(T, K, E, fmt), "gate_up_us": gu_us,
+        "gate_up_GBps": gu_gbps, "gate_up_TFLOPs": gu_tflops,
+        "gate_up_frac": gu_tflops / F16_MFMA_PEAK_TFLOPS if prefill else gu_gbps / HBM_PEAK_GBPS,
+        "gate_up_bound": "mfma" if prefill else "hbm",
+        "_gate_up_alg_bytes": gate_up_alg_bytes, "_gate_up_flops": gu_flops,
+        "_U_last": U_last,
+    }
+    if stage_avg_us is not None:
+        res["stage_avg_us_with_event_nodes"] = stage_avg_us
+    for g in (graph, gu_graph):
+        hip.h.hipGraphExecDestroy(g)
+    return res
+
+
+def roofline(res, workload):
+    """The dominant kernel's roofline: the HBM one for decode (its algorithmic
+    bytes: the active experts' gate and up tensors, the f16 activations and
+    A written), the f16 MFMA one for prefill (its algorithmic flops
+    2 P 2 I H); the other one beside it."""
+    T, K, I, H = res["tokens"], 8, 704, 2816
+    traffic = profiled_traffic(res["workload"], res["gate_up_kernel"])
+    U, P = res["_U_last"], T * K
+    w_bytes = res["_gate_up_alg_bytes"] - T * H * 2 - P * I * 2
+    hbm = {"kernel": res["gate_up_kernel"], "bound": "hbm", "achieved": res["gate_up_GBps"],
+           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": res["gate_up_GBps"] / HBM_PEAK_GBPS,
+           "traffic": traffic, "alg_bytes_per_launch": res["_gate_up_alg_bytes"],
+           "avg_launch_us": res["gate_up_us"],
+           "units": f"{U} active experts x {w_bytes // max(U, 1)} B + {T} x {H} x 2 B + "
+                    f"{P} x {I} x 2 B"}
+    mfma = {"kernel": res["gate_up_kernel"], "bound": "mfma", "achieved": res["gate_up_TFLOPs"],
+            "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": res["gate_up_TFLOPs"] / F16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+            "alg_flops_per_launch": res["_gate_up_flops"], "avg_launch_us": res["gate_up_us"],
+            "units": f"2 x {P} rows x 2 x {I} x {H}"}
+    return (mfma, hbm) if workload in (2, 4) else (hbm, mfma)
+
+
+DTYPES = {"nvfp4": "nvfp4 weights (e2m1 x e4m3 x fp32) x bf16 activations; f16 MFMA, fp32 accumulate",
+          "q4_0": "int4 q4_0 weights ((q - 8) x fp16 d per 32) x bf16 activations; f16 MFMA",
+          "aff4": "int4 affine weights (q x fp16 s + fp16 b per 32) x bf16 activations; f16 MFMA"}
+DATA = {"nvfp4": "synthetic (seeded; bf16 N(0,0.02) experts quantised to NVFP4 on the GPU)",
+        "q4_0": "synthetic (seeded; uniform int4 codes, fp16 d ~ U(0.004, 0.008))",
+        "aff4": "synthetic (seeded; uniform int4 codes, fp16 s ~ U(0.004, 0.008), "
+                "b ~ U(-0.06, -0.035))"}
+
+
+def public(res):
+    return {k: v for k, v in res.items() if not k.startswith("_")}
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
+              "multi-GPU path is described, not implemented.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_synth as S
+    import nvfp4_weight_only_moe_amd as moe
+
+    torch.cuda.set_device(0)
+    moe.lib()
+    B = Bench(args)
+    suffix = "" if args.format == "nvfp4" else f"_{args.format}"
+    if args.workload is None:
+        runs = list(ALL_RUNS)
+    elif args.workload == 3:
+        runs = [(3, args.sweep_T)]
+    else:
+        runs = [(args.workload, args.tokens or S.WORKLOADS[args.workload]["T"][0])]
+    results = []
+    for workload, T in runs:
+        steps, warmup = step_defaults(workload, args.steps, args.warmup)
+        name = S.WORKLOADS[workload]["name"]
+        if workload == 3:
+            name = f"moe_30layer_decode_sweep_T{T}" + ("_chained" if args.chain else "")
+        elif T != S.WORKLOADS[workload]["T"][0]:
+            name = re.sub(r"_T\d+", f"_T{T}", name)
+        res = run_workload(B, workload, T, steps, warmup, stages=args.stages and not results,
+                           chain=args.chain and workload == 3, name=name + suffix)
+        results.append((workload, res))
+        print(f"# {res['workload']}: {res['ms_per_step'] * 1e3:.1f} us/step "
+              f"({res['tokens_per_s']:.0f} tok/s), gate/up {res['gate_up_us']:.1f} us "
+              f"frac {res['gate_up_frac']:.3f}", file=sys.stderr, flush=True)
+    head_w, head = results[0]
+    rl, rl_other = roofline(head, head_w)
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s" if head_w != 3 else "tokens/s (30-layer sweep)",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPES[args.format],
+        "data": DATA[args.format],
+        "config": {"workload": head["workload"], "tokens": head["tokens"], "hidden": B.H,
+                   "experts": B.E, "top_k": B.K, "moe_intermediate": B.I,
+                   "layers": head["layers"], "weight_replicas": head["weight_replicas"],
+                   "timing": "hip_graph (one stream); GPU time by HIP events around the replay"},
+        "detail": {"headline": public(head),
+                   "workloads": {r["workload"]: public(r) for _, r in results[1:]}},
+        "roofline": rl,
+        ("roofline_hbm" if rl["bound"] == "mfma" else "roofline_mfma"): rl_other,
+    }
+    if not args.no_cpu_baseline and head_w != 3:
+        out["cpu_baseline"] = cpu_baseline(args, S.WORKLOADS[head_w], head_w, head["tokens"])
+    print(json.dumps(out), flush=True)
 
 
 def copy_reference(mib):
@@ -556,10 +575,11 @@ def copy_reference(mib):
     print(json.dumps({"copy_reference_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(args, wl, T):
-    """The fp64 oracle as it stands, single-threaded, on a bounded sample of
-    the same workload: the block for the first n tokens (expert weights
-    quantised by the oracle itself beforehand, untimed)."""
+def cpu_baseline(args, wl, workload, T):
+    """The fp64 oracle as it stands on a bounded sample of the same workload:
+    the block for the first n tokens (expert weights quantised by the oracle
+    itself beforehand, untimed), its BLAS calls on every core of the
+    process's affinity set."""
     from threadpoolctl import threadpool_limits
     import moe_synth as S
     from oracle import formats as F
@@ -568,14 +588,14 @@ def cpu_baseline(args, wl, T):
     from oracle.quantize import quantize
     from concurrent.futures import ThreadPoolExecutor
 
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
     n = min(T, args.cpu_sample_tokens)
     p = S.router_params(0, zipf=wl["zipf"])
     r = dict(w_router=F.bf16_bits_to_f64(p["w_router"]), scale=F.bf16_bits_to_f64(p["scale"]),
              per_expert_scale=F.bf16_bits_to_f64(p["per_expert_scale"]), bias=p["bias"])
-    x = F.bf16_bits_to_f64(S.activations(args.workload, T, outliers=wl["outliers"]))[:n]
+    x = F.bf16_bits_to_f64(S.activations(workload, T, outliers=wl["outliers"]))[:n]
     ids = M.route(x, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])["idx"]
     todo = [(proj, int(e)) for e in np.unique(ids) for proj in (S.GATE, S.UP, S.DOWN)]
-
     fmt = args.format
 
     def q(item):
@@ -584,31 +604,32 @@ def cpu_baseline(args, wl, T):
             return item, S.int4_expert(fmt, 0, proj, e)
         return item, quantize(F.bf16_bits_to_f64(S.expert_weight(0, proj, e)))
 
-    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+    with ThreadPoolExecutor(cores) as ex:
         packed = dict(ex.map(q, todo))                    # weight preparation, untimed
 
     def decode(item):
         if fmt == "nvfp4":
             return F.dequantize(*packed[item])
-        p, sb = packed[item]
+        pk, sb = packed[item]
         bits = sb.view(np.uint16)
         if fmt == "q4_0":
-            return Q.decode_q4_0(p, bits)
-        return Q.decode_aff4(p, bits.reshape(bits.shape[0], -1, 2))
+            return Q.decode_q4_0(pk, bits)
+        return Q.decode_aff4(pk, bits.reshape(bits.shape[0], -1, 2))
     fn = {proj: (lambda e, proj=proj: decode((proj, e))) for proj in (S.GATE, S.UP, S.DOWN)}
     # the same block again until at least 10 s have been timed (the expert
     # decode, not the token count, dominates one run)
     runs, dt = 0, 0.0
-    with threadpool_limits(1):
+    with threadpool_limits(cores):
         while runs == 0 or (dt < 10.0 and runs < 8):
             t0 = time.perf_counter()
             M.moe_block(x, x, r, fn[S.GATE], fn[S.UP], fn[S.DOWN], k=8)
             dt += time.perf_counter() - t0
             runs += 1
-    return {"value": n * runs / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": n * runs / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of the {T} tokens of {wl['name']} through the fp64 oracle block "
                       f"(route, bucket, {fmt} decode of the {len(todo) // 3} touched experts, "
-                      f"expert MLPs, combine), {runs} run(s) in {dt:.1f} s"}
+                      f"expert MLPs, combine), {runs} run(s) in {dt:.1f} s; BLAS on {cores} "
+                      f"threads, the numpy expert decode single-threaded"}
 
 
 if __name__ == "__main__":

@@ -128,8 +128,10 @@ typedef struct {
  *                                  ties on the logit go to the lower id
  *   topk_w    out [T][top_k] float routing weights (renormalised x pes)
  *   topk_w_raw out [T][top_k] float or NULL: renormalised weights before pes
- *   logits    out [T][E] float     required: the logits (also the scratch
- *                                  between the projection and the selection)
+ *   logits    out [T][E] float or NULL: the logits.  With NULL they never
+ *                                  leave the chip: one workgroup per 64
+ *                                  tokens computes every expert's logit into
+ *                                  LDS and selects there (no scratch memory).
  * Arithmetic: the logits accumulate in fp32 with no rounding of the
  * normalised activation (the per-token 1/rms factor is applied to the dot
  * product); softmax and renormalisation in fp32.
@@ -155,7 +157,8 @@ int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *route
  *   workspace       >= moe_bucket_workspace_bytes(T, top_k, E) bytes; its
  *                   first int32 is the device error word: the number of pairs
  *                   whose id was outside [0, E).  Such pairs are placed after
- *                   every bucket (positions >= off[E]) and go to no expert.
+ *                   every bucket (positions >= off[E]), go to no expert and
+ *                   get pair_rank -1, so moe_combine adds nothing for them.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k <= 0, E <= 0),
  * MOE_ERR_UNSUPPORTED (E > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOPK),
  * MOE_ERR_WORKSPACE.
@@ -169,7 +172,8 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  * moe_route_bucket -- moe_route followed by moe_bucket in one call, with the
  * same arguments as the two calls and the same output bytes (topk_idx,
  * topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs, pair_rank and the
- * workspace error word).  For decode batches (T <= 64, H <= 4096) the top-k
+ * workspace error word; logits may be NULL as in moe_route, which then runs
+ * as moe_route + moe_bucket).  For decode batches (T <= 64, H <= 4096) the top-k
  * selection and the bucketing run in one kernel after the logits kernel,
  * which saves a launch on the latency-bound decode path: one wave per token
  * over ceil(T/4) workgroups, the last of which to finish does the bucketing
@@ -222,6 +226,12 @@ int moe_route_bucket_prep(const uint16_t *x, const uint16_t *w_router,
  *                                alias the router's x)
  *   gate, up       nvfp4_tensor  N = I, K = H, MOE_LAYOUT_TILED
  *   down           nvfp4_tensor  N = H, K = I, MOE_LAYOUT_TILED
+ *                  (the expert kernels read the tiled layout only: a stack
+ *                  in the canonical layout is rejected and is converted once
+ *                  by nvfp4_repack, a pure permutation of its bytes checked
+ *                  bit-exact by nvfp4_dequant_bf16.  Repacking per call would
+ *                  read and write the whole stack -- 428 MB for a model layer
+ *                  -- for every batch.)
  *   expert_offsets [E+1], sorted_pairs [T*top_k]  from moe_bucket
  *   y_sorted       out [T*top_k][H] bf16  expert output of the pair at each
  *                                sorted position (routing weight not applied)
@@ -290,15 +300,15 @@ int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pa
                 int32_t top_k, int32_t H, uint16_t *out, void *stream);
 
 /*
- * The learned norms around the sparse branch ("Gemma 4 26B-A4B (MoE) - Core
- * AI", Architecture code sketch: the experts read
- * pre_feedforward_layernorm_2(residual); the weighted sum passes through
- * post_feedforward_layernorm_2; the layer then adds the residual and scales
- * by layer_scalar).  Each norm is an RMSNorm with a multiplicative weight:
+ * The learned norms of the layer ("Gemma 4 26B-A4B (MoE) - Core AI",
+ * Architecture code sketch):
+ *     h2 = experts(pre_feedforward_layernorm_2(residual), idx)
+ *     h2 = post_feedforward_layernorm_2(sum_k w_k h2_k)
+ *     x  = (residual + post_feedforward_layernorm(h1 + h2)) * layer_scalar
+ * where h1 is the output of the layer's dense branch (outside the block).
+ * Each norm is an RMSNorm with a multiplicative weight:
  *   rmsnorm(v) = v / sqrt(mean(v^2) + eps) * norm_weight     (fp32)
  * (a checkpoint that stores the weight as an offset from 1 passes 1 + w).
- * The layer's dense MLP and its outer post_feedforward_layernorm are outside
- * the block.
  *
  * nvfp4_expert_prep_rmsnorm -- nvfp4_expert_prep with x_expert =
  * rmsnorm(x): the norm is computed from the bf16 row of x in fp32 and feeds
@@ -306,7 +316,7 @@ int moe_combine(const uint16_t *y_sorted, const float *topk_w, const int32_t *pa
  * normed row).  Queue it in place of nvfp4_expert_prep, before
  * nvfp4_expert_gate_up, with the same workspace and shape arguments.
  *   x            [T][H] bf16 (the raw residual; the router reads the same x)
- *   norm_weight  [H] bf16
+ *   norm_weight  [H] bf16 (pre_feedforward_layernorm_2)
  * Errors: those of nvfp4_expert_prep; MOE_ERR_NULL (norm_weight);
  * MOE_ERR_SHAPE (eps < 0 or NaN).
  */
@@ -315,18 +325,28 @@ int nvfp4_expert_prep_rmsnorm(const uint16_t *x, const uint16_t *norm_weight, fl
                               size_t ws_bytes, void *stream);
 
 /*
- * moe_combine_rmsnorm -- moe_combine followed by the post norm, the residual
- * add and the layer scalar:
- *   s = sum_j topk_w[t][j] * y_sorted[pair_rank[t*top_k+j]]   (fp32, j order)
- *   out[t] = (residual[t] + rmsnorm(s)) * layer_scalar         (one bf16 rounding)
- *   norm_weight  [H] bf16
- *   residual     [T][H] bf16, or NULL for none; out may be the same buffer
- *                (each element is read before it is written, by one thread)
- * Errors: as moe_combine; MOE_ERR_NULL (norm_weight); MOE_ERR_SHAPE (eps < 0
- * or NaN); MOE_ERR_UNSUPPORTED (H > 8192).
+ * moe_combine_rmsnorm -- moe_combine followed by the norms of the layer step:
+ *   s  = sum_j topk_w[t][j] * y_sorted[pair_rank[t*top_k+j]]   (fp32, j order)
+ *   h2 = rmsnorm(s, post_norm2_weight)                          (fp32)
+ *   with post_norm_weight:
+ *     out[t] = (residual[t] + rmsnorm(h1[t] + h2, post_norm_weight))
+ *              * layer_scalar                                   (one bf16 rounding)
+ *   without (NULL): out[t] = h2 (the sparse branch's output, one bf16
+ *     rounding; h1 and residual must then be NULL, layer_scalar is unused)
+ *   post_norm2_weight  [H] bf16 (post_feedforward_layernorm_2)
+ *   h1                 [T][H] bf16 or NULL (zero): the dense branch's output
+ *   post_norm_weight   [H] bf16 or NULL (post_feedforward_layernorm)
+ *   residual           [T][H] bf16, required with post_norm_weight
+ *   out                [T][H] bf16; may be the same buffer as residual or h1
+ *                      (each element is read before it is written, by one
+ *                      thread)
+ * Errors: as moe_combine; MOE_ERR_NULL (post_norm2_weight, or residual with
+ * post_norm_weight); MOE_ERR_SHAPE (eps < 0 or NaN; h1 or residual without
+ * post_norm_weight); MOE_ERR_UNSUPPORTED (H > 8192).
  */
 int moe_combine_rmsnorm(const uint16_t *y_sorted, const float *topk_w, const int32_t *pair_rank,
-                        const uint16_t *norm_weight, float eps, const uint16_t *residual,
+                        const uint16_t *post_norm2_weight, const uint16_t *h1,
+                        const uint16_t *post_norm_weight, const uint16_t *residual, float eps,
                         float layer_scalar, int32_t T, int32_t top_k, int32_t H, uint16_t *out,
                         void *stream);
 
@@ -385,7 +405,8 @@ int moe_dequant_f16(const nvfp4_tensor *w, int32_t e, uint16_t *out, void *strea
 /* Text of a status code (static storage). */
 const char *moe_status_str(int status);
 
-/* ABI version of this header: (major << 16) | minor (2.1: moe_route_bucket_prep). */
+/* ABI version of this header: (major << 16) | minor (3.0: moe_combine_rmsnorm takes the
+ * layer step's h1 and outer norm; moe_route's logits may be NULL). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -76,8 +76,8 @@ def lib(path=None):
         "moe_combine": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "nvfp4_expert_prep_rmsnorm": (ctypes.c_int, [vp, vp, f32, i32, i32, i32, i32, i32, vp, sz,
                                                      vp]),
-        "moe_combine_rmsnorm": (ctypes.c_int, [vp, vp, vp, vp, f32, vp, f32, i32, i32, i32, vp,
-                                               vp]),
+        "moe_combine_rmsnorm": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32,
+                                               vp, vp]),
         "nvfp4_quantize": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_repack": (ctypes.c_int, [P, vp, vp, vp]),
         "nvfp4_dequant_bf16": (ctypes.c_int, [P, i32, vp, vp]),
@@ -319,18 +319,21 @@ def moe_combine(y_sorted, topk_w, pair_rank, out, stream=None):
     _check("moe_combine", st)
 
 
-def moe_combine_rmsnorm(y_sorted, topk_w, pair_rank, norm_weight, eps, out, residual=None,
-                        layer_scalar=1.0, stream=None):
-    """out = (residual + rmsnorm(sum_j w_j y_j)) * layer_scalar (residual optional)."""
+def moe_combine_rmsnorm(y_sorted, topk_w, pair_rank, post_norm2, eps, out, h1=None,
+                        post_norm=None, residual=None, layer_scalar=1.0, stream=None):
+    """h2 = rmsnorm(sum_j w_j y_j, post_norm2); with post_norm:
+    out = (residual + rmsnorm(h1 + h2, post_norm)) * layer_scalar (h1 None:
+    zero), else out = h2."""
     T, top_k = topk_w.shape
     H = out.shape[1]
-    res = None if residual is None else _ptr(residual, _B16, (T, H), "residual")
+    opt = lambda t, n: None if t is None else _ptr(t, _B16, (T, H), n)
     st = lib().moe_combine_rmsnorm(_ptr(y_sorted, _B16, (T * top_k, H), "y_sorted"),
                                    _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
                                    _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"),
-                                   _ptr(norm_weight, _B16, (H,), "norm_weight"), float(eps), res,
-                                   float(layer_scalar), T, top_k, H, _ptr(out, _B16, (T, H), "out"),
-                                   _stream(stream))
+                                   _ptr(post_norm2, _B16, (H,), "post_norm2"), opt(h1, "h1"),
+                                   _ptr(post_norm, _B16, (H,), "post_norm"),
+                                   opt(residual, "residual"), float(eps), float(layer_scalar), T,
+                                   top_k, H, _ptr(out, _B16, (T, H), "out"), _stream(stream))
     _check("moe_combine_rmsnorm", st)
 
 

@@ -123,29 +123,33 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
 
 @dataclass
 class BranchNorms:
-    """The learned norms around the sparse branch and the layer's residual
-    step ("Gemma 4 26B-A4B (MoE) - Core AI", Architecture sketch)."""
-    pre: torch.Tensor               # [H] bf16, pre_feedforward_layernorm_2 weight
-    post: torch.Tensor              # [H] bf16, post_feedforward_layernorm_2 weight
+    """The learned norms of the layer step around the sparse branch ("Gemma 4
+    26B-A4B (MoE) - Core AI", Architecture sketch) and its layer scalar."""
+    pre2: torch.Tensor                    # [H] bf16, pre_feedforward_layernorm_2
+    post2: torch.Tensor                   # [H] bf16, post_feedforward_layernorm_2
+    post: Optional[torch.Tensor] = None   # [H] bf16, post_feedforward_layernorm (None: h2 only)
     eps: float = 1e-6
     layer_scalar: float = 1.0
-    add_residual: bool = True
 
 
-def forward_branch(layer: MoeLayer, residual, buf: MoeBuffers, norms: BranchNorms, stream=None):
-    """The sparse branch with its norms: the router reads the raw residual, the
-    experts read rmsnorm(residual, pre), and buf.out = (residual +
-    rmsnorm(sum_k w_k y_k, post)) * layer_scalar (no residual when
-    ``norms.add_residual`` is false)."""
+def forward_branch(layer: MoeLayer, residual, buf: MoeBuffers, norms: BranchNorms, h1=None,
+                   stream=None):
+    """The sparse branch with its norms and the layer step: the router reads
+    the raw residual, the experts read rmsnorm(residual, pre2), h2 =
+    rmsnorm(sum_k w_k y_k, post2), and buf.out = (residual + rmsnorm(h1 + h2,
+    post)) * layer_scalar (h1: the dense branch's output, None for zero).
+    Without ``norms.post`` buf.out is h2."""
     _lib.moe_route_bucket_prep(residual, layer.w_router, layer.router_scale,
                                layer.per_expert_scale, layer.logit_bias, layer.top_k, layer.eps,
                                buf.topk_idx, buf.topk_w, buf.topk_w_raw, buf.logits,
                                buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.bucket_ws,
-                               norms.pre, norms.eps, layer.I, buf.ws, stream)
+                               norms.pre2, norms.eps, layer.I, buf.ws, stream)
     _lib.nvfp4_expert_gate_up(layer.gate, layer.up, buf.expert_offsets, buf.sorted_pairs, buf.T,
                               layer.top_k, layer.H, buf.ws, stream)
     _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,
                            buf.ws, stream)
-    _lib.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank, norms.post, norms.eps,
-                             buf.out, residual if norms.add_residual else None,
-                             norms.layer_scalar, stream)
+    step = norms.post is not None
+    _lib.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank, norms.post2, norms.eps,
+                             buf.out, h1=h1 if step else None, post_norm=norms.post,
+                             residual=residual if step else None,
+                             layer_scalar=norms.layer_scalar, stream=stream)

@@ -4,7 +4,8 @@
 //
 // Order is (expert, token, slot), i.e. by expert and then by pair id
 // p = t*top_k + j.  Pairs with an id outside [0, E) go to an extra bucket E
-// placed after all experts and are counted in the error word.
+// placed after all experts, are counted in the error word and get rank -1
+// (so the combine adds nothing for them).
 //
 // Up to kSmallP pairs: one workgroup does everything (LDS histogram, scan,
 // stable scatter).  Beyond that, in chunks of kChunk pairs: (1) per-chunk
@@ -58,7 +59,7 @@ __device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_
       pos += rank_w;
       const int p = pbase + i;
       sorted[pos] = p;
-      rank[p] = pos;
+      rank[p] = b == nb - 1 ? -1 : pos;  // the invalid bucket: no rank, no expert
     }
     __syncthreads();
     for (int bb = tid; bb < nb; bb += THREADS) {

@@ -186,12 +186,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b, co
 // A row whose largest magnitude is M gets the factor 2^(14 - floor(log2 M)),
 // putting M in [2^14, 2^15): every bf16 value down to M * 2^-29 converts to
 // f16 exactly and nothing overflows.  The returned exponent is what the fp32
-// sums are multiplied back by (2^(expo - 14)).
+// sums are multiplied back by (2^(expo - 14)).  It is clamped at -110, so the
+// factor stays finite (at most 2^124) for rows below 2^-110: their values
+// then land below the f16 range's top and the smallest underflow to zero.
+constexpr int kMinRowExponent = -110;
 __device__ __forceinline__ int row_exponent(float amax) {
   if (!(amax > 0.0f) || !(amax < __builtin_huge_valf())) return 0;  // zero / non-finite row
   int e;
   (void)__builtin_frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
-  return e - 1;                      // floor(log2 amax)
+  return max(e - 1, kMinRowExponent);  // floor(log2 amax), clamped
 }
 
 // Maximum over the 16 lanes of each DPP row (lanes 16g .. 16g + 15), in every

@@ -23,14 +23,14 @@
 //    power of two are applied to the fp32 sums.
 //    Two kernel families, chosen from host-known shapes only:
 //     - GEMV mode (few rows per expert, decode): every wave is an independent
-//       stream, no LDS staging and no barrier in the K loop; activation
-//       operands come from transposed copies (16-byte chunks [k/8][row]) so a
-//       quarter-wave reads 16 rows of one chunk column.
+//       stream, no LDS staging and no barrier in the K loop; each lane loads
+//       its activation chunks (16 bytes of one row, row-major [row][K]) with
+//       buffer loads straight into MFMA operand registers.
 //     - tiled mode (prefill): 16*MSUB rows per tile staged in LDS per K unit
 //       and shared by the 4 waves, weights streamed once per tile.
-//    Gate/up epilogue: GELU-tanh gating, A rounded to bf16 (stored transposed
-//    in GEMV mode), per-row max|A| by atomicMax on the float bits (an integer
-//    max: order-independent).  Down rescales A to f16 by that maximum's power
+//    Gate/up epilogue: GELU-tanh gating, A rounded to bf16 (row-major
+//    [P][I] in sorted-row order), per-row max|A| by atomicMax on the float
+//    bits (an integer max: order-independent).  Down rescales A to f16 by that maximum's power
 //    of two and writes Y as bf16 in sorted-row order.
 #include "common.h"
 
@@ -907,7 +907,7 @@ int check_common(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I, cons
     return MOE_ERR_UNSUPPORTED;
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
   // buffer-resource offsets are 32-bit: one expert's tensor and the
-  // transposed activations must stay below 2 GiB
+  // activation buffers (x16 [T][H], A [P][I]) must stay below 2 GiB
   if ((long long)H * I / 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long long)(H > I ? H : I) * T * top_k * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < ws_layout(T, top_k, E, H, I).total) return MOE_ERR_WORKSPACE;

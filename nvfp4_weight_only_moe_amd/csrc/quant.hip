@@ -294,4 +294,4 @@ extern "C" const char *moe_status_str(int status) {
   }
 }
 
-extern "C" int moe_abi_version(void) { return (2 << 16) | 1; }
+extern "C" int moe_abi_version(void) { return (3 << 16) | 0; }

@@ -6,17 +6,19 @@
 // renormalise to sum 1 -> x per_expert_scale at the chosen ids.
 //
 // Kernel 1 (logits): the per-token factor 1/rms(x_t) * H^-0.5 is a scalar, so
-//   logit[t][e] = (1/rms_t) H^-0.5 * sum_i x[t][i] * scale[i] * W[e][i].
-// A product of two bf16 values is exact in fp32 (at most 16 significant bits)
-// and splits exactly into hi + lo, both bf16; with it each term x*scale*W is
-// formed exactly by two bf16 MFMAs and summed in fp32 -- the normalised
-// activation is never rounded to bf16.  Two tilings:
-//  * few tokens (T <= 64): the split is taken on the weight side,
-//    scale*W = hi + lo, and x is the MFMA operand as it is; a workgroup owns
-//    16 experts and all tokens, its 8 waves split K and meet in LDS.
-//  * many tokens: the split is taken on the activation side,
-//    x*scale = hi + lo, W is the operand as it is; a workgroup owns 64 tokens
-//    (4 waves x 16) and NF*16 experts per wave, full K.
+//   logit[t][e] = (1/rms_t) H^-0.5 * sum_i x[t][i] * scale[i] * W[e][i],
+// every term formed exactly and summed in fp32 -- the normalised activation
+// is never rounded to bf16.  Two tilings:
+//  * few tokens (T <= 64): plain fp32 FMAs, no LDS.  x*scale*W is a product
+//    of three bf16 values (at most 24 significant bits), exact in fp32.  A
+//    workgroup owns one expert and 16 tokens, each wave 4 of them, the whole
+//    row of scale*W kept in registers.
+//  * many tokens: bf16 MFMAs.  The product of two bf16 values is exact in
+//    fp32 and splits exactly into hi + lo, both bf16: x*scale = hi + lo is
+//    staged in LDS, W is the operand as it is, two MFMAs per term.  A
+//    workgroup owns 64 tokens (4 waves x 16) and EXP experts, full K.  With
+//    no logits buffer the workgroup holds every expert, keeps the logits in
+//    LDS and selects there (kernel 2 folded in).
 //
 // Kernel 2 (select): one wave per token; softmax over all E logits in fp32,
 // k rounds of a wave arg-max (ties to the lower id), renormalisation over the
@@ -165,11 +167,16 @@ constexpr int kWideLd = kWideKC + 8;  // bf16 per LDS row (padding spreads banks
 // T = 512: 232 -> 228 us; T = 2048 unchanged, T = 16384 slower)
 constexpr int kWideExp16Below = 2048;
 
-template <int EXP>
+// SELECT (moe_route without a logits buffer): one workgroup holds every
+// expert (EXP >= E) of its 64 tokens, writes their logits into LDS (over the
+// weight staging area, free after the K loop) instead of memory, and its
+// waves then select for the tokens from there.
+template <int EXP, bool SELECT>
 __global__ __launch_bounds__(256) void k_route_logits_wide(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
-    float eps, float *__restrict__ logits) {
+    float eps, float *__restrict__ logits, const uint16_t *__restrict__ pes, int K,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw) {
   __shared__ __attribute__((aligned(16))) uint16_t s_xh[kWideTok * kWideLd];
   __shared__ __attribute__((aligned(16))) uint16_t s_xl[kWideTok * kWideLd];
   constexpr int NF = EXP / 16;  // 16-expert MFMA column tiles per wave
@@ -258,6 +265,8 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
   }
   __syncthreads();
   const float hs = 1.0f / sqrtf((float)H);
+  static_assert(!SELECT || EXP * kWideLd * 2 >= kWideTok * EXP * 4, "LDS logits fit the W area");
+  float *s_logit = reinterpret_cast<float *>(s_w);  // SELECT: [kWideTok][E]
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int e = e0 + f * 16 + r;
@@ -266,8 +275,16 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = wave * 16 + 4 * g + j, t = t0 + m;
-      if (t < T) logits[(size_t)t * E + e] = acc[f][j] * (1.0f / sqrtf(s_ss[m] / (float)H + eps) * hs) + b;
+      const float v = acc[f][j] * (1.0f / sqrtf(s_ss[m] / (float)H + eps) * hs) + b;
+      if (SELECT) s_logit[m * E + e] = v;
+      else if (t < T) logits[(size_t)t * E + e] = v;
     }
+  }
+  if (SELECT) {
+    __syncthreads();
+    for (int m = wave; m < kWideTok && t0 + m < T; m += 4)
+      select_token_n<(EXP + kWave - 1) / kWave, true>(s_logit + m * E, pes, t0 + m, E, K,
+                                                      topk_idx, topk_w, topk_w_raw);
   }
 }
 
@@ -300,11 +317,23 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
                          float *topk_w, float *topk_w_raw, float *logits, void *stream) {
   using namespace moe;
   if (!w_router || !router_scale || !per_expert_scale) return MOE_ERR_NULL;
-  if (T > 0 && (!x || !topk_idx || !topk_w || !logits)) return MOE_ERR_NULL;
+  if (T > 0 && (!x || !topk_idx || !topk_w)) return MOE_ERR_NULL;
   if (T < 0 || H <= 0 || H % 64 || E <= 0 || top_k <= 0 || top_k > E) return MOE_ERR_SHAPE;
   if (E > MOE_MAX_EXPERTS || E % 16 || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (!logits) {  // logits kept in LDS: one workgroup per 64 tokens holds every expert
+    const dim3 grid(1, (T + kWideTok - 1) / kWideTok);
+#define MOE_ALL(EXP)                                                                            \
+  MOE_LAUNCH((k_route_logits_wide<EXP, true>), grid, dim3(256), 0, s, x, w_router, router_scale, \
+             logit_bias, T, H, E, eps, (float *)nullptr, per_expert_scale, top_k, topk_idx,       \
+             topk_w, topk_w_raw)
+    if (E <= 64) MOE_ALL(64);
+    else if (E <= 128) MOE_ALL(128);
+    else MOE_ALL(256);
+#undef MOE_ALL
+    return MOE_OK;
+  }
   const int nv = (H + 511) / 512;
   if (T <= 64 && nv <= kFewMaxV) {
     switch (nv) {
@@ -318,12 +347,17 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
 #undef MOE_FEW
     }
   } else {
+    const uint16_t *no_pes = nullptr;
+    int32_t *no_idx = nullptr;
+    float *no_w = nullptr;
     if (T < kWideExp16Below)
-      MOE_LAUNCH(k_route_logits_wide<16>, dim3(E / 16, (T + kWideTok - 1) / kWideTok), dim3(256), 0,
-                 s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+      MOE_LAUNCH((k_route_logits_wide<16, false>), dim3(E / 16, (T + kWideTok - 1) / kWideTok),
+                 dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits,
+                 no_pes, 0, no_idx, no_w, no_w);
     else
-      MOE_LAUNCH(k_route_logits_wide<32>, dim3((E + 31) / 32, (T + kWideTok - 1) / kWideTok),
-                 dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits);
+      MOE_LAUNCH((k_route_logits_wide<32, false>), dim3((E + 31) / 32, (T + kWideTok - 1) / kWideTok),
+                 dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits,
+                 no_pes, 0, no_idx, no_w, no_w);
   }
   MOE_LAUNCH(k_route_select, dim3((T + 3) / 4), dim3(256), 0, s, logits, per_expert_scale,
                      T, E, top_k, topk_idx, topk_w, topk_w_raw);
@@ -335,13 +369,12 @@ namespace {
 // the checks of moe_route and moe_bucket, before anything is queued
 int route_bucket_checks(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
                         const uint16_t *per_expert_scale, int32_t T, int32_t H, int32_t E,
-                        int32_t top_k, int32_t *topk_idx, float *topk_w, float *logits,
+                        int32_t top_k, int32_t *topk_idx, float *topk_w,
                         int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
                         void *workspace, size_t ws_bytes) {
   if (!w_router || !router_scale || !per_expert_scale || !expert_offsets || !workspace)
     return MOE_ERR_NULL;
-  if (T > 0 && (!x || !topk_idx || !topk_w || !logits || !sorted_pairs || !pair_rank))
-    return MOE_ERR_NULL;
+  if (T > 0 && (!x || !topk_idx || !topk_w || !sorted_pairs || !pair_rank)) return MOE_ERR_NULL;
   if (T < 0 || H <= 0 || H % 64 || E <= 0 || top_k <= 0 || top_k > E) return MOE_ERR_SHAPE;
   if (E > MOE_MAX_EXPERTS || E % 16 || top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
@@ -349,10 +382,11 @@ int route_bucket_checks(const uint16_t *x, const uint16_t *w_router, const uint1
   return MOE_OK;
 }
 
-// true: the decode path, logits then one selection + bucketing launch
-bool fused_route(int T, int H, int top_k) {
+// true: the decode path, logits (into the caller's buffer) then one
+// selection + bucketing launch
+bool fused_route(int T, int H, int top_k, const float *logits) {
   const int nv = (H + 511) / 512;
-  return T > 0 && T <= kFusedMaxT && nv <= kFewMaxV && T * top_k <= 4096;
+  return logits && T > 0 && T <= kFusedMaxT && nv <= kFewMaxV && T * top_k <= 4096;
 }
 
 int route_bucket_fused(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -390,10 +424,10 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
                                 size_t ws_bytes, void *stream) {
   using namespace moe;
   int st = route_bucket_checks(x, w_router, router_scale, per_expert_scale, T, H, E, top_k,
-                               topk_idx, topk_w, logits, expert_offsets, sorted_pairs, pair_rank,
+                               topk_idx, topk_w, expert_offsets, sorted_pairs, pair_rank,
                                workspace, ws_bytes);
   if (st != MOE_OK) return st;
-  if (!fused_route(T, H, top_k)) {
+  if (!fused_route(T, H, top_k, logits)) {
     // T == 0 included: the offsets are all zero, as moe_bucket writes them
     if (T > 0) {
       st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k,
@@ -417,7 +451,7 @@ extern "C" int moe_route_bucket_prep(
     void *expert_ws, size_t expert_ws_bytes, void *stream) {
   using namespace moe;
   int st = route_bucket_checks(x, w_router, router_scale, per_expert_scale, T, H, E, top_k,
-                               topk_idx, topk_w, logits, expert_offsets, sorted_pairs, pair_rank,
+                               topk_idx, topk_w, expert_offsets, sorted_pairs, pair_rank,
                                bucket_ws, bucket_ws_bytes);
   if (st != MOE_OK) return st;
   if (norm_weight && !(norm_eps >= 0.0f)) return MOE_ERR_SHAPE;
@@ -425,7 +459,7 @@ extern "C" int moe_route_bucket_prep(
   st = expert_prep_buffers(T, top_k, E, H, I, expert_ws, expert_ws_bytes, &pa.x16, &pa.x_exp,
                            &pa.a_max);
   if (st != MOE_OK) return st;
-  if (!fused_route(T, H, top_k)) {
+  if (!fused_route(T, H, top_k, logits)) {
     st = moe_route_bucket(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k,
                           eps, topk_idx, topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs,
                           pair_rank, bucket_ws, bucket_ws_bytes, stream);

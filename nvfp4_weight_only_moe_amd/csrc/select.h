@@ -58,8 +58,10 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // per_expert_scale at the chosen ids.  Lane l holds experts l, l + 64, ...
 // (NPER of them, 64 NPER >= E).  A NaN logit is treated as -inf, so every
 // round finds a candidate and the ids are always distinct and in [0, E).
-template <int NPER>
-__device__ __forceinline__ void select_token_n(const float *__restrict__ logits,
+// The logits row `lrow` (E floats) is in global memory (buffer loads), or in
+// LDS when LDS is true.
+template <int NPER, bool LDS = false>
+__device__ __forceinline__ void select_token_n(const float *__restrict__ lrow,
                                                const uint16_t *__restrict__ pes, int t, int E,
                                                int K, int32_t *__restrict__ topk_idx,
                                                float *__restrict__ topk_w,
@@ -68,14 +70,23 @@ __device__ __forceinline__ void select_token_n(const float *__restrict__ logits,
   t = __builtin_amdgcn_readfirstlane(t);  // one token per wave: uniform
   // unguarded buffer loads (lanes past E read zeros), all in flight at once;
   // per_expert_scale of this lane's experts is loaded up front as well
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4u);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(pes, (uint32_t)E * 2u);
   uint32_t lraw[NPER], praw[NPER];
+  if (LDS) {
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const uint32_t e = lane + i * kWave;
-    lraw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, e * 4u, 0, 0);
-    praw[i] = bload2(rp, e * 2u);
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + i * kWave;
+      lraw[i] = e < E ? __float_as_uint(lrow[e]) : 0u;
+      praw[i] = bload2(rp, (uint32_t)e * 2u);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lrow, (uint32_t)E * 4u);
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const uint32_t e = lane + i * kWave;
+      lraw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, e * 4u, 0, 0);
+      praw[i] = bload2(rp, e * 2u);
+    }
   }
   float v[NPER];
   uint32_t key[NPER];
@@ -142,9 +153,10 @@ __device__ __forceinline__ void select_token(const float *__restrict__ logits,
                                              float *__restrict__ topk_w,
                                              float *__restrict__ topk_w_raw) {
   if (E <= 2 * kWave)
-    select_token_n<2>(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
+    select_token_n<2>(logits + (size_t)t * E, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
   else
-    select_token_n<MOE_MAX_EXPERTS / kWave>(logits, pes, t, E, K, topk_idx, topk_w, topk_w_raw);
+    select_token_n<MOE_MAX_EXPERTS / kWave>(logits + (size_t)t * E, pes, t, E, K, topk_idx, topk_w,
+                                            topk_w_raw);
 }
 
 }  // namespace moe

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for st in (0, -1, -2, -3, -4, -5):
         assert L.moe_status_str(st)
-    assert L.moe_abi_version() >> 16 == 2
+    assert L.moe_abi_version() >> 16 == 3
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -53,8 +53,10 @@ def test_route_rejects(L):
     args = [FAKE, FAKE, FAKE, FAKE, NULL, 4, 2816, 128, 8, 1e-6, FAKE, FAKE, NULL, FAKE, NULL]
     a = list(args); a[0] = NULL
     assert L.moe_route(*a) == -1                      # x NULL with T > 0
-    a = list(args); a[13] = NULL
-    assert L.moe_route(*a) == -1                      # logits required
+    a = list(args); a[11] = NULL
+    assert L.moe_route(*a) == -1                      # topk_w required (logits may be NULL)
+    a = list(args); a[13], a[6] = NULL, 2800
+    assert L.moe_route(*a) == -2                      # checked without logits too
     a = list(args); a[6] = 2800
     assert L.moe_route(*a) == -2                      # H % 64
     a = list(args); a[8] = 129
@@ -153,20 +155,29 @@ def test_combine_quantize_dequant_reject(L):
 
 def test_norm_entry_points_reject(L):
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 17, 2816, FAKE, NULL) == -4        # top_k > 16
-    # moe_combine_rmsnorm(y, w, rank, norm_w, eps, residual, scalar, T, k, H, out, stream)
-    ok = [FAKE, FAKE, FAKE, FAKE, 1e-6, NULL, 1.0, 4, 8, 2816, FAKE, NULL]
+    # moe_combine_rmsnorm(y, w, rank, norm2_w, h1, norm_w, residual, eps, scalar, T, k, H,
+    #                     out, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, 1.0, 4, 8, 2816, FAKE, NULL]
     a = list(ok); a[3] = NULL
-    assert L.moe_combine_rmsnorm(*a) == -1                                      # norm weight
-    a = list(ok); a[4] = -1.0
+    assert L.moe_combine_rmsnorm(*a) == -1                                      # norm2 weight
+    a = list(ok); a[6] = NULL
+    assert L.moe_combine_rmsnorm(*a) == -1                                      # residual for the step
+    a = list(ok); a[5] = NULL
+    assert L.moe_combine_rmsnorm(*a) == -2                                      # h1/residual without the step
+    a = list(ok); a[5], a[6] = NULL, NULL
+    assert L.moe_combine_rmsnorm(*a) == -2                                      # h1 without the step
+    a = list(ok); a[7] = -1.0
     assert L.moe_combine_rmsnorm(*a) == -2                                      # eps < 0
-    a = list(ok); a[4] = float("nan")
+    a = list(ok); a[7] = float("nan")
     assert L.moe_combine_rmsnorm(*a) == -2
-    a = list(ok); a[9] = 8200
+    a = list(ok); a[11] = 8200
     assert L.moe_combine_rmsnorm(*a) == -4                                      # H > 8192
-    a = list(ok); a[9] = 2812
+    a = list(ok); a[11] = 2812
     assert L.moe_combine_rmsnorm(*a) == -2                                      # H % 8
-    a = list(ok); a[8] = 17
+    a = list(ok); a[10] = 17
     assert L.moe_combine_rmsnorm(*a) == -4                                      # top_k > 16
+    a = list(ok); a[9] = 0
+    assert L.moe_combine_rmsnorm(*a) == 0                                       # T = 0: no-op
     # nvfp4_expert_prep_rmsnorm(x, norm_w, eps, T, k, E, H, I, ws, ws_bytes, stream)
     ws = L.moe_workspace_bytes(4, 8, 128, 2816, 704)
     ok = [FAKE, FAKE, 1e-6, 4, 8, 128, 2816, 704, FAKE, ws, NULL]

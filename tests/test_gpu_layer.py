@@ -66,12 +66,22 @@ def _check_block(buf, x_bits, router_p, oe, sample=None, tol=REL_FROB_TOL):
     assert buf.bucket_error_count() == 0
     oe.prefetch(np.unique(gidx))
     # the oracle follows the GPU's choice on flagged near-ties (same set otherwise)
-    ref = M.moe_block(xs[toks], xs[toks], r, oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
-                      ids=gidx.astype(np.int64))["out"]
+    blk = M.moe_block(xs[toks], xs[toks], r, oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
+                      ids=gidx.astype(np.int64))
+    ref = blk["out"]
     got = buf.out.float().cpu().numpy()[toks]
     err = rel_frob(got, ref)
     assert np.all(np.isfinite(got))
     assert err <= tol, err
+    # the expert output rows of these tokens' pairs, each against the oracle's
+    # row of the same (token, slot): GPU rank from pair_rank, oracle rank from
+    # its own bucketing of the sample
+    k = 8
+    gpr = buf.pair_rank.cpu().numpy().reshape(-1, k)[toks].reshape(-1)
+    y_got = buf.y_sorted[torch.from_numpy(gpr.astype(np.int64)).cuda()].float().cpu().numpy()
+    y_ref = blk["y_sorted"][blk["buckets"]["pair_rank"]]
+    assert np.all(np.isfinite(y_got))
+    assert np.max(row_rel(y_got, y_ref)) <= tol
     return err, np.max(row_rel(got, ref))
 
 
@@ -114,36 +124,91 @@ def test_layer_intermediate_T_zipf(layer0_zipf, oracle_experts, T):
     print(f"T={T} zipf rel_frob={err:.3e} rows/active expert={counts.sum() / max(1, (counts > 0).sum()):.1f}")
 
 
-def test_layer_T2048_zipf_sampled(layer0_zipf, oracle_experts):
+@pytest.mark.parametrize("T", [1, 8])
+def test_layer_sweep_shapes_all_tokens(layer0, oracle_experts, T):
+    """The per-layer shapes of the 30-layer decode sweep (T = 1: the split-K
+    down GEMV; T = 8), every token."""
+    x = S.activations(3, T)
+    buf = _run(layer0, x)
+    err, worst_row = _check_block(buf, x, S.router_params(0), oracle_experts)
+    assert worst_row <= 1e-2
+    print(f"T={T} rel_frob={err:.3e} worst_row={worst_row:.3e}")
+
+
+def _check_sorted_rows(buf, ref_blk, rows=None, tol=REL_FROB_TOL):
+    """Every (or the given) sorted expert output row of y_sorted against the
+    oracle's, row by row (same bucketing: the ids are the GPU's)."""
+    got = buf.y_sorted.float().cpu().numpy()
+    ref = ref_blk["y_sorted"]
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(got))
+    worst = float(np.max(row_rel(got, ref)))
+    assert worst <= tol, worst
+    return rel_frob(got, ref), worst
+
+
+def test_layer_T2048_zipf_every_token(layer0_zipf, oracle_experts):
+    """Prefill T = 2048 with Zipf routing: every token of the output and every
+    sorted row of the expert outputs (all 16,384, covering every expert's
+    ragged last row block) against the fp64 oracle."""
     x = S.activations(2, 2048)
     buf = _run(layer0_zipf, x)
     counts = np.diff(buf.expert_offsets.cpu().numpy())
     assert counts.sum() == 2048 * 8
     assert counts.max() > 4 * counts.mean()   # the skew is there
-    sample = np.linspace(0, 2047, 12).astype(int)
-    err, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, sample)
-    print(f"T=2048 rel_frob(sample)={err:.3e} max/mean={counts.max() / counts.mean():.1f}")
+    r = router_f64(S.router_params(0, zipf=True))
+    xs = F.bf16_bits_to_f64(x)
+    ref_r = M.route(xs, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])
+    gidx = buf.topk_idx.cpu().numpy()
+    check_route(gidx, buf.topk_w.cpu().numpy(), buf.topk_w_raw.cpu().numpy(), ref_r,
+                r["per_expert_scale"])
+    oracle_experts.prefetch(range(128))
+    blk = M.moe_block(xs, xs, r, oracle_experts.fn(S.GATE), oracle_experts.fn(S.UP),
+                      oracle_experts.fn(S.DOWN), k=8, ids=gidx.astype(np.int64))
+    assert np.array_equal(buf.expert_offsets.cpu().numpy(), blk["buckets"]["offsets"])
+    assert np.array_equal(buf.sorted_pairs.cpu().numpy(), blk["buckets"]["sorted_pairs"])
+    ey, wy = _check_sorted_rows(buf, blk)
+    got = buf.out.float().cpu().numpy()
+    err = rel_frob(got, blk["out"])
+    worst = float(np.max(row_rel(got, blk["out"])))
+    assert err <= REL_FROB_TOL and worst <= REL_FROB_TOL, (err, worst)
+    print(f"T=2048 all tokens rel_frob={err:.3e} worst_row={worst:.3e}; y_sorted rel_frob={ey:.3e} "
+          f"worst_row={wy:.3e}; max/mean={counts.max() / counts.mean():.1f}")
 
 
-def test_layer_T16384_zipf_outliers_sampled(layer0_zipf, oracle_experts):
+def test_layer_T16384_zipf_outliers(layer0_zipf, oracle_experts):
+    """Long prefill with 1% outlier rows (x20): all 164 outlier tokens and 256
+    other tokens, checked separately (the outliers would otherwise dominate
+    the norm), and their sorted expert rows."""
     x = S.activations(4, 16384, outliers=True)
     buf = _run(layer0_zipf, x)
     out_rows = S.outlier_rows(4, 16384)
-    normal = np.setdiff1d(np.linspace(0, 16383, 10).astype(int), out_rows)
-    e1, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, out_rows[:5])
-    e2, _ = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, normal)
-    print(f"T=16384 outlier rows rel_frob={e1:.3e} normal rows={e2:.3e}")
+    assert len(out_rows) == 164
+    rng = np.random.default_rng(16384)
+    normal = np.sort(rng.choice(np.setdiff1d(np.arange(16384), out_rows), 256, replace=False))
+    e1, w1 = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, out_rows)
+    e2, w2 = _check_block(buf, x, S.router_params(0, zipf=True), oracle_experts, normal)
+    assert w1 <= REL_FROB_TOL and w2 <= REL_FROB_TOL, (w1, w2)
+    print(f"T=16384 outlier rows rel_frob={e1:.3e} worst={w1:.3e}; normal rows={e2:.3e} worst={w2:.3e}")
 
 
-# ------------------------------------- sparse branch with its learned norms
-def _branch_check(layer, x_bits, router_p, oe, T_sample=None, add_residual=True, scalar=0.8):
+# ------------------------- sparse branch with its learned norms, layer step
+def _branch_check(layer, x_bits, router_p, oe, T_sample=None, step=True, with_h1=True,
+                  scalar=0.8, workload=6):
+    """forward_branch against the oracle's sparse_branch ("Gemma 4 26B-A4B
+    (MoE) - Core AI", Architecture code sketch).  Returns the relative error of
+    the output and, for the layer step, of its normed part (out / scalar -
+    residual), which the residual would otherwise dominate."""
     T = x_bits.shape[0]
-    pre, post = S.norm_weights(0)
-    norms = moe.BranchNorms(W.to_device_bf16(pre), W.to_device_bf16(post), 1e-6, scalar,
-                            add_residual)
+    pre2, post2, post = S.norm_weights(0)
+    norms = moe.BranchNorms(W.to_device_bf16(pre2), W.to_device_bf16(post2),
+                            W.to_device_bf16(post) if step else None, 1e-6, scalar)
+    h1_bits = S.dense_branch_output(workload, T) if (step and with_h1) else None
     buf = moe.MoeBuffers(T, layer.H, layer.I, layer.E, layer.top_k)
     x = W.to_device_bf16(x_bits)
-    moe.forward_branch(layer, x, buf, norms)
+    moe.forward_branch(layer, x, buf, norms,
+                       h1=None if h1_bits is None else W.to_device_bf16(h1_bits))
     torch.cuda.synchronize()
     r = router_f64(router_p)
     xs = F.bf16_bits_to_f64(x_bits)
@@ -153,49 +218,60 @@ def _branch_check(layer, x_bits, router_p, oe, T_sample=None, add_residual=True,
     check_route(gidx, buf.topk_w.cpu().numpy()[toks], buf.topk_w_raw.cpu().numpy()[toks], ref_r,
                 r["per_expert_scale"])
     oe.prefetch(np.unique(gidx))
-    ref = M.sparse_branch(xs[toks], r, F.bf16_bits_to_f64(pre), F.bf16_bits_to_f64(post),
-                          oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
-                          ids=gidx.astype(np.int64), layer_scalar=scalar, add_residual=add_residual)
+    f64 = F.bf16_bits_to_f64
+    ref = M.sparse_branch(xs[toks], r, f64(pre2), f64(post2), oe.fn(S.GATE), oe.fn(S.UP),
+                          oe.fn(S.DOWN), k=8, ids=gidx.astype(np.int64),
+                          post_norm=f64(post) if step else None,
+                          h1=None if h1_bits is None else f64(h1_bits)[toks], layer_scalar=scalar)
     got = buf.out.float().cpu().numpy()[toks]
     assert np.all(np.isfinite(got))
-    return rel_frob(got, ref["out"]), rel_frob(got / scalar - (xs[toks] if add_residual else 0.0),
-                                                ref["branch"])
+    if not step:
+        return rel_frob(got, ref["h2"]), None
+    return rel_frob(got, ref["out"]), rel_frob(got / scalar - xs[toks], ref["out"] / scalar - xs[toks])
 
 
 @pytest.mark.parametrize("T", [4, 64])
 def test_branch_with_norms_all_tokens(layer0, oracle_experts, T):
     x = S.activations(6, T)
-    err_out, err_branch = _branch_check(layer0, x, S.router_params(0), oracle_experts)
-    assert err_out <= REL_FROB_TOL, err_out
-    # without the residual the branch itself is the output
-    e2, eb2 = _branch_check(layer0, x, S.router_params(0), oracle_experts, add_residual=False)
-    assert eb2 <= REL_FROB_TOL and e2 <= REL_FROB_TOL, (e2, eb2)
-    print(f"T={T} branch with norms: out {err_out:.3e}, branch alone {eb2:.3e}")
+    err_out, err_part = _branch_check(layer0, x, S.router_params(0), oracle_experts)
+    assert err_out <= REL_FROB_TOL and err_part <= REL_FROB_TOL, (err_out, err_part)
+    # h1 = 0 (no dense branch)
+    e0, p0 = _branch_check(layer0, x, S.router_params(0), oracle_experts, with_h1=False)
+    assert e0 <= REL_FROB_TOL and p0 <= REL_FROB_TOL, (e0, p0)
+    # without the outer norm the output is h2, the sparse branch alone
+    eb, _ = _branch_check(layer0, x, S.router_params(0), oracle_experts, step=False)
+    assert eb <= REL_FROB_TOL, eb
+    print(f"T={T} layer step: out {err_out:.3e}, normed part {err_part:.3e}; h1 = 0 {p0:.3e}; "
+          f"h2 alone {eb:.3e}")
 
 
 def test_branch_with_norms_prefill_sampled(layer0_zipf, oracle_experts):
     x = S.activations(7, 2048)
     sample = np.linspace(0, 2047, 10).astype(int)
-    e, _ = _branch_check(layer0_zipf, x, S.router_params(0, zipf=True), oracle_experts, sample,
-                         add_residual=False)
-    assert e <= REL_FROB_TOL, e
+    e, part = _branch_check(layer0_zipf, x, S.router_params(0, zipf=True), oracle_experts, sample,
+                            workload=7)
+    assert e <= REL_FROB_TOL and part <= REL_FROB_TOL, (e, part)
+    eb, _ = _branch_check(layer0_zipf, x, S.router_params(0, zipf=True), oracle_experts, sample,
+                          step=False)
+    assert eb <= REL_FROB_TOL, eb
 
 
 def test_chained_layers_teacher_forced():
     """Three layers chained through the residual (layer l reads layer l-1's
-    bf16 output), each layer checked against the oracle's sparse branch on
-    the input the GPU actually gave it."""
+    bf16 output; the dense branch absent, h1 = 0), each layer checked against
+    the oracle's layer step on the input the GPU actually gave it."""
     T, scalar = 4, 0.9
     x_bits = S.activations(8, T)
     x = W.to_device_bf16(x_bits)
+    f64 = F.bf16_bits_to_f64
     for l in range(3):
         layer = W.build_layer(l, zipf=False)
-        pre, post = S.norm_weights(l)
-        norms = moe.BranchNorms(W.to_device_bf16(pre), W.to_device_bf16(post), 1e-6, scalar)
+        pre2, post2, post = S.norm_weights(l)
+        norms = moe.BranchNorms(*[W.to_device_bf16(a) for a in (pre2, post2, post)], 1e-6, scalar)
         buf = moe.MoeBuffers(T, layer.H, layer.I, layer.E, layer.top_k)
         moe.forward_branch(layer, x, buf, norms)
         torch.cuda.synchronize()
-        xin = F.bf16_bits_to_f64(x.view(torch.int16).cpu().numpy().view(np.uint16))
+        xin = f64(x.view(torch.int16).cpu().numpy().view(np.uint16))
         r = router_f64(S.router_params(l))
         gidx = buf.topk_idx.cpu().numpy()
         ref_r = M.route(xin, r["w_router"], r["scale"], r["per_expert_scale"], 8, r["bias"])
@@ -203,11 +279,12 @@ def test_chained_layers_teacher_forced():
                     r["per_expert_scale"])
         oe = OracleExperts(l)
         oe.prefetch(np.unique(gidx))
-        ref = M.sparse_branch(xin, r, F.bf16_bits_to_f64(pre), F.bf16_bits_to_f64(post),
-                              oe.fn(S.GATE), oe.fn(S.UP), oe.fn(S.DOWN), k=8,
-                              ids=gidx.astype(np.int64), layer_scalar=scalar)
+        ref = M.sparse_branch(xin, r, f64(pre2), f64(post2), oe.fn(S.GATE), oe.fn(S.UP),
+                              oe.fn(S.DOWN), k=8, ids=gidx.astype(np.int64), post_norm=f64(post),
+                              layer_scalar=scalar)
         got = buf.out.float().cpu().numpy()
         assert rel_frob(got, ref["out"]) <= REL_FROB_TOL
+        assert rel_frob(got / scalar - xin, ref["out"] / scalar - xin) <= REL_FROB_TOL
         x = buf.out.clone()
         del layer
         torch.cuda.empty_cache()
