@@ -259,6 +259,29 @@ int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *gate, const n
 size_t moe_workspace_bytes(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I);
 
 /*
+ * nvfp4_expert_mlp_noalloc -- nvfp4_expert_mlp for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same output bytes.  The workspace is a file-scope device
+ * array of MOE_NOALLOC_MAX_WORKSPACE_BYTES inside the library, one per GPU,
+ * held until the process ends; the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Every call on a GPU shares that GPU's array
+ * and leaves its last contents there, so calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race.
+ * Errors: those of nvfp4_expert_mlp; MOE_ERR_WORKSPACE when
+ * moe_workspace_bytes(T, top_k, E, H, I) exceeds
+ * MOE_NOALLOC_MAX_WORKSPACE_BYTES (at the model's H = 2816, I = 704,
+ * top_k = 8: up to 495 tokens); MOE_ERR_LAUNCH when the array's device
+ * address cannot be looked up.
+ */
+#define MOE_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)8 << 20)
+int nvfp4_expert_mlp_noalloc(const uint16_t *x_expert, const nvfp4_tensor *gate,
+                             const nvfp4_tensor *up, const nvfp4_tensor *down,
+                             const int32_t *expert_offsets, const int32_t *sorted_pairs, int32_t T,
+                             int32_t top_k, int32_t H, int32_t I, uint16_t *y_sorted,
+                             void *stream);
+
+/*
  * The three stages of nvfp4_expert_mlp as separate calls, for callers that
  * want to time or overlap them; queued in this order with the same workspace
  * they give the same bytes as nvfp4_expert_mlp.

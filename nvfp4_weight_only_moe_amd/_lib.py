@@ -17,7 +17,8 @@ MOE_OK = 0
 _ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
            -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_LAUNCH"}
 
-EXPORTED = ("moe_route", "moe_route_bucket", "moe_route_bucket_prep", "moe_bucket", "moe_bucket_workspace_bytes", "nvfp4_expert_mlp",
+EXPORTED = ("moe_route", "moe_route_bucket", "moe_route_bucket_prep", "moe_bucket",
+            "moe_bucket_workspace_bytes", "nvfp4_expert_mlp", "nvfp4_expert_mlp_noalloc",
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
             "moe_workspace_bytes", "moe_combine", "nvfp4_expert_prep_rmsnorm",
             "moe_combine_rmsnorm", "nvfp4_quantize", "nvfp4_repack",
@@ -69,6 +70,8 @@ def lib(path=None):
                                                  vp, vp, vp, vp, vp, vp, sz, vp, f32, i32, vp, sz,
                                                  vp]),
         "nvfp4_expert_mlp": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
+        "nvfp4_expert_mlp_noalloc": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp,
+                                                    vp]),
         "nvfp4_expert_prep": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_gate_up": (ctypes.c_int, [P, P, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_down": (ctypes.c_int, [P, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
@@ -264,6 +267,21 @@ def nvfp4_expert_mlp(x_expert, gate, up, down, expert_offsets, sorted_pairs, top
                                 _ptr(workspace, None, None, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check("nvfp4_expert_mlp", st)
+
+
+def nvfp4_expert_mlp_noalloc(x_expert, gate, up, down, expert_offsets, sorted_pairs, top_k,
+                             y_sorted, stream=None):
+    """nvfp4_expert_mlp on the library's own per-GPU scratch array (no
+    workspace argument, nothing allocated); calls that overlap on one GPU race."""
+    T, H = x_expert.shape
+    I = gate.N
+    cg, cu, cd = gate.c(), up.c(), down.c()
+    st = lib().nvfp4_expert_mlp_noalloc(
+        _ptr(x_expert, _B16, (T, H), "x_expert"), ctypes.byref(cg), ctypes.byref(cu),
+        ctypes.byref(cd), _ptr(expert_offsets, torch.int32, (gate.E + 1,), "expert_offsets"),
+        _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"), T, top_k, H, I,
+        _ptr(y_sorted, _B16, (T * top_k, H), "y_sorted"), _stream(stream))
+    _check("nvfp4_expert_mlp_noalloc", st)
 
 
 def nvfp4_expert_prep(x_expert, E, I, top_k, workspace, stream=None):

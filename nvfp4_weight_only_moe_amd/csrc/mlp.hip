@@ -32,6 +32,8 @@
 //    [P][I] in sorted-row order), per-row max|A| by atomicMax on the float
 //    bits (an integer max: order-independent).  Down rescales A to f16 by that maximum's power
 //    of two and writes Y as bf16 in sorted-row order.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -1132,4 +1134,52 @@ extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *ga
   if (st != MOE_OK) return st;
   return nvfp4_expert_down(down, expert_offsets, T, top_k, H, I, y_sorted, workspace, ws_bytes,
                            stream);
+}
+
+// ---- nvfp4_expert_mlp without a caller workspace -------------------------
+// For callers that cannot allocate device memory: the workspace is a
+// file-scope device array of kStaticScratchBytes, one copy per GPU, which the
+// GPU holds until the process ends.  Its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is handed to kernels; the host-side name of the array is not a
+// device address.  Every call on a GPU shares that GPU's array.
+namespace {
+constexpr size_t kStaticScratchBytes = MOE_NOALLOC_MAX_WORKSPACE_BYTES;
+constexpr int kStaticMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kStaticMaxDevices] = {};
+
+// the device address of this device's scratch array (nullptr on failure)
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int nvfp4_expert_mlp_noalloc(const uint16_t *x_expert, const nvfp4_tensor *gate,
+                                        const nvfp4_tensor *up, const nvfp4_tensor *down,
+                                        const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                        int32_t T, int32_t top_k, int32_t H, int32_t I,
+                                        uint16_t *y_sorted, void *stream) {
+  if (tensor_null(gate) || tensor_null(up) || tensor_null(down) || !expert_offsets)
+    return MOE_ERR_NULL;
+  if (T > 0 && (!x_expert || !sorted_pairs || !y_sorted)) return MOE_ERR_NULL;
+  if (T < 0 || top_k <= 0 || H <= 0 || I <= 0) return MOE_ERR_SHAPE;
+  const int E = gate->E;
+  if (E <= 0) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k > 0x7FFFFFFFLL / 2) return MOE_ERR_SHAPE;
+  const size_t need = moe_workspace_bytes(T, top_k, E, H, I);
+  if (need == 0 || need > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  void *ws = device_scratch();
+  if (!ws) return MOE_ERR_LAUNCH;
+  return nvfp4_expert_mlp(x_expert, gate, up, down, expert_offsets, sorted_pairs, T, top_k, H, I,
+                          y_sorted, ws, kStaticScratchBytes, stream);
 }
