@@ -79,6 +79,9 @@ def parse(argv=None):
                     help="tokens of the workload the fp64 oracle baseline runs")
     ap.add_argument("--stages", action="store_true",
                     help="also time every stage call (a second graph with event nodes)")
+    ap.add_argument("--four-calls", action="store_true",
+                    help="run decode batches through the separate calls instead of "
+                         "moe_layer_decode")
     ap.add_argument("--separate-prep", action="store_true",
                     help="queue moe_route_bucket and the expert-input prep as two calls instead "
                          "of one moe_route_bucket_prep")
@@ -321,7 +324,10 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     t_setup = time.perf_counter() - t_setup
     hs, stream = B.hs, B.stream
     separate = B.args.separate_prep
-    stage_names = SEPARATE_STAGES if separate else STAGES
+    # decode batches run as moe_layer_decode (four launches) unless a
+    # variant asks for the separate calls
+    fused = buf.decode and not (chain or separate or B.args.four_calls)
+    stage_names = ("layer_decode",) if fused else SEPARATE_STAGES if separate else STAGES
 
     def stage_calls(layer, li):
         """The stage calls of one block pass (layer li of the step), by name."""
@@ -355,11 +361,19 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
             "down": lambda: C.nvfp4_expert_down(layer.down, buf.expert_offsets, T, K,
                                                 buf.y_sorted, buf.ws, stream),
             "combine": combine,
+            "layer_decode": lambda: C.moe_layer_decode(
+                x_in, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                layer.logit_bias, K, layer.eps, layer.gate, layer.up, layer.down, buf.topk_idx,
+                buf.topk_w, buf.topk_w_raw, buf.expert_offsets, buf.sorted_pairs, buf.pair_rank,
+                buf.out, buf.layer_ws, stream),
         }
 
     def queue_step(layers):
         for li, layer in enumerate(layers):
             c = stage_calls(layer, li)
+            if fused:
+                c["layer_decode"]()
+                continue
             if separate:
                 c["prep"]()
                 c["route_bucket"]()
@@ -385,14 +399,18 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     # back (the same routing and buffers, the layers of the step plan in
     # turn, so the weights stream from HBM as in the steps) between two
     # events on the launch stream; the event cost spreads over R
-    gu_calls = [stage_calls(layers[li], li)["gate_up"] for layers in plan
-                for li in range(len(layers))]
-    reps_gu = max(20, len(gu_calls))
-    gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
-    gu_graph = hip.instantiate(hip.capture(hs, lambda: [c() for c in gu_seq]))
-    hip.launch(gu_graph, hs)                    # warm
-    gu_ms, _ = hip.timed_replay(gu_graph, hs, torch.cuda.synchronize)
-    gu_us = 1e3 * gu_ms / reps_gu
+    # (the decode path's gate/up kernel has no call of its own: its duration
+    # comes from the kernel trace)
+    gu_us, gu_graph = None, None
+    if not fused:
+        gu_calls = [stage_calls(layers[li], li)["gate_up"] for layers in plan
+                    for li in range(len(layers))]
+        reps_gu = max(20, len(gu_calls))
+        gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
+        gu_graph = hip.instantiate(hip.capture(hs, lambda: [c() for c in gu_seq]))
+        hip.launch(gu_graph, hs)                # warm
+        gu_ms, _ = hip.timed_replay(gu_graph, hs, torch.cuda.synchronize)
+        gu_us = 1e3 * gu_ms / reps_gu
 
     stage_avg_us = None
     if stages:
@@ -417,7 +435,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     if n_layers > 1:
         U_total = 0
         for li, layer in enumerate(step_layers[0]):
-            stage_calls(layer, li)["route_bucket_prep"]()
+            stage_calls(layer, li)["layer_decode" if fused else "route_bucket_prep"]()
             torch.cuda.synchronize()
             U_total += int((np.diff(buf.expert_offsets.cpu().numpy()) > 0).sum())
     else:
@@ -427,9 +445,9 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     gu_w_bytes = 2 * proj_bytes(H, I, fmt)
     step_s = ms_per_step / 1e3
     gate_up_alg_bytes = gu_w_bytes * U_last + T * H * 2 + P * I * 2     # per launch
-    gu_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9
     gu_flops = 2.0 * P * 2 * I * H
-    gu_tflops = gu_flops / (gu_us * 1e-6) / 1e12
+    gu_gbps = gate_up_alg_bytes / (gu_us * 1e-6) / 1e9 if gu_us else None
+    gu_tflops = gu_flops / (gu_us * 1e-6) / 1e12 if gu_us else None
     expert_flops = 2.0 * P * 3 * I * H * n_layers
     prefill = workload in (2, 4)
     res = {
@@ -443,17 +461,23 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
         "expert_TFLOPs": expert_flops / step_s / 1e12,
         "max_over_mean_bucket": float(counts.max() / max(counts.mean(), 1e-9)),
         "weight_replicas": replicas, "setup_s": t_setup,
-        "gate_up_kernel": gate_up_kernel_name(T, K, E, fmt), "gate_up_us": gu_us,
+        "gate_up_kernel": ("k_decode_gate_up (in moe_layer_decode)" if fused else
+                           gate_up_kernel_name(T, K, E, fmt)), "gate_up_us": gu_us,
         "gate_up_GBps": gu_gbps, "gate_up_TFLOPs": gu_tflops,
-        "gate_up_frac": gu_tflops / F16_MFMA_PEAK_TFLOPS if prefill else gu_gbps / HBM_PEAK_GBPS,
+        "gate_up_frac": (None if not gu_us else gu_tflops / F16_MFMA_PEAK_TFLOPS if prefill
+                         else gu_gbps / HBM_PEAK_GBPS),
         "gate_up_bound": "mfma" if prefill else "hbm",
         "_gate_up_alg_bytes": gate_up_alg_bytes, "_gate_up_flops": gu_flops,
         "_U_last": U_last,
     }
     if stage_avg_us is not None:
         res["stage_avg_us_with_event_nodes"] = stage_avg_us
+    res["path"] = ("moe_layer_decode (4 launches)" if fused else
+                   "moe_route_bucket + nvfp4_expert_prep + gate_up + down + combine" if separate else
+                   "moe_route_bucket_prep + nvfp4_expert_gate_up + nvfp4_expert_down + combine")
     for g in (graph, gu_graph):
-        hip.h.hipGraphExecDestroy(g)
+        if g is not None:
+            hip.h.hipGraphExecDestroy(g)
     return res
 
 
@@ -466,15 +490,16 @@ def roofline(res, workload):
     traffic = profiled_traffic(res["workload"], res["gate_up_kernel"])
     U, P = res["_U_last"], T * K
     w_bytes = res["_gate_up_alg_bytes"] - T * H * 2 - P * I * 2
+    frac = lambda v, p: None if v is None else v / p
     hbm = {"kernel": res["gate_up_kernel"], "bound": "hbm", "achieved": res["gate_up_GBps"],
-           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": res["gate_up_GBps"] / HBM_PEAK_GBPS,
+           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": frac(res["gate_up_GBps"], HBM_PEAK_GBPS),
            "traffic": traffic, "alg_bytes_per_launch": res["_gate_up_alg_bytes"],
            "avg_launch_us": res["gate_up_us"],
            "units": f"{U} active experts x {w_bytes // max(U, 1)} B + {T} x {H} x 2 B + "
                     f"{P} x {I} x 2 B"}
     mfma = {"kernel": res["gate_up_kernel"], "bound": "mfma", "achieved": res["gate_up_TFLOPs"],
             "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": res["gate_up_TFLOPs"] / F16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+            "frac": frac(res["gate_up_TFLOPs"], F16_MFMA_PEAK_TFLOPS), "traffic": traffic,
             "alg_flops_per_launch": res["_gate_up_flops"], "avg_launch_us": res["gate_up_us"],
             "units": f"2 x {P} rows x 2 x {I} x {H}"}
     return (mfma, hbm) if workload in (2, 4) else (hbm, mfma)
@@ -527,9 +552,11 @@ def main(argv=None):
         res = run_workload(B, workload, T, steps, warmup, stages=args.stages and not results,
                            chain=args.chain and workload == 3, name=name + suffix)
         results.append((workload, res))
+        gu = ("" if res["gate_up_us"] is None else
+              f", gate/up {res['gate_up_us']:.1f} us frac {res['gate_up_frac']:.3f}")
         print(f"# {res['workload']}: {res['ms_per_step'] * 1e3:.1f} us/step "
-              f"({res['tokens_per_s']:.0f} tok/s), gate/up {res['gate_up_us']:.1f} us "
-              f"frac {res['gate_up_frac']:.3f}", file=sys.stderr, flush=True)
+              f"({res['tokens_per_s']:.0f} tok/s, {res['path']}){gu}", file=sys.stderr,
+              flush=True)
     head_w, head = results[0]
     rl, rl_other = roofline(head, head_w)
     out = {

@@ -216,6 +216,40 @@ int moe_route_bucket_prep(const uint16_t *x, const uint16_t *w_router,
                           void *expert_ws, size_t expert_ws_bytes, void *stream);
 
 /*
+ * moe_layer_decode -- the whole block for a decode batch in one call: the
+ * router, the bucketing, the expert MLP and the weighted combine of
+ * moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine, queued as four
+ * kernels instead of five ("Gemma-4-26B-A4B-IT - UD-Q8KXL (mlx-node)",
+ * Performance: decode gains from fusing the per-layer dispatch):
+ *   1. the router logits, beside the expert input's f16 rows;
+ *   2. the gate/up projection, every workgroup repeating the top-k selection
+ *      of every token and the bucketing in LDS (no kernel of their own);
+ *   3. the down projection; 4. the combine.
+ * Arguments as those calls' (x is also the expert input).  Every output has
+ * the same bytes as the four calls': topk_idx, topk_w, topk_w_raw (NULL
+ * allowed), expert_offsets, sorted_pairs, pair_rank and out.
+ *   gate, up, down  nvfp4_tensor as nvfp4_expert_mlp's (MOE_LAYOUT_TILED)
+ *   out             [T][H] bf16
+ *   workspace       >= moe_layer_decode_workspace_bytes(T, top_k, E, H, I)
+ *                   bytes; its word at byte moe_layer_decode_error_offset is
+ *                   the bucketing's error word (ids outside [0, E))
+ * Limits: T <= MOE_DECODE_MAX_TOKENS, T * top_k <= MOE_DECODE_MAX_PAIRS,
+ * H <= 4096 (MOE_ERR_UNSUPPORTED beyond); the checks of moe_route and
+ * nvfp4_expert_mlp otherwise.  T == 0 queues nothing.
+ */
+#define MOE_DECODE_MAX_TOKENS 8
+#define MOE_DECODE_MAX_PAIRS 64
+int moe_layer_decode(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+                     const uint16_t *per_expert_scale, const float *logit_bias, int32_t T,
+                     int32_t H, int32_t E, int32_t top_k, float eps, const nvfp4_tensor *gate,
+                     const nvfp4_tensor *up, const nvfp4_tensor *down, int32_t I,
+                     int32_t *topk_idx, float *topk_w, float *topk_w_raw,
+                     int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_rank,
+                     uint16_t *out, void *workspace, size_t ws_bytes, void *stream);
+size_t moe_layer_decode_workspace_bytes(int32_t T, int32_t top_k, int32_t E, int32_t H, int32_t I);
+size_t moe_layer_decode_error_offset(int32_t T, int32_t top_k, int32_t E);
+
+/*
  * nvfp4_expert_mlp -- every routed (token, expert) pair through its expert:
  * A = gelu_tanh(X Wg^T) * (X Wu^T), Y = A Wd^T ("Gemma 4 26B-A4B (MoE) -
  * Core AI", Architecture: GELU-gated experts in the tanh form; gate/up

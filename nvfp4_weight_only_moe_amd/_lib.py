@@ -19,12 +19,15 @@ _ERRORS = {-1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_WORKSPACE",
 
 EXPORTED = ("moe_route", "moe_route_bucket", "moe_route_bucket_prep", "moe_bucket",
             "moe_bucket_workspace_bytes", "nvfp4_expert_mlp", "nvfp4_expert_mlp_noalloc",
+            "moe_layer_decode", "moe_layer_decode_workspace_bytes", "moe_layer_decode_error_offset",
             "nvfp4_expert_prep", "nvfp4_expert_gate_up", "nvfp4_expert_down",
             "moe_workspace_bytes", "moe_combine", "nvfp4_expert_prep_rmsnorm",
             "moe_combine_rmsnorm", "nvfp4_quantize", "nvfp4_repack",
             "nvfp4_dequant_bf16", "moe_dequant_f16", "moe_status_str", "moe_abi_version")
 
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+# limits of moe_layer_decode (the three-launch decode path)
+DECODE_MAX_TOKENS, DECODE_MAX_PAIRS, DECODE_MAX_HIDDEN = 8, 64, 4096
 FORMAT_NVFP4, FORMAT_Q4_0, FORMAT_AFF4 = 0, 1, 2
 FORMATS = {"nvfp4": FORMAT_NVFP4, "q4_0": FORMAT_Q4_0, "aff4": FORMAT_AFF4}
 # scale bytes per 32 weights of a row: NVFP4 two E4M3 codes, Q4_0 one fp16 d,
@@ -73,6 +76,10 @@ def lib(path=None):
         "nvfp4_expert_mlp_noalloc": (ctypes.c_int, [vp, P, P, P, vp, vp, i32, i32, i32, i32, vp,
                                                     vp]),
         "nvfp4_expert_prep": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, sz, vp]),
+        "moe_layer_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, P, P, P,
+                                            i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_layer_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "moe_layer_decode_error_offset": (sz, [i32, i32, i32]),
         "nvfp4_expert_gate_up": (ctypes.c_int, [P, P, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
         "nvfp4_expert_down": (ctypes.c_int, [P, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
         "moe_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -248,6 +255,44 @@ def moe_bucket(topk_idx, E, expert_offsets, sorted_pairs, pair_rank, workspace, 
                           _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
                           _stream(stream))
     _check("moe_bucket", st)
+
+
+def moe_layer_decode_workspace_bytes(T, top_k, E, H, I):
+    return int(lib().moe_layer_decode_workspace_bytes(T, top_k, E, H, I))
+
+
+def moe_layer_decode_error_offset(T, top_k, E):
+    return int(lib().moe_layer_decode_error_offset(T, top_k, E))
+
+
+def decode_fits(T, top_k, H):
+    """Whether moe_layer_decode takes this shape."""
+    return 0 < T <= DECODE_MAX_TOKENS and T * top_k <= DECODE_MAX_PAIRS and H <= DECODE_MAX_HIDDEN
+
+
+def moe_layer_decode(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps, gate,
+                     up, down, topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs,
+                     pair_rank, out, workspace, stream=None):
+    """The whole block for a decode batch (T <= 8) in four launches."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = gate.N
+    cg, cu, cd = gate.c(), up.c(), down.c()
+    st = lib().moe_layer_decode(
+        _ptr(x, _B16, (T, H), "x"), _ptr(w_router, _B16, (E, H), "w_router"),
+        _ptr(router_scale, _B16, (H,), "router_scale"),
+        _ptr(per_expert_scale, _B16, (E,), "per_expert_scale"),
+        _ptr(logit_bias, torch.float32, (E,), "logit_bias"), T, H, E, top_k, float(eps),
+        ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd), I,
+        _ptr(topk_idx, torch.int32, (T, top_k), "topk_idx"),
+        _ptr(topk_w, torch.float32, (T, top_k), "topk_w"),
+        _ptr(topk_w_raw, torch.float32, (T, top_k), "topk_w_raw"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(sorted_pairs, torch.int32, (T * top_k,), "sorted_pairs"),
+        _ptr(pair_rank, torch.int32, (T * top_k,), "pair_rank"),
+        _ptr(out, _B16, (T, H), "out"), _ptr(workspace, None, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_layer_decode", st)
 
 
 def moe_workspace_bytes(T, top_k, E, H, I):

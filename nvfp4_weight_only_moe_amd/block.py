@@ -63,21 +63,46 @@ class MoeBuffers:
         self.ws = torch.empty((_lib.moe_workspace_bytes(T, top_k, E, H, I),), dtype=torch.uint8, **kw)
         self.y_sorted = torch.empty((P, H), dtype=torch.bfloat16, **kw)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, **kw)
+        # the three-launch decode path's workspace (small batches only)
+        self.decode = _lib.decode_fits(T, top_k, H)
+        self.layer_ws = None
+        if self.decode:
+            self.layer_ws = torch.empty((_lib.moe_layer_decode_workspace_bytes(T, top_k, E, H, I),),
+                                        dtype=torch.uint8, **kw)
+            self._decode_err = _lib.moe_layer_decode_error_offset(T, top_k, E)
+        self._err_src = self.bucket_ws[:4]
+        self.y_sorted_valid = False  # y_sorted holds the last four-call pass's expert outputs
 
     def bucket_error_count(self):
-        """Pairs whose expert id was out of range in the last moe_bucket."""
-        return int(self.bucket_ws[:4].view(torch.int32)[0].item())
+        """Pairs whose expert id was out of range in the last bucketing."""
+        return int(self._err_src.view(torch.int32)[0].item())
 
 
-def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, marks=None):
+def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, marks=None,
+            fused=None):
     """Queue the whole block for x [T, H] bf16; the result lands in buf.out.
 
-    ``marks`` (optional) is a callable invoked with a stage name between the
-    calls ("route", "bucket", "prep", "gate_up", "down", "combine" after each);
-    with it the expert MLP runs as its three stage calls so that a caller can
-    record timing events around each stage."""
+    Decode batches (T <= 8) run as moe_layer_decode (four launches) unless
+    ``fused`` is False or the experts read another input.  ``marks``
+    (optional) is a callable invoked with a stage name between the calls
+    ("route", "bucket", "prep", "gate_up", "down", "combine" after each); with
+    it the block runs as the separate stage calls so that a caller can record
+    timing events around each stage."""
     xe = x if x_expert is None else x_expert
     mark = marks or (lambda name: None)
+    if fused is None:
+        fused = buf.decode and x_expert is None and marks is None
+    if fused:
+        _lib.moe_layer_decode(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
+                              layer.logit_bias, layer.top_k, layer.eps, layer.gate, layer.up,
+                              layer.down, buf.topk_idx, buf.topk_w, buf.topk_w_raw,
+                              buf.expert_offsets, buf.sorted_pairs, buf.pair_rank, buf.out,
+                              buf.layer_ws, stream)
+        buf._err_src = buf.layer_ws[buf._decode_err:buf._decode_err + 4]
+        buf.y_sorted_valid = False   # the expert outputs are in the call's workspace
+        return buf.out
+    buf._err_src = buf.bucket_ws[:4]
+    buf.y_sorted_valid = True
     if marks is None and x_expert is None:
         # the router and the expert-input prep read the same x: one call
         _lib.moe_route_bucket_prep(x, layer.w_router, layer.router_scale, layer.per_expert_scale,
@@ -148,6 +173,8 @@ def forward_branch(layer: MoeLayer, residual, buf: MoeBuffers, norms: BranchNorm
                               layer.top_k, layer.H, buf.ws, stream)
     _lib.nvfp4_expert_down(layer.down, buf.expert_offsets, buf.T, layer.top_k, buf.y_sorted,
                            buf.ws, stream)
+    buf._err_src = buf.bucket_ws[:4]
+    buf.y_sorted_valid = True
     step = norms.post is not None
     _lib.moe_combine_rmsnorm(buf.y_sorted, buf.topk_w, buf.pair_rank, norms.post2, norms.eps,
                              buf.out, h1=h1 if step else None, post_norm=norms.post,

@@ -16,6 +16,7 @@
 // mask of lanes holding the same bucket; a popcount below the lane is its rank
 // in the wave, per-wave counts in LDS order the waves.  No atomics decide any
 // position, so the output is the same on every run.
+#include "bucket_core.h"
 #include "common.h"
 #include "select.h"
 
@@ -26,9 +27,7 @@ constexpr int kBucketThreads = 256;
 constexpr int kBucketWaves = kBucketThreads / kWave;
 constexpr int kSmallP = 4096;            // up to this many pairs: one workgroup
 constexpr int kChunk = 1024;             // pairs per workgroup beyond that
-constexpr int kMaxB = MOE_MAX_EXPERTS + 1;  // buckets incl. the invalid one
 
-__device__ __forceinline__ int bucket_of(int e, int E) { return (e >= 0 && e < E) ? e : E; }
 
 // Stable scatter of the n bucket ids in s_b (pairs pbase .. pbase+n-1),
 // starting from the per-bucket positions in s_run (updated in place), by a
@@ -78,25 +77,6 @@ __device__ void scatter_rounds(const int *s_b, int n, int pbase, int nb, int *s_
 template <int THREADS = kBucketThreads>
 __device__ void zero_wcnt(int (*s_wcnt)[kMaxB], int nb) {
   for (int i = threadIdx.x; i < THREADS / kWave * nb; i += THREADS) s_wcnt[i / nb][i % nb] = 0;
-}
-
-// Exclusive scan of cnt[0..nb) into out[0..nb) by the first wave (nb <= 257).
-__device__ void wave_exclusive_scan(const int *cnt, int *out, int nb) {
-  const int lane = threadIdx.x;
-  if (lane >= kWave) return;
-  int carry = 0;
-  for (int base = 0; base < nb; base += kWave) {
-    const int i = base + lane;
-    int v = i < nb ? cnt[i] : 0;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += u;
-    }
-    if (i < nb) out[i] = carry + incl - v;
-    carry += __shfl(incl, kWave - 1, kWave);
-  }
 }
 
 // Every step of the bucketing for P <= kSmallP pairs by one workgroup of

@@ -153,6 +153,13 @@ struct WeightFmt<MOE_FORMAT_AFF4> {
 // or beyond `bytes` returns zeros (hardware range check), which is how lanes
 // past the end of a tensor or tile read zeros without a select.
 constexpr uint32_t kOOB = 0x80000000u;  // an offset outside every buffer used here
+// `off` (< 2^31) when ok, else an offset past the buffer (the load returns
+// zeros), without a branch: a select around a load's address can otherwise be
+// compiled into two loads under complementary masks, the second waiting for
+// every load in flight (it rewrites the same registers)
+__device__ __forceinline__ uint32_t off_if(bool ok, uint32_t off) {
+  return off | ((uint32_t)!ok << 31);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -215,6 +222,21 @@ __device__ __forceinline__ uint32_t bf16_abs_bits(uint16_t b) {
   return mag > 0x7F80u ? 0u : mag << 16;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts, then the
+// row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_zero_fill(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_zero_fill<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_zero_fill<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_zero_fill<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_zero_fill<0x118, 0xF>(v);  // row_shr:8 (rows of 16 now scanned)
+  v += dpp_zero_fill<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

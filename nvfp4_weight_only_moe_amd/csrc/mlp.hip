@@ -34,7 +34,9 @@
 //    of two and writes Y as bf16 in sorted-row order.
 #include <mutex>
 
+#include "bucket_core.h"
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -148,21 +150,6 @@ constexpr int kUnitK = 128;
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts, then the
-// row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_zero_fill(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
-}
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += dpp_zero_fill<0x111, 0xF>(v);  // row_shr:1
-  v += dpp_zero_fill<0x112, 0xF>(v);  // row_shr:2
-  v += dpp_zero_fill<0x114, 0xF>(v);  // row_shr:4
-  v += dpp_zero_fill<0x118, 0xF>(v);  // row_shr:8 (rows of 16 now scanned)
-  v += dpp_zero_fill<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_zero_fill<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
 // Row blocks per group of the block order (below).
 constexpr int kRowGroup = 8;
 
@@ -600,6 +587,7 @@ constexpr int kDownNPWide = 4;   // ... with 16-row tiles
 // unsplit grid faster)
 constexpr int kGemvSplitBelow = 512;
 
+
 template <int NL, int NW>
 struct GemvUnit {
   u32x4 a[NL];
@@ -617,7 +605,7 @@ struct GemvArgs {
   uint16_t *out;           // GATED: A [P][N] bf16; else Y [P][N] bf16
 };
 
-template <int R, int NP, bool GATED, int KS, int FMT>
+template <int R, int NP, bool GATED, int KS, int FMT, int PD = kGemvPD>
 __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, const Nvfp4 &w1,
                                          int e, int row0, int mrows, int nt0, float *s_red) {
   constexpr int NW = GATED ? 2 * NP : NP;
@@ -712,20 +700,20 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     }
   };
 
-  // ---- K loop: kGemvPD + 1 register buffers.  The loads of unit u + kGemvPD
-  // are issued before unit u is multiplied (a scheduling barrier keeps them
-  // there), so kGemvPD units stay in flight while a wave computes.  The unit
+  // ---- K loop: PD + 1 register buffers.  The loads of unit u + PD are
+  // issued before unit u is multiplied (a scheduling barrier keeps them
+  // there), so PD units stay in flight while a wave computes.  The unit
   // count is rounded up to a multiple of the buffer count; the extra units
   // read zeros through the buffer range check and add nothing.
-  constexpr int NB = kGemvPD + 1;
+  constexpr int NB = PD + 1;
   GemvUnit<NL, NW> buf[NB];
 #pragma unroll
-  for (int d = 0; d < kGemvPD; ++d) load(ub + d, buf[d]);
+  for (int d = 0; d < PD; ++d) load(ub + d, buf[d]);
   const int nu = (ue - ub + NB - 1) / NB * NB;
   for (int u0 = ub; u0 < ub + nu; u0 += NB) {
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
-      load(u0 + d + kGemvPD, buf[(d + kGemvPD) % NB]);
+      load(u0 + d + PD, buf[(d + PD) % NB]);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[d]);
       __builtin_amdgcn_sched_barrier(0);
@@ -801,19 +789,16 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
 
 // Tile y of the GEMV grid, for "expert e contributes ceil(M_e / rows) tiles
 // of rows rows, in expert order": each wave finds it from the expert offsets
-// (E + 1 ints, L2-resident) with a DPP prefix sum over the per-expert tile
-// counts -- about the latency of one load, so no separate tile-list kernel.
-// Lane l takes experts PER*l .. PER*l + PER - 1.  Returns false when y is at
-// or past the tile count (uniform).
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
-                                          int y, int &e, int &row0, int &mrows) {
-  constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
+// (E + 1 ints) with a DPP prefix sum over the per-expert tile counts --
+// about the latency of one load, so no separate tile-list kernel.  Lane l
+// takes experts PER*l .. PER*l + PER - 1 and holds off[i] = offsets[PER*l + i]
+// (any value past E).  Returns false when y is at or past the tile count
+// (uniform).
+constexpr int kTilePer = MOE_MAX_EXPERTS / kWave;  // 4
+__device__ __forceinline__ bool find_tile_from(const int (&off)[kTilePer + 1], int E, int rows,
+                                               int y, int &e, int &row0, int &mrows) {
+  constexpr int PER = kTilePer;
   const int lane = threadIdx.x & 63;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4u);
-  int off[PER + 1];
-#pragma unroll
-  for (int i = 0; i <= PER; ++i)
-    off[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ro, (uint32_t)(PER * lane + i) * 4u, 0, 0);
   int c[PER], sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -844,14 +829,29 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   return true;
 }
 
+// the offsets from memory (buffer loads; lanes past E read zeros)
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
+                                          int y, int &e, int &row0, int &mrows) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4u);
+  int off[kTilePer + 1];
+#pragma unroll
+  for (int i = 0; i <= kTilePer; ++i)
+    off[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ro, (uint32_t)(kTilePer * lane + i) * 4u, 0, 0);
+  return find_tile_from(off, E, rows, y, e, row0, mrows);
+}
+
 // GATED: A = gelu_tanh(X Wg^T) * (X Wu^T) -> A [P][N] bf16; else
 // Y = A Wd^T -> Y [P][N] bf16.  Tiles of ROWS sorted rows from the tile list.
 // KS = 1: the 4 waves take 4 consecutive column groups of NP row tiles, each
 // all of K; KS = 4: the 4 waves share one column group and split K (gate/up
 // always; down for batches with few tiles, where whole-K streams per wave
 // would leave HBM idle).
-template <int ROWS, int NP, bool GATED, int KS, int FMT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROWS == 8 ? 4 : 3)))
+// PD: K units in flight per wave (deeper for small batches, whose few loads
+// are latency-bound and whose occupancy does not matter).
+template <int ROWS, int NP, bool GATED, int KS, int FMT, int PD = kGemvPD>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(PD > kGemvPD ? 2 : ROWS == 8 ? 4 : 3)))
 void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets, int E, Nvfp4 w0, Nvfp4 w1) {
   constexpr int NW = GATED ? 2 * NP : NP;
   __shared__ __attribute__((aligned(16))) float s_red[KS > 1 ? KS * 64 * NW * 4 : 4];
@@ -861,14 +861,90 @@ void k_expert_gemv(GemvArgs p, const int32_t *__restrict__ offsets, int E, Nvfp4
   int e, row0, mrows;
   if (!find_tile(offsets, E, ROWS, blockIdx.y, e, row0, mrows)) return;  // uniform
   // rows per MFMA block: the smallest packing that holds the tile (uniform)
-  if (mrows <= 4) gemv_run<4, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
-  else if (ROWS == 8 || mrows <= 8) gemv_run<8, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
-  else gemv_run<16, NP, GATED, KS, FMT>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  if (mrows <= 4) gemv_run<4, NP, GATED, KS, FMT, PD>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else if (ROWS == 8 || mrows <= 8)
+    gemv_run<8, NP, GATED, KS, FMT, PD>(p, w0, w1, e, row0, mrows, nt0, s_red);
+  else gemv_run<16, NP, GATED, KS, FMT, PD>(p, w0, w1, e, row0, mrows, nt0, s_red);
 }
 
 bool tensor_ok(const nvfp4_tensor *t, int E, int N, int K) {
   return t->E == E && t->N == N && t->K == K;
 }
+
+// ----------------------------------------------- fused decode layer ----
+// For T <= kDecodeMaxT tokens (moe_layer_decode) the selection kernel does
+// not run: every workgroup of k_decode_gate_up repeats the top-k selection of
+// every token from the logits (a wave per two tokens) and the bucketing of
+// the pairs (one wave, in LDS) -- a few microseconds after one load, instead
+// of a kernel of its own -- and then runs its gate/up GEMV tile: expert tile
+// y (an expert has at most T <= 8 rows: one 8-row tile), column group x.
+// Workgroup (0, 0) also writes the routing and bucketing outputs for the
+// down projection and the combine.
+constexpr int kDecodeMaxT = MOE_DECODE_MAX_TOKENS;
+constexpr int kDecodeMaxP = MOE_DECODE_MAX_PAIRS;
+static_assert(kDecodeMaxP <= kWave, "the bucketing of the decode layer is one wave's");
+static_assert(kDecodeMaxT <= 2 * (kThreads / kWave), "two tokens per selecting wave");
+constexpr int kDecodePD = kGemvPD;  // gate/up K units in flight per wave
+
+struct DecodeRoute {
+  const float *logits;  // [T][E]
+  const uint16_t *pes;  // [E]
+  int T, E;
+  int32_t *topk_idx;    // outputs of workgroup (0, 0): [T][top_k]
+  float *topk_w, *topk_w_raw;  // topk_w_raw may be null
+  int32_t *offsets, *sorted, *rank, *err;  // [E+1], [P], [P], [1]
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_gate_up(GemvArgs p, DecodeRoute r, Nvfp4 w0, Nvfp4 w1) {
+  constexpr int NP = kGateNP, NW = 2 * NP, KS = 4;
+  __shared__ __attribute__((aligned(16))) float s_red[KS * 64 * NW * 4];
+  __shared__ int32_t s_idx[kDecodeMaxP], s_sorted[kDecodeMaxP], s_rank[kDecodeMaxP];
+  __shared__ float s_w[kDecodeMaxP], s_wr[kDecodeMaxP];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_cnt[kMaxB];
+  __shared__ int32_t s_err;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = p.top_k, P = p.P;
+  // tokens wave and wave + 4 (T <= 8), the two chains interleaved
+  constexpr int NWV = kThreads / kWave;
+  if (wave < r.T) {
+    if (r.T <= NWV)
+      select_token(r.logits, r.pes, wave, r.E, K, s_idx, s_w, s_wr);
+    else if (r.E <= 2 * kWave)
+      select_tokens_n<2, 2>(r.logits, r.pes, wave, NWV, r.T, r.E, K, s_idx, s_w, s_wr);
+    else
+      select_tokens_n<MOE_MAX_EXPERTS / kWave, 2>(r.logits, r.pes, wave, NWV, r.T, r.E, K, s_idx,
+                                                   s_w, s_wr);
+  }
+  __syncthreads();
+  bucket_one_wave(s_idx, P, r.E, s_off, s_sorted, s_rank, &s_err, s_cnt);
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < P; i += kThreads) {
+      r.topk_idx[i] = s_idx[i];
+      r.topk_w[i] = s_w[i];
+      if (r.topk_w_raw) r.topk_w_raw[i] = s_wr[i];
+      r.sorted[i] = s_sorted[i];
+      r.rank[i] = s_rank[i];
+    }
+    for (int i = tid; i <= r.E; i += kThreads) r.offsets[i] = s_off[i];
+    if (tid == 0) *r.err = s_err;
+  }
+  const int nt0 = blockIdx.x * NP;
+  if (nt0 * 16 >= p.N) return;  // uniform: past the last column
+  int off[kTilePer + 1];
+#pragma unroll
+  for (int i = 0; i <= kTilePer; ++i) off[i] = s_off[min(kTilePer * lane + i, r.E)];
+  int e, row0, mrows;
+  if (!find_tile_from(off, r.E, 8, blockIdx.y, e, row0, mrows)) return;  // uniform
+  GemvArgs q = p;
+  q.sorted_pairs = s_sorted;
+  if (mrows <= 4) gemv_run<4, NP, true, KS, FMT, kDecodePD>(q, w0, w1, e, row0, mrows, nt0, s_red);
+  else gemv_run<8, NP, true, KS, FMT, kDecodePD>(q, w0, w1, e, row0, mrows, nt0, s_red);
+}
+
 
 }  // namespace
 }  // namespace moe
@@ -1035,9 +1111,9 @@ int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E
     const dim3 grid(split ? (H + 16 * np - 1) / (16 * np) : gx, w.L.max_tiles);
     const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, T * top_k,
                      (uint32_t)((size_t)T * top_k * I * 2), y_sorted};
-#define MOE_GEMV_DN(ROWS, NP, KS)                                                               \
-  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS, FMT>), grid, dim3(kThreads), 0, s, a,          \
-             expert_offsets, E, d, d)
+#define MOE_GEMV_DN(ROWS, NP, KS, ...)                                                          \
+  MOE_LAUNCH((k_expert_gemv<ROWS, NP, false, KS, FMT, ##__VA_ARGS__>), grid, dim3(kThreads), 0, s, \
+             a, expert_offsets, E, d, d)
     if (rows == 8 && many) {
       if (split) MOE_GEMV_DN(8, kDownNPMany, 4); else MOE_GEMV_DN(8, kDownNPMany, 1);
     } else if (rows == 8) {
@@ -1135,6 +1211,38 @@ extern "C" int nvfp4_expert_mlp(const uint16_t *x_expert, const nvfp4_tensor *ga
   return nvfp4_expert_down(down, expert_offsets, T, top_k, H, I, y_sorted, workspace, ws_bytes,
                            stream);
 }
+
+namespace moe {
+// The gate/up stage of the fused decode layer (moe_layer_decode), with the
+// top-k selection and the bucketing folded in.  Arguments validated by the
+// caller (T <= kDecodeMaxT, T * top_k <= kDecodeMaxP); expert_ws is the
+// expert MLP's workspace for (T, top_k, E, H, I), its f16 rows and exponents
+// already written and its row maxima cleared.
+__attribute__((visibility("hidden"))) int launch_decode_gate_up(
+    const float *logits, const uint16_t *pes, int T, int top_k, int E, int H, int I,
+    const nvfp4_tensor *gate, const nvfp4_tensor *up, int32_t *topk_idx, float *topk_w,
+    float *topk_w_raw, int32_t *offsets, int32_t *sorted, int32_t *rank, int32_t *err,
+    void *expert_ws, hipStream_t s) {
+  const Ws w = ws_ptrs(expert_ws, ws_layout(T, top_k, E, H, I));
+  const int P = T * top_k;
+  const GemvArgs a{w.x16, w.x_exp, w.a_max, nullptr, top_k, H, I, P,
+                   (uint32_t)((size_t)T * H * 2), w.a};
+  const DecodeRoute dr{logits, pes, T, E, topk_idx, topk_w, topk_w_raw, offsets, sorted, rank, err};
+  const Nvfp4 g{gate->packed, gate->scales, gate->global}, u{up->packed, up->scales, up->global};
+  const dim3 grid((I + 16 * kGateNP - 1) / (16 * kGateNP), P < E ? P : E);
+  switch (gate->format) {
+    case MOE_FORMAT_Q4_0:
+      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_Q4_0>, grid, dim3(kThreads), 0, s, a, dr, g, u);
+      break;
+    case MOE_FORMAT_AFF4:
+      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_AFF4>, grid, dim3(kThreads), 0, s, a, dr, g, u);
+      break;
+    default:
+      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_NVFP4>, grid, dim3(kThreads), 0, s, a, dr, g, u);
+  }
+  return MOE_OK;
+}
+}  // namespace moe
 
 // ---- nvfp4_expert_mlp without a caller workspace -------------------------
 // For callers that cannot allocate device memory: the workspace is a

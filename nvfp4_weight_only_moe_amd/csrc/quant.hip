@@ -8,8 +8,9 @@
 //   g    = fl32(max|W| / (6 * 448))                  per expert tensor
 //   code = E4M3_rne_sat(amax_block / (6 g))          in IEEE double
 //   q    = E2M1_rne(clip(w / (E4M3(code) g), -6, 6)) in IEEE double
-// Three kernels: per-expert max|W| (integer atomicMax of float bits: exact and
-// order-independent), the per-block quantisation, and the write of g.
+// Three kernels: per-expert max|W| (integer atomicMax of float bits, one per
+// workgroup: exact and order-independent), the per-block quantisation, and
+// the write of g.
 #include "common.h"
 
 namespace moe {
@@ -20,14 +21,20 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, int 
   if (i < n) p[i] = v;
 }
 
+// max|W| of expert blockIdx.y: each workgroup takes a contiguous slice,
+// reduces it in registers and LDS, and issues one integer atomicMax of the
+// float bits (gridDim.x atomics per expert: same-address atomics serialise,
+// so there are few of them).
 __global__ __launch_bounds__(256) void k_absmax(const uint16_t *__restrict__ w, size_t per_e,
                                                 uint32_t *__restrict__ amax_bits) {
+  __shared__ float s_m[4];
   const int e = blockIdx.y;
   const uint16_t *base = w + (size_t)e * per_e;
+  const size_t n8 = per_e / 8;  // 16-byte pieces (K % 32 == 0)
+  const size_t b0 = n8 * blockIdx.x / gridDim.x, b1 = n8 * (blockIdx.x + 1) / gridDim.x;
   float m = 0.0f;
-  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_e;
-       i += (size_t)gridDim.x * 256 * 8) {
-    const u32x4 v = *(const u32x4 *)(base + i);
+  for (size_t i = b0 + threadIdx.x; i < b1; i += 256) {
+    const u32x4 v = *(const u32x4 *)(base + i * 8);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       m = fmaxf(m, fabsf(__uint_as_float(v[q] << 16)));
@@ -35,7 +42,10 @@ __global__ __launch_bounds__(256) void k_absmax(const uint16_t *__restrict__ w, 
     }
   }
   m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(&amax_bits[e], __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(&amax_bits[e], __float_as_uint(fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]))));
 }
 
 // nearest E4M3 code of r >= 0 (ties to even mantissa, saturate at 448)
@@ -208,8 +218,9 @@ extern "C" int nvfp4_quantize(const uint16_t *w, int32_t E, int32_t N, int32_t K
   uint32_t *amax = (uint32_t *)global;
   MOE_LAUNCH(k_fill_u32, dim3((E + 255) / 256), dim3(256), 0, s, amax, E, 0u);
   const size_t per_e = (size_t)N * K;
-  const size_t gx0 = (per_e / 8 + 255) / 256;
-  const int gx = (int)(gx0 < 1024 ? gx0 : 1024);
+  // slices of at least 16 KiB, at most 64 workgroups per expert
+  const size_t gx0 = (per_e * 2 + 16383) / 16384;
+  const int gx = (int)(gx0 < 64 ? gx0 : 64);
   MOE_LAUNCH(k_absmax, dim3(gx, E), dim3(256), 0, s, w, per_e, amax);
   const size_t nblk = (size_t)N * (K / 16);
   MOE_LAUNCH(k_quant, dim3((unsigned)((nblk + 255) / 256), E), dim3(256), 0, s, w, N, K,

@@ -73,13 +73,29 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, con
 // 16-byte-per-lane read along a row.
 constexpr int kFewMaxV = 8;  // 16-byte vectors per lane: H <= 64 * 8 * kFewMaxV
 
+// With pa.x16 (the fused decode layer), ceil(T/4) more workgroups in the row
+// y = 0 (blockIdx.x >= E) write the expert input's f16 rows (one wave per
+// token) and clear the per-row maximum of A.
 template <int NV>  // 16-byte vectors per lane: lane holds k = (v*64 + lane)*8 .. +7
 __global__ __launch_bounds__(256) void k_route_logits_few(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
-    float eps, float *__restrict__ logits, int32_t *__restrict__ arrive) {
+    float eps, float *__restrict__ logits, int32_t *__restrict__ arrive, PrepArgs pa) {
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (e >= E) {  // the expert-input prep (uniform per workgroup)
+    if (blockIdx.y != 0) return;
+    const int wg = e - E;
+    for (int i = wg * 256 + threadIdx.x; i < pa.P; i += 256 * ((T + 3) / 4)) pa.a_max[i] = 0u;
+    const int t = wg * 4 + wave;
+    if (t < T) {
+      if (pa.norm_w)
+        prep_row<true>(pa.x, pa.norm_w, pa.norm_eps, pa.H, t, pa.x16, pa.x_exp);
+      else
+        prep_row<false>(pa.x, nullptr, 0.0f, pa.H, t, pa.x16, pa.x_exp);
+    }
+    return;
+  }
   // the arrival counter of the selection kernel that follows (when given)
   if (arrive && e == 0 && blockIdx.y == 0 && threadIdx.x == 0) *arrive = 0;
   // workgroup (e, y) takes tokens 16y .. 16y+15, 4 per wave
@@ -340,7 +356,7 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
 #define MOE_FEW(NV)                                                                          \
   case NV:                                                                                   \
     MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, router_scale, \
-               logit_bias, T, H, E, eps, logits, (int32_t *)nullptr);                        \
+               logit_bias, T, H, E, eps, logits, (int32_t *)nullptr, PrepArgs{});            \
     break;
       MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
       default: MOE_FEW(8)
@@ -403,7 +419,7 @@ int route_bucket_fused(const uint16_t *x, const uint16_t *w_router, const uint16
 #define MOE_FEW(NV)                                                                          \
   case NV:                                                                                   \
     MOE_LAUNCH(k_route_logits_few<NV>, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, w_router, \
-               router_scale, logit_bias, T, H, E, eps, logits, arrive);                      \
+               router_scale, logit_bias, T, H, E, eps, logits, arrive, PrepArgs{});          \
     break;
     MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
     default: MOE_FEW(8)
@@ -478,3 +494,27 @@ extern "C" int moe_route_bucket_prep(
                             top_k, eps, topk_idx, topk_w, topk_w_raw, logits, expert_offsets,
                             sorted_pairs, pair_rank, bucket_ws, pa, (hipStream_t)stream);
 }
+
+namespace moe {
+// The fused decode layer's first kernel: the router logits of T <= 64 tokens
+// (H <= 4096) into `logits`, beside the expert input's prep (pa) in
+// ceil(T/4) more workgroups.  Arguments validated by the caller.
+__attribute__((visibility("hidden"))) int launch_route_logits_prep(
+    const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+    const float *logit_bias, int T, int H, int E, float eps, float *logits, const PrepArgs &pa,
+    hipStream_t s) {
+  const int nv = (H + 511) / 512;
+  const dim3 grid(E + (T + 3) / 4, (T + 15) / 16);
+  switch (nv) {
+#define MOE_FEW(NV)                                                                          \
+  case NV:                                                                                   \
+    MOE_LAUNCH(k_route_logits_few<NV>, grid, dim3(256), 0, s, x, w_router, router_scale,      \
+               logit_bias, T, H, E, eps, logits, (int32_t *)nullptr, pa);                    \
+    break;
+    MOE_FEW(1) MOE_FEW(2) MOE_FEW(3) MOE_FEW(4) MOE_FEW(5) MOE_FEW(6) MOE_FEW(7)
+    default: MOE_FEW(8)
+#undef MOE_FEW
+  }
+  return MOE_OK;
+}
+}  // namespace moe

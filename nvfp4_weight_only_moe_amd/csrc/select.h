@@ -147,6 +147,106 @@ __device__ __forceinline__ void select_token_n(const float *__restrict__ lrow,
   }
 }
 
+// NT tokens by one wave at once (t0, t0 + tstride, ...; those at or past T
+// are skipped): the same arithmetic as select_token_n, token by token, with
+// the NT independent chains of each round interleaved so that their
+// cross-lane latencies overlap.
+template <int NPER, int NT>
+__device__ __forceinline__ void select_tokens_n(const float *__restrict__ logits,
+                                                const uint16_t *__restrict__ pes, int t0,
+                                                int tstride, int T, int E, int K,
+                                                int32_t *__restrict__ topk_idx,
+                                                float *__restrict__ topk_w,
+                                                float *__restrict__ topk_w_raw) {
+  const int lane = threadIdx.x & 63;
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(pes, (uint32_t)E * 2u);
+  uint32_t praw[NPER];
+  uint32_t key[NT][NPER];
+  float v[NT][NPER];
+  bool on[NT];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) praw[i] = bload2(rp, (uint32_t)(lane + i * kWave) * 2u);
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const int t = t0 + q * tstride;
+    on[q] = t < T;
+    const __amdgpu_buffer_rsrc_t rl =
+        make_rsrc(logits + (size_t)(on[q] ? t : 0) * E, on[q] ? (uint32_t)E * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const uint32_t x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(lane + i * kWave) * 4u, 0, 0);
+      const float f = __uint_as_float(x);
+      const bool ok = lane + i * kWave < E;
+      v[q][i] = (ok && f == f) ? f : -__builtin_huge_valf();
+      key[q][i] = ok ? float_key(v[q][i]) : 0u;
+    }
+  }
+  float m[NT], z[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) kmax = max(kmax, key[q][i]);
+    m[q] = key_float(wave_max_key(kmax));
+  }
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    float zz = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) zz += (lane + i * kWave < E) ? expf(v[q][i] - m[q]) : 0.0f;
+    z[q] = wave_sum_u(zz);
+  }
+  uint32_t my_id[NT], my_key[NT], my_pes[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) my_id[q] = my_key[q] = my_pes[q] = 0;
+  for (int s = 0; s < K; ++s) {
+    uint32_t ms[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      uint32_t b = key[q][0];
+#pragma unroll
+      for (int i = 1; i < NPER; ++i) b = max(b, key[q][i]);
+      ms[q] = wave_max_key(b);
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      int id = 0;
+      uint32_t pw = 0;
+#pragma unroll
+      for (int i = NPER - 1; i >= 0; --i) {
+        const unsigned long long hit = __ballot(key[q][i] == ms[q]);
+        if (hit) {
+          const int l = (int)__builtin_ctzll(hit);
+          id = i * kWave + l;
+          pw = lane_read(praw[i], l);
+        }
+      }
+      id = __builtin_amdgcn_readfirstlane(id);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (lane + i * kWave == id) key[q][i] = 0u;
+      if (lane == s) {
+        my_id[q] = (uint32_t)id;
+        my_key[q] = ms[q];
+        my_pes[q] = pw;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const float p = lane < K ? expf(key_float(my_key[q]) - m[q]) / z[q] : 0.0f;
+    const float psum = wave_sum_u(p);
+    const int t = t0 + q * tstride;
+    if (on[q] && lane < K) {
+      const float wr = p / psum;
+      topk_idx[(size_t)t * K + lane] = (int32_t)my_id[q];
+      topk_w[(size_t)t * K + lane] = wr * bf16_to_f32((uint16_t)my_pes[q]);
+      if (topk_w_raw) topk_w_raw[(size_t)t * K + lane] = wr;
+    }
+  }
+}
+
 __device__ __forceinline__ void select_token(const float *__restrict__ logits,
                                              const uint16_t *__restrict__ pes, int t, int E,
                                              int K, int32_t *__restrict__ topk_idx,

@@ -257,3 +257,32 @@ def test_route_bucket_prep_rejects(L):
     assert L.moe_route_bucket_prep(*a) == -1                 # x NULL with T > 0
     a = list(ok); a[7] = 120
     assert L.moe_route_bucket_prep(*a) == -4                 # E % 16
+
+
+def test_layer_decode_rejects(L):
+    T, k, E, H, I = 8, 8, 128, 2816, 704
+    ws = L.moe_layer_decode_workspace_bytes(T, k, E, H, I)
+    assert ws >= L.moe_workspace_bytes(T, k, E, H, I) + T * E * 4
+    assert L.moe_layer_decode_error_offset(T, k, E) >= T * E * 4
+    R = ctypes.byref
+    g, u, d = _tensor(E, I, H), _tensor(E, I, H), _tensor(E, H, I)
+    # (x, w, scale, pes, bias, T, H, E, k, eps, gate, up, down, I, idx, w, w_raw, off, sp, pr,
+    #  out, ws, ws_bytes, stream)
+    ok = [FAKE, FAKE, FAKE, FAKE, NULL, T, H, E, k, 1e-6, R(g), R(u), R(d), I, FAKE, FAKE, NULL,
+          FAKE, FAKE, FAKE, FAKE, FAKE, ws, NULL]
+    a = list(ok); a[22] = ws - 1
+    assert L.moe_layer_decode(*a) == -3                     # workspace too small
+    a = list(ok); a[20] = NULL
+    assert L.moe_layer_decode(*a) == -1                     # out NULL
+    a = list(ok); a[5] = 9
+    a[22] = L.moe_layer_decode_workspace_bytes(9, k, E, H, I)
+    assert L.moe_layer_decode(*a) == -4                     # T > 8
+    a = list(ok); a[8] = 9
+    a[22] = L.moe_layer_decode_workspace_bytes(T, 9, E, H, I)
+    assert L.moe_layer_decode(*a) == -4                     # T * top_k > 64
+    a = list(ok); a[12] = R(_tensor(E, H, I, layout=0))
+    assert L.moe_layer_decode(*a) == -4                     # canonical layout
+    a = list(ok); a[12] = R(_tensor(E, H, I + 64))
+    assert L.moe_layer_decode(*a) == -2                     # descriptor shape
+    a = list(ok); a[5] = 0
+    assert L.moe_layer_decode(*a) == 0                      # T = 0: nothing queued
