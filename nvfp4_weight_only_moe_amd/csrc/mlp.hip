@@ -33,6 +33,7 @@
 //    bits (an integer max: order-independent).  Down rescales A to f16 by that maximum's power
 //    of two and writes Y as bf16 in sorted-row order.
 #include <mutex>
+#include <type_traits>
 
 #include "bucket_core.h"
 #include "common.h"
@@ -212,16 +213,10 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 // Register budget of the K loop: weight register sets of the LDS-direct
-// (gate/up) pipeline (3: weights two units ahead; 2: one unit ahead) and
-// activation fragment sets (2: the next step's fragments are read from LDS
-// while this step multiplies; 1: read just before use).  LDS activation
-// buffers of that pipeline: kGemmLdsBufs - 1 units in flight.
+// (gate/up) pipeline (3: weights two units ahead; 2: one unit ahead).  LDS
+// activation buffers of that pipeline: kGemmLdsBufs - 1 units in flight.
 constexpr int kGemmWeightSets = 3;
 constexpr int kGemmLdsBufs = 3;
-
-constexpr int kGemmAFragSets = 2;
-// dequantise the next K step's weights while this step's MFMAs run
-constexpr bool kGemmPipeDequant = true;
 
 // LDS activation buffers of the tiled-mode kernels
 template <bool GATED>
@@ -246,7 +241,9 @@ __device__ __forceinline__ void gemm_run(
   using WF = WeightFmt<FMT>;
   constexpr int SB = WF::kScaleBytes;       // scale bytes per lane and K unit
   constexpr int NBUF = gemm_lds_bufs<GATED>();  // LDS activation buffers
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave: uniform (a scalar register), so the LDS destinations of the
+  // staging loads are computed on the scalar unit
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (K + kUnitK - 1) / kUnitK;
   const int nt0 = (cb * 4 + wave) * NP;          // first output row tile of this wave
@@ -284,7 +281,7 @@ __device__ __forceinline__ void gemm_run(
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_src, a_bytes);
   auto a_offset = [&](int u, int q) -> uint32_t {
     const bool kok = u < nunits && u * kUnitK + st_c * 8 < K;
-    return kok ? st_off[q] + (uint32_t)u * kUnitK * 2 : kOOB;  // kOOB + 256u stays out of range
+    return off_if(kok, st_off[q] + (uint32_t)u * kUnitK * 2);  // kOOB + 256u stays out of range
   };
   // DIRECT staging of unit u into buffer b
   auto load_a_lds = [&](int u, int b) {
@@ -334,8 +331,10 @@ __device__ __forceinline__ void gemm_run(
     const bool ok = u < nunits && u * kUnitK + 32 * g < K;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      wv[i] = bload16_nt(rw[i], ok ? vw[i] + (uint32_t)u * 1024 : kOOB);
-      sv[i] = load_scale<SB>(rs[i], ok ? vs[i] + (uint32_t)u * 64 * SB : kOOB);
+      // a plain load: the row blocks of a block group reuse these weights
+      // from L2 (streamed loads measured 7% slower at 16384 tokens)
+      wv[i] = bload16(rw[i], off_if(ok, vw[i] + (uint32_t)u * 1024));
+      sv[i] = load_scale<SB>(rs[i], off_if(ok, vs[i] + (uint32_t)u * 64 * SB));
     }
   };
 
@@ -345,69 +344,43 @@ __device__ __forceinline__ void gemm_run(
 #pragma unroll
     for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
 
-  // One K unit: 4 steps of 32.  The activation fragments of step j+1 are
-  // read from LDS while step j is dequantised and multiplied (two register
-  // sets), and scheduling-group barriers keep that order, so LDS latency
-  // hides behind the MFMAs instead of stalling each of them.
+  // One K unit: 4 steps of 32.  The weights of step j + 1 are dequantised
+  // while the MFMAs of step j run (two register sets), and scheduling-group
+  // barriers interleave one MFMA with two VALU ops so that the VALU and the
+  // matrix core work side by side.  The activation fragment q of step j is
+  // row 16q + r, K chunk 4g + j: lds_chunk(16q + r, c) = lds_chunk(r, c) +
+  // 256 q, so one address per step serves every q (immediate offsets).
   auto compute = [&](const uint16_t *abuf, const u32x4 (&wv)[NW], const uint32_t (&sv)[NW]) {
     typename WF::Prep bs[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) bs[i] = WF::prep(sv[i]);
-    if (kGemmPipeDequant) {
-      // the weights of step j + 1 are dequantised while the MFMAs of step j
-      // run (two register sets), one MFMA between every two VALU ops
-      f16x8 a[Q], b[2][NW];
+    f16x8 a[Q], b[2][NW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) b[0][i] = WF::dequant(wv[i][0], bs[i], 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-          a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
-        if (j < 3) {
-#pragma unroll
-          for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = WF::dequant(wv[i][j + 1], bs[i], j + 1);
-        }
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-#pragma unroll
-          for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[q], b[j & 1][i], acc[q][i]);
-        __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
-        if (j < 3) {
-#pragma unroll
-          for (int m = 0; m < Q * NW; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (8 * NW) / (Q * NW), 0);
-          }
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, Q * NW, 0);
-        }
-      }
-      return;
-    }
-    constexpr int NA = kGemmAFragSets;
-    f16x8 a[NA][Q];
-    auto read_a = [&](int j, f16x8 (&dst)[Q]) {
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-        dst[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(q * kBM + r, 4 * g + j) * 8));
-    };
-    if (NA == 2) read_a(0, a[0]);
+    for (int i = 0; i < NW; ++i) b[0][i] = WF::dequant(wv[i][0], bs[i], 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (NA == 2 && j < 3) read_a(j + 1, a[(j + 1) % NA]);
-      if (NA == 1) read_a(j, a[0]);
-      f16x8 b[NW];
+      const uint16_t *aj = abuf + lds_chunk(r, 4 * g + j) * 8;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) b[i] = WF::dequant(wv[i][j], bs[i], j);
+      for (int q = 0; q < Q; ++q)
+        a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(aj + q * kBM * kUnitK));
+      if (j < 3) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) b[(j + 1) & 1][i] = WF::dequant(wv[i][j + 1], bs[i], j + 1);
+      }
 #pragma unroll
       for (int q = 0; q < Q; ++q)
 #pragma unroll
-        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[j % NA][q], b[i], acc[q][i]);
-      // order: LDS reads (of the next step with two fragment sets), dequantisation, MFMAs
-      if (NA == 1 || j < 3) __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8 * NW, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, Q * NW, 0);
+        for (int i = 0; i < NW; ++i) acc[q][i] = mfma16x16x32(a[q], b[j & 1][i], acc[q][i]);
+      __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
+      if (j < 3) {
+#pragma unroll
+        for (int m = 0; m < Q * NW; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (8 * NW) / (Q * NW), 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, Q * NW, 0);
+      }
     }
   };
 
@@ -439,20 +412,26 @@ __device__ __forceinline__ void gemm_run(
     for (int i = 0; i < WS - 1; ++i) load_w(i, wv[i], sv[i]);
     MOE_WAIT_VMCNT(PRE);  // unit 0 of the activations has landed
     __syncthreads();
+    // Units past the last one (up to UNR - 1 of them) multiply zeros; waves
+    // past N run a copy of the loop without MFMAs (no branch inside the loop)
     const int nuu = (nunits + UNR - 1) / UNR * UNR;
-    for (int u0 = 0; u0 < nuu; u0 += UNR) {
+    auto k_loop = [&](auto on) {
+      for (int u0 = 0; u0 < nuu; u0 += UNR) {
 #pragma unroll
-      for (int d = 0; d < UNR; ++d) {
-        const int u = u0 + d;  // LDS ring buffer of unit u: u % NBUF = d % NBUF
-        load_a_lds(u + NBUF - 1, (d + NBUF - 1) % NBUF);
-        load_w(u + WS - 1, wv[(d + WS - 1) % WS], sv[(d + WS - 1) % WS]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (u < nunits && wave_on) compute(s_a[d % NBUF], wv[d % WS], sv[d % WS]);
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_WAIT_VMCNT(AHEAD);  // unit u+1 of the activations has landed
-        __syncthreads();
+        for (int d = 0; d < UNR; ++d) {
+          const int u = u0 + d;  // LDS ring buffer of unit u: u % NBUF = d % NBUF
+          load_a_lds(u + NBUF - 1, (d + NBUF - 1) % NBUF);
+          load_w(u + WS - 1, wv[(d + WS - 1) % WS], sv[(d + WS - 1) % WS]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (decltype(on)::value) compute(s_a[d % NBUF], wv[d % WS], sv[d % WS]);
+          __builtin_amdgcn_sched_barrier(0);
+          MOE_WAIT_VMCNT(AHEAD);  // unit u+1 of the activations has landed
+          __syncthreads();
+        }
       }
-    }
+    };
+    if (wave_on) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
   } else {
     const int nu = (nunits + 1) & ~1;
     u32x4 av[2][Q];
