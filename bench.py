@@ -222,7 +222,7 @@ def gate_up_kernel_name(T, K, E, fmt="nvfp4"):
     f = FORMAT_INDEX[fmt]
     if avg < 24:
         rows = 8 if P <= 4 * E else 16
-        return f"k_expert_gemv<{rows}, 2, true, 4, {f}>"
+        return f"k_expert_gemv<{rows}, 2, true, 4, {f}, 1>"   # ..., prefetch depth 1
     return f"k_expert_gemm<4, 2, true, {f}>"
 
 

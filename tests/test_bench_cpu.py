@@ -19,11 +19,11 @@ def test_projection_bytes_match_the_formats():
 def test_gate_up_kernel_follows_the_dispatch_rule():
     # GEMV mode below 24 rows per active expert on average: 8-row tiles up
     # to 4 rows per expert, else 16; the tiled GEMM above
-    assert bench.gate_up_kernel_name(64, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0>"
-    assert bench.gate_up_kernel_name(4, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0>"
-    assert bench.gate_up_kernel_name(128, 8, 128) == "k_expert_gemv<16, 2, true, 4, 0>"
+    assert bench.gate_up_kernel_name(64, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0, 1>"
+    assert bench.gate_up_kernel_name(4, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0, 1>"
+    assert bench.gate_up_kernel_name(128, 8, 128) == "k_expert_gemv<16, 2, true, 4, 0, 1>"
     assert bench.gate_up_kernel_name(2048, 8, 128) == "k_expert_gemm<4, 2, true, 0>"
-    assert bench.gate_up_kernel_name(64, 8, 128, "aff4") == "k_expert_gemv<8, 2, true, 4, 2>"
+    assert bench.gate_up_kernel_name(64, 8, 128, "aff4") == "k_expert_gemv<8, 2, true, 4, 2, 1>"
 
 
 def test_stage_lists():
