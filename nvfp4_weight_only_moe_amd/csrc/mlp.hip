@@ -249,6 +249,38 @@ __device__ __forceinline__ void gemm_run(
   const int nt0 = (cb * 4 + wave) * NP;          // first output row tile of this wave
   const bool wave_on = nt0 * 16 < N;  // waves past the last column stage only (gate/up: no MFMAs)
 
+  // ---- weight streams of this wave (buffer resources over expert e's
+  // tensors; lanes past K, units past the end and waves past N read zeros)
+  __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
+  uint32_t vw[NW], vs[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
+    const int nt = nt0 + (GATED ? i % NP : i);
+    rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
+    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
+    vw[i] = wave_on ? (uint32_t)nt * 16 * (K / 2) + lane * 16 : kOOB;
+    vs[i] = wave_on ? (uint32_t)nt * K * SB / 2 + lane * SB : kOOB;
+  }
+  auto load_w = [&](int u, u32x4 (&wv)[NW], uint32_t (&sv)[NW]) {
+    const bool ok = u < nunits && u * kUnitK + 32 * g < K;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      // a plain load: the row blocks of a block group reuse these weights
+      // from L2 (streamed loads measured 7% slower at 16384 tokens)
+      wv[i] = bload16(rw[i], off_if(ok, vw[i] + (uint32_t)u * 1024));
+      sv[i] = load_scale<SB>(rs[i], off_if(ok, vs[i] + (uint32_t)u * 64 * SB));
+    }
+  };
+
+  // weight register sets; unit 0's weights are requested first, before the
+  // staging map looks up the block's rows (they do not depend on them)
+  constexpr int WS = DIRECT ? kGemmWeightSets : 2;
+  u32x4 wv[WS][NW];
+  uint32_t sv[WS][NW];
+  load_w(0, wv[0], sv[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- staging map.  DIRECT: load q of wave w fills rows 16q + 4w + lane/16,
   // LDS chunk positions lane%16 (one contiguous kilobyte per load); the lane
   // fetches the K chunk that belongs at that position.  Otherwise: thread ->
@@ -314,30 +346,6 @@ __device__ __forceinline__ void gemm_run(
     }
   };
 
-  // ---- weight streams of this wave (buffer resources over expert e's
-  // tensors; lanes past K, units past the end and waves past N read zeros)
-  __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
-  uint32_t vw[NW], vs[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
-    const int nt = nt0 + (GATED ? i % NP : i);
-    rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
-    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
-    vw[i] = wave_on ? (uint32_t)nt * 16 * (K / 2) + lane * 16 : kOOB;
-    vs[i] = wave_on ? (uint32_t)nt * K * SB / 2 + lane * SB : kOOB;
-  }
-  auto load_w = [&](int u, u32x4 (&wv)[NW], uint32_t (&sv)[NW]) {
-    const bool ok = u < nunits && u * kUnitK + 32 * g < K;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      // a plain load: the row blocks of a block group reuse these weights
-      // from L2 (streamed loads measured 7% slower at 16384 tokens)
-      wv[i] = bload16(rw[i], off_if(ok, vw[i] + (uint32_t)u * 1024));
-      sv[i] = load_scale<SB>(rs[i], off_if(ok, vs[i] + (uint32_t)u * 64 * SB));
-    }
-  };
-
   f32x4 acc[Q][NW];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
@@ -390,9 +398,6 @@ __device__ __forceinline__ void gemm_run(
   // double-buffered in registers, unit u+1 issued before unit u is
   // multiplied; activations in two register sets, unit u+3 loaded when unit
   // u+1 has been converted into the LDS double buffer.
-  constexpr int WS = DIRECT ? kGemmWeightSets : 2;  // weight register sets
-  u32x4 wv[WS][NW];
-  uint32_t sv[WS][NW];
   if (DIRECT) {
     // activations NBUF - 1 units ahead (a ring of NBUF LDS buffers), weights
     // WS - 1 units ahead (WS register sets); the loop is unrolled by a
@@ -402,15 +407,18 @@ __device__ __forceinline__ void gemm_run(
     // (past the end they read zeros), so the vector-memory counter waits
     // below are exact: after the activations of a unit come the NBUF - 2
     // later units' activation loads and, before it is needed, at least
-    // min(NBUF - 1, WS) groups of weight loads.
+    // min(NBUF - 1, WS) groups of weight loads.  (Unit 0's weights went
+    // first, before the activation loads of units 0 .. NBUF - 2; then units
+    // 1 .. WS - 2 of the weights.)
+    static_assert(WS >= 2, "");
     constexpr int UNR = NBUF * WS / gcd_c(NBUF, WS);
-    constexpr int PRE = (NBUF - 2) * Q + (WS - 1) * 2 * NW;  // after unit 0's activations
+    constexpr int PRE = (NBUF - 2) * Q + (WS - 2) * 2 * NW;  // after unit 0's activations
     constexpr int AHEAD = (NBUF - 2) * Q + (NBUF - 1 < WS ? NBUF - 1 : WS) * 2 * NW;
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) load_a_lds(i, i);
 #pragma unroll
-    for (int i = 0; i < WS - 1; ++i) load_w(i, wv[i], sv[i]);
-    MOE_WAIT_VMCNT(PRE);  // unit 0 of the activations has landed
+    for (int i = 1; i < WS - 1; ++i) load_w(i, wv[i], sv[i]);
+    MOE_WAIT_VMCNT(PRE);  // unit 0 of the activations (and of the weights) has landed
     __syncthreads();
     // Units past the last one (up to UNR - 1 of them) multiply zeros; waves
     // past N run a copy of the loop without MFMAs (no branch inside the loop)
@@ -435,8 +443,7 @@ __device__ __forceinline__ void gemm_run(
   } else {
     const int nu = (nunits + 1) & ~1;
     u32x4 av[2][Q];
-    load_a(0, av[0]);
-    load_w(0, wv[0], sv[0]);
+    load_a(0, av[0]);  // unit 0's weights are already in flight
     load_a(1, av[1]);
     store_a(0, av[0]);
     load_a(2, av[0]);
@@ -597,6 +604,43 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   // partial sums meet in LDS after the loop; KS = 1: all of K)
   const int ub = KS == 1 ? 0 : wave * nunits / KS, ue = KS == 1 ? nunits : (wave + 1) * nunits / KS;
 
+  using WF = WeightFmt<FMT>;
+  constexpr int SB = WF::kScaleBytes;  // scale bytes per lane and K unit
+  const float ep_g0 = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
+  const float ep_g1 = !GATED ? 0.0f : FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
+
+  // weight streams: expert e's tensors through buffer resources; offsets past
+  // the end (lanes past K, units past the end) read hardware zeros
+  __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
+  uint32_t vw[NW], vs[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
+    const int nt = nt0 + (GATED ? i % NP : i);
+    rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
+    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
+    vw[i] = (uint32_t)nt * 16 * (K / 2) + lane * 16;
+    vs[i] = (uint32_t)nt * K * SB / 2 + lane * SB;
+  }
+  auto load_w = [&](int u, GemvUnit<NL, NW> &d) {
+    const bool kok = u < ue && u * kUnitK + 32 * g < K;
+    const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 64 * SB : kOOB;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      d.w[i] = bload16_nt(rw[i], vw[i] + ow);
+      d.s[i] = load_scale<SB>(rs[i], vs[i] + os);
+    }
+  };
+
+  // ---- K-loop buffers; the first units' weight loads leave before this
+  // lane's activation row is looked up (they do not depend on it), so their
+  // latency overlaps that lookup
+  constexpr int NB = PD + 1;
+  GemvUnit<NL, NW> buf[NB];
+#pragma unroll
+  for (int d = 0; d < PD; ++d) load_w(ub + d, buf[d]);
+  __builtin_amdgcn_sched_barrier(0);
+
   // activation row of this lane
   const bool row_ok = m < mrows;
   const int prow = row_ok ? row0 + m : row0;
@@ -616,39 +660,18 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
     row_ex = row_exponent(__uint_as_float(p.a_max[prow]));
     a_scale = __builtin_ldexpf(1.0f, 14 - row_ex);
   }
-  using WF = WeightFmt<FMT>;
-  constexpr int SB = WF::kScaleBytes;  // scale bytes per lane and K unit
-  const float ep_g0 = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
-  const float ep_g1 = !GATED ? 0.0f : FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_src, p.a_bytes);
-
-  // weight streams: expert e's tensors through buffer resources; offsets past
-  // the end (lanes past K, units past the end) read hardware zeros
-  __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
-  uint32_t vw[NW], vs[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const Nvfp4 &w = (GATED && i >= NP) ? w1 : w0;
-    const int nt = nt0 + (GATED ? i % NP : i);
-    rw[i] = make_rsrc(w.packed + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
-    rs[i] = make_rsrc(w.scales + (size_t)e * N * K * SB / 32, (uint32_t)((size_t)N * K * SB / 32));
-    vw[i] = (uint32_t)nt * 16 * (K / 2) + lane * 16;
-    vs[i] = (uint32_t)nt * K * SB / 2 + lane * SB;
-  }
-  auto load = [&](int u, GemvUnit<NL, NW> &d) {
+  auto load_a = [&](int u, GemvUnit<NL, NW> &d) {
     const bool kok = u < ue && u * kUnitK + 32 * g < K;
-    const uint32_t ow = kok ? (uint32_t)u * 1024 : kOOB, os = kok ? (uint32_t)u * 64 * SB : kOOB;
     // va is kOOB for rows past the tile; kOOB + 256u + 16s stays out of range
     const uint32_t oa = kok ? va + (uint32_t)u * kUnitK * 2 : kOOB;
 #pragma unroll
     for (int sl = 0; sl < NL; ++sl) d.a[sl] = bload16(ra, oa + 16 * sl);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      d.w[i] = bload16_nt(rw[i], vw[i] + ow);
-      d.s[i] = load_scale<SB>(rs[i], vs[i] + os);
-    }
   };
-
+  auto load = [&](int u, GemvUnit<NL, NW> &d) {
+    load_a(u, d);
+    load_w(u, d);
+  };
   f32x4 acc[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) acc[i] = f32x4{0, 0, 0, 0};
@@ -684,10 +707,8 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
   // there), so PD units stay in flight while a wave computes.  The unit
   // count is rounded up to a multiple of the buffer count; the extra units
   // read zeros through the buffer range check and add nothing.
-  constexpr int NB = PD + 1;
-  GemvUnit<NL, NW> buf[NB];
 #pragma unroll
-  for (int d = 0; d < PD; ++d) load(ub + d, buf[d]);
+  for (int d = 0; d < PD; ++d) load_a(ub + d, buf[d]);
   const int nu = (ue - ub + NB - 1) / NB * NB;
   for (int u0 = ub; u0 < ub + nu; u0 += NB) {
 #pragma unroll
