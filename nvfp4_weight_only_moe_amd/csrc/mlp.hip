@@ -27,7 +27,9 @@
 //       its activation chunks (16 bytes of one row, row-major [row][K]) with
 //       buffer loads straight into MFMA operand registers.
 //     - tiled mode (prefill): 16*MSUB rows per tile staged in LDS per K unit
-//       and shared by the 4 waves, weights streamed once per tile.
+//       and shared by the 4 waves, weights streamed once per tile; 64-row
+//       tiles, and for gate/up 128-row tiles once buckets average 384 rows
+//       (accumulators held in place in the accumulation registers).
 //    Gate/up epilogue: GELU-tanh gating, A rounded to bf16 (row-major
 //    [P][I] in sorted-row order), per-row max|A| by atomicMax on the float
 //    bits (an integer max: order-independent).  Down rescales A to f16 by that maximum's power
@@ -65,6 +67,17 @@ int choose_msub(int T, int top_k, int E) {
   const long long avg = buckets > 0 ? P / buckets : 0;
   if (avg < 24) return 1;
   return 4;
+}
+
+// rows per gate/up block in tiled mode: 128 (MSUB = 8) once buckets hold 384
+// rows or more on average (measured crossover: equal at 256 rows, 8% faster
+// at 512, 13% at 1024; slower below), else 64
+int gate_up_msub(int T, int top_k, int E) {
+  const int m = choose_msub(T, top_k, E);
+  if (m == 1) return 1;
+  const long long P = (long long)T * top_k;
+  const long long buckets = P < E ? P : E;
+  return P / buckets >= 384 ? 8 : m;
 }
 
 // Few rows per expert (decode): the GEMV-mode kernels.  Otherwise tiled mode.
@@ -120,6 +133,27 @@ __device__ __forceinline__ float gelu_tanh(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// acc += a * b on the matrix core with the accumulator kept in place in the
+// accumulation registers (the "a" constraint), for kernels whose
+// accumulators fill them.  The compiler still tracks the operands (it waits
+// for the loads that produce a and b), but it does not know the statement is
+// an MFMA, so the statement and its users carry the pipeline waits the
+// compiler would otherwise insert:
+//  * a VALU write of a, b or acc (the accumulators' zeroing included) needs
+//    two wait states before an MFMA reads it: the s_nop 1 in front;
+//  * an MFMA result read as the next MFMA's accumulator in the same
+//    registers needs no wait (the compiler issues such chains back to back);
+//  * an MFMA result read by anything else: mfma_acc_drain(), 24 wait states
+//    (more than a 16x16x32 f16 MFMA needs) and a scheduling barrier, after
+//    the last mfma_acc and before the accumulators are read.
+__device__ __forceinline__ void mfma_acc(f32x4 &acc, const f16x8 &a, const f16x8 &b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------- grouped expert GEMM ----
 // Tiled mode (prefill).  A workgroup (4 waves) owns one block of 16*MSUB
 // sorted rows of one expert and 4*NP*16 output columns; each wave owns NP row
@@ -139,6 +173,11 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 // the others but issue no MFMAs.  Gate/up keeps the weights of two units and
 // the activations of two units in flight while a unit is multiplied; down
 // one unit of weights and two of activations.
+//
+// 128-row gate/up blocks (MSUB = 8) keep their 128 accumulators per wave in
+// the accumulation registers through mfma_acc (below), the only way found to
+// fit them beside the rest at two waves per SIMD: the compiler, left to
+// itself, moved accumulators between register files or spilled them.
 //
 // Order of the workgroups: a 1-D grid, a multiple of the 8 XCDs.  Hardware
 // hands workgroup b to XCD b % 8; b is mapped to the logical index
@@ -217,10 +256,19 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
 // activation buffers of that pipeline: kGemmLdsBufs - 1 units in flight.
 constexpr int kGemmWeightSets = 3;
 constexpr int kGemmLdsBufs = 3;
+// 128-row gate/up blocks (MSUB = 8, for buckets of many rows): each wave
+// keeps 8 row groups x 2 gate + 2 up row tiles = 128 accumulators, which
+// fill the accumulation registers (mfma_acc), so each dequantised weight
+// fragment feeds 8 MFMAs instead of 4 -- half the dequant VALU work per
+// MFMA.  The other 128 registers of a wave at two waves per SIMD then hold
+// one activation fragment set, two weight sets and a two-buffer LDS ring
+// (64 KB: two workgroups per CU).
+template <int MSUB>
+constexpr int gemm_weight_sets() { return MSUB == 8 ? 2 : kGemmWeightSets; }
 
 // LDS activation buffers of the tiled-mode kernels
-template <bool GATED>
-constexpr int gemm_lds_bufs() { return GATED ? kGemmLdsBufs : 2; }
+template <int MSUB, bool GATED>
+constexpr int gemm_lds_bufs() { return GATED ? (MSUB == 8 ? 2 : kGemmLdsBufs) : 2; }
 
 // One block of the tiled mode: rows row0 .. row0 + mrows - 1 (mrows <= 16 Q)
 // of expert e, column block cb.  Q: the 16-row groups holding rows; only
@@ -240,7 +288,7 @@ __device__ __forceinline__ void gemm_run(
   constexpr int NW = GATED ? 2 * NP : NP;  // weight row tiles streamed by a wave
   using WF = WeightFmt<FMT>;
   constexpr int SB = WF::kScaleBytes;       // scale bytes per lane and K unit
-  constexpr int NBUF = gemm_lds_bufs<GATED>();  // LDS activation buffers
+  constexpr int NBUF = gemm_lds_bufs<MSUB, GATED>();  // LDS activation buffers
   // wave: uniform (a scalar register), so the LDS destinations of the
   // staging loads are computed on the scalar unit
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -275,7 +323,7 @@ __device__ __forceinline__ void gemm_run(
 
   // weight register sets; unit 0's weights are requested first, before the
   // staging map looks up the block's rows (they do not depend on them)
-  constexpr int WS = DIRECT ? kGemmWeightSets : 2;
+  constexpr int WS = DIRECT ? gemm_weight_sets<MSUB>() : 2;
   u32x4 wv[WS][NW];
   uint32_t sv[WS][NW];
   load_w(0, wv[0], sv[0]);
@@ -362,6 +410,58 @@ __device__ __forceinline__ void gemm_run(
     typename WF::Prep bs[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) bs[i] = WF::prep(sv[i]);
+    if constexpr (MSUB == 8) {
+      // 128-row blocks (accumulators in the accumulation registers, updated
+      // in place by mfma_acc).  One activation fragment set: fragment q of
+      // step j + 1 is read from LDS right after its last MFMA of step j.
+      // Weight tile s + 1 (step-major order) is dequantised while the Q MFMAs
+      // of tile s run; for NVFP4 its 8 VALU ops are placed one after each
+      // MFMA (scheduling barriers keep that order).
+      f16x8 a[Q], b[2];
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        a[q] = __builtin_bit_cast(f16x8, *(const u32x4 *)(abuf + lds_chunk(r, 4 * g) * 8 + q * kBM * kUnitK));
+      b[0] = WF::dequant(wv[0][0], bs[0], 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          const int st = j * NW + i;
+          const bool next = st + 1 < 4 * NW;
+          const int ni = (i + 1) % NW, nj = j + (i + 1) / NW;
+          constexpr bool kSpread = FMT == MOE_FORMAT_NVFP4;
+          if (!kSpread && next) b[(st + 1) & 1] = WF::dequant(wv[ni][nj], bs[ni], nj);
+          f16x2 c[4];
+          const uint32_t wn = wv[ni][nj];
+          f16x2 ss = {};
+          if constexpr (kSpread) ss = f16x2{bs[ni].s[nj >> 1], bs[ni].s[nj >> 1]};
+          auto deq_step = [&](int k) {  // k: a constant once the loops are unrolled
+            switch (k) {
+              case 0: c[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wn, 1.0f, 0); break;
+              case 2: c[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wn, 1.0f, 1); break;
+              case 4: c[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wn, 1.0f, 2); break;
+              case 6: c[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wn, 1.0f, 3); break;
+              default: c[k >> 1] = c[k >> 1] * ss;
+            }
+          };
+#pragma unroll
+          for (int q = 0; q < Q; ++q) {
+            mfma_acc(acc[q][i], a[q], b[st & 1]);
+            if (i == NW - 1 && j < 3)
+              a[q] = __builtin_bit_cast(
+                  f16x8, *(const u32x4 *)(abuf + lds_chunk(r, 4 * g + j + 1) * 8 + q * kBM * kUnitK));
+            if (kSpread && next && q < 8) deq_step(q);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (kSpread && next) {
+#pragma unroll
+            for (int k = Q; k < 8; ++k) deq_step(k);
+            b[(st + 1) & 1] = f16x8{c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
+          }
+        }
+      }
+      return;
+    }
     f16x8 a[Q], b[2][NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) b[0][i] = WF::dequant(wv[i][0], bs[i], 0);
@@ -463,6 +563,7 @@ __device__ __forceinline__ void gemm_run(
     }
   }
   if (!wave_on) return;  // no barrier follows
+  if constexpr (MSUB == 8) mfma_acc_drain();
 
   // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
   if (GATED) {
@@ -516,9 +617,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int E, int ncb, uint32_t a_bytes,
     Nvfp4 w0, Nvfp4 w1,                  // GATED: gate, up; else w0 = down
     int K, int N, uint16_t *__restrict__ out) {
-  static_assert(MSUB == 4, "one instantiation per 16-row group count below");
+  static_assert(MSUB == 4 || MSUB == 8, "one instantiation per 16-row group count below");
   constexpr int BM = kBM * MSUB;
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[gemm_lds_bufs<GATED>()][BM * kUnitK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[gemm_lds_bufs<MSUB, GATED>()][BM * kUnitK];
   __shared__ float s_rowscale[BM];
   const int per_xcd = gridDim.x / kXcds;
   const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -530,10 +631,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   gemm_run<MSUB, Q, NP, GATED, FMT>(a_src, x_exp, a_max, sorted_pairs, top_k, a_bytes, w0, w1, K, \
                                     N, out, e, row0, mrows, cb, s_a, s_rowscale)
   // the 16-row groups holding rows (uniform)
-  if (mrows > 3 * kBM) MOE_GEMM_RUN(4);
-  else if (mrows > 2 * kBM) MOE_GEMM_RUN(3);
-  else if (mrows > kBM) MOE_GEMM_RUN(2);
-  else MOE_GEMM_RUN(1);
+  if constexpr (MSUB == 4) {
+    if (mrows > 3 * kBM) MOE_GEMM_RUN(4);
+    else if (mrows > 2 * kBM) MOE_GEMM_RUN(3);
+    else if (mrows > kBM) MOE_GEMM_RUN(2);
+    else MOE_GEMM_RUN(1);
+  } else {
+    if (mrows > 4 * kBM) MOE_GEMM_RUN(8);
+    else if (mrows > 2 * kBM) MOE_GEMM_RUN(4);
+    else if (mrows > kBM) MOE_GEMM_RUN(2);
+    else MOE_GEMM_RUN(1);
+  }
 #undef MOE_GEMM_RUN
 }
 
@@ -1011,8 +1119,9 @@ dim3 gemm_grid(int P, int E, int bm, int ncb) {
 template <int MSUB, int FMT>
 int launch_gate_up(const Ws &w, const int32_t *offsets, const int32_t *sorted_pairs, int T,
                    int top_k, int E, Nvfp4 g, Nvfp4 u, int H, int I, hipStream_t s) {
-  const int ncb = (I + 64 * kGemmGateNP - 1) / (64 * kGemmGateNP);
-  MOE_LAUNCH((k_expert_gemm<MSUB, kGemmGateNP, true, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
+  constexpr int NP = kGemmGateNP;
+  const int ncb = (I + 64 * NP - 1) / (64 * NP);
+  MOE_LAUNCH((k_expert_gemm<MSUB, NP, true, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
              dim3(kThreads), 0, s,
              (const uint16_t *)w.x16, (const int32_t *)w.x_exp, w.a_max, offsets, sorted_pairs,
              top_k, E, ncb, (uint32_t)((size_t)T * H * 2), g, u, H, I, w.a);
@@ -1094,6 +1203,8 @@ int gate_up_fmt(const Ws &w, const int32_t *expert_offsets, const int32_t *sorte
                  expert_offsets, E, g, u);
     return MOE_OK;
   }
+  if (gate_up_msub(T, top_k, E) == 8)
+    return launch_gate_up<8, FMT>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
   return launch_gate_up<4, FMT>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
 }
 

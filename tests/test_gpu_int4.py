@@ -186,12 +186,14 @@ def _expert_mlp_check(fmt_gu, fmt_d, T, k, E, H, I, seed):
     assert np.max(row_rel(got, ref)) <= 1e-2
 
 
-# GEMV mode with 8- and 16-row tiles (split and unsplit K) and the GEMM, with
+# GEMV mode with 8- and 16-row tiles (split and unsplit K) and the GEMM with
+# 64- and (T = 1600: 400 rows per expert) 128-row gate/up blocks, with
 # partial K units (H, I odd multiples of 64)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (16, 2, 8, 128, 64),
                                        (24, 4, 16, 256, 128), (37, 4, 8, 192, 128),
-                                       (300, 2, 4, 256, 64), (100, 4, 8, 192, 128)])
+                                       (300, 2, 4, 256, 64), (100, 4, 8, 192, 128),
+                                       (1600, 2, 8, 192, 128)])
 def test_int4_expert_mlp_small(fmt, T, k, E, H, I):
     _expert_mlp_check(fmt, fmt, T, k, E, H, I, seed=T + 3)
 

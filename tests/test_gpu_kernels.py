@@ -465,6 +465,26 @@ def test_expert_mlp_gemm_every_row_group():
     _check_expert_mlp(c, idx, T, k, E, H, I)
 
 
+def test_expert_mlp_gemm_128_row_blocks():
+    # buckets of 384 rows or more on average take the gate/up kernel with
+    # 128-row blocks (accumulators in the accumulation registers): bucket
+    # sizes whose last block holds 1, 17..32, 33..64 and 65..128 rows (each
+    # count of 16-row groups that kernel specialises on), a full block, and
+    # experts of 3, 6 and 14 blocks (block groups of 8 with a shorter last
+    # group); H = 192 leaves half a K unit, I = 64 leaves waves past N
+    sizes = [1, 20, 50, 100, 128, 300, 700, 1773]
+    k, E, H, I = 1, 8, 192, 64
+    T = sum(sizes)
+    assert T * k // min(T * k, E) >= 384
+    c = S.small_case(2025, T, H, I, E, k)
+    rng = np.random.default_rng(12)
+    experts = rng.permutation(E)[:len(sizes)]
+    idx = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in zip(experts, sizes)])
+    idx = idx[rng.permutation(T)].reshape(T, k)
+    assert sorted(np.bincount(idx.ravel(), minlength=E)[experts]) == sorted(sizes)
+    _check_expert_mlp(c, idx, T, k, E, H, I)
+
+
 def _check_expert_mlp(c, idx, T, k, E, H, I):
     layer = W.build_small_layer(c, k)
     off, sp, pr, _ = _bucket_gpu(idx, E)
