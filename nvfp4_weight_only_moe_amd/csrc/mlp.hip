@@ -55,7 +55,7 @@ struct Nvfp4 {
 };
 
 struct WsLayout {
-  size_t x_exp, a_max, x16, a, total;
+  size_t x_exp, a_max, x16, a, a16, total;
   int max_tiles;
 };
 
@@ -92,7 +92,8 @@ int tile_rows(int T, int top_k, int E) {
 }
 
 // Workspace: token exponents [T], per-row max of A [P], the f16 activations
-// [T][H], A [P][I] bf16.  max_tiles bounds the tile count (sum over experts
+// [T][H], A [P][I] bf16 (and, with 128-row blocks, A [P][I] as f16 scaled by
+// its row's power of two).  max_tiles bounds the tile count (sum over experts
 // of ceil(M_e / rows)) for the grids.
 WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
   WsLayout L;
@@ -103,7 +104,9 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
   L.a_max = L.x_exp + moe_align_up((size_t)T * 4, 256);
   L.x16 = L.a_max + moe_align_up(P * 4, 256);
   L.a = L.x16 + moe_align_up((size_t)T * H * 2, 256);
-  L.total = L.a + moe_align_up(P * (size_t)I * 2, 256);
+  L.a16 = L.a + moe_align_up(P * (size_t)I * 2, 256);
+  // 128-row down blocks read A converted to f16 (a copy beside A)
+  L.total = L.a16 + (gate_up_msub(T, top_k, E) == 8 ? moe_align_up(P * (size_t)I * 2, 256) : 0);
   if (L.total < 256) L.total = 256;  // never empty, so T = 0 still gets a valid pointer
   return L;
 }
@@ -268,13 +271,14 @@ constexpr int gemm_weight_sets() { return MSUB == 8 ? 2 : kGemmWeightSets; }
 
 // LDS activation buffers of the tiled-mode kernels
 template <int MSUB, bool GATED>
-constexpr int gemm_lds_bufs() { return GATED ? (MSUB == 8 ? 2 : kGemmLdsBufs) : 2; }
+constexpr int gemm_lds_bufs() { return MSUB == 8 ? 2 : GATED ? kGemmLdsBufs : 2; }
 
 // One block of the tiled mode: rows row0 .. row0 + mrows - 1 (mrows <= 16 Q)
 // of expert e, column block cb.  Q: the 16-row groups holding rows; only
 // those are staged, multiplied and stored.  s_a: the LDS activation buffers
 // [gemm_lds_bufs][16 MSUB * kUnitK]; s_rowscale: [16 MSUB].
-// DIRECT: the activations are f16 in memory (gate/up): buffer loads write
+// DIRECT: the activations are f16 in memory (gate/up; down with 128-row
+// blocks, whose A was converted to f16 beforehand): buffer loads write
 // them straight into LDS (no registers).  Otherwise (down, bf16 A): they go
 // through registers and are converted to f16 with the row's power of two.
 template <int MSUB, int Q, int NP, bool GATED, int FMT>
@@ -283,7 +287,7 @@ __device__ __forceinline__ void gemm_run(
     uint32_t *__restrict__ a_max, const int32_t *__restrict__ sorted_pairs, int top_k,
     uint32_t a_bytes, const Nvfp4 &w0, const Nvfp4 &w1, int K, int N, uint16_t *__restrict__ out,
     int e, int row0, int mrows, int cb, uint16_t (*s_a)[kBM * MSUB * kUnitK], float *s_rowscale) {
-  constexpr bool DIRECT = GATED;
+  constexpr bool DIRECT = GATED || MSUB == 8;
   constexpr int BM = kBM * MSUB;
   constexpr int NW = GATED ? 2 * NP : NP;  // weight row tiles streamed by a wave
   using WF = WeightFmt<FMT>;
@@ -643,6 +647,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else MOE_GEMM_RUN(1);
   }
 #undef MOE_GEMM_RUN
+}
+
+// For the 128-row down blocks: A [P][I] bf16 -> f16 times its row's power of
+// two 2^(14 - exponent of max|A|) (exact, as the 64-row kernel converts it
+// while staging), once per element instead of once per column block, so
+// that the down kernel stages A into LDS with direct loads.
+__global__ __launch_bounds__(kThreads) void k_a_f16(const uint16_t *__restrict__ a,
+                                                    const uint32_t *__restrict__ a_max, int P,
+                                                    int I, uint16_t *__restrict__ a16) {
+  const int per_row = I / 8;  // 16-byte chunks per row
+  const size_t n = (size_t)P * per_row;
+  for (size_t c = (size_t)blockIdx.x * kThreads + threadIdx.x; c < n;
+       c += (size_t)gridDim.x * kThreads) {
+    const int row = (int)(c / per_row);
+    const float f = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[row])));
+    const u32x4 v = *(const u32x4 *)(a + c * 8);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16 lo = (f16)(__uint_as_float(v[i] << 16) * f);
+      const f16 hi = (f16)(__uint_as_float(v[i] & 0xFFFF0000u) * f);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *(u32x4 *)(a16 + c * 8) = o;
+  }
 }
 
 // ------------------------------------------------------- GEMV mode ----
@@ -1070,7 +1099,7 @@ struct Ws {
   WsLayout L;
   int32_t *x_exp;
   uint32_t *a_max;
-  uint16_t *x16, *a;
+  uint16_t *x16, *a, *a16;
 };
 
 Ws ws_ptrs(void *workspace, const WsLayout &L) {
@@ -1081,6 +1110,7 @@ Ws ws_ptrs(void *workspace, const WsLayout &L) {
   w.a_max = (uint32_t *)(ws + L.a_max);
   w.x16 = (uint16_t *)(ws + L.x16);
   w.a = (uint16_t *)(ws + L.a);
+  w.a16 = (uint16_t *)(ws + L.a16);
   return w;
 }
 
@@ -1132,8 +1162,16 @@ template <int MSUB, int FMT>
 int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nvfp4 d, int H,
                 int I, uint16_t *y, hipStream_t s) {
   const int ncb = (H + 64 * kGemmDownNP - 1) / (64 * kGemmDownNP);
+  const uint16_t *a = w.a;
+  if (MSUB == 8) {
+    const long long chunks = (long long)T * top_k * (I / 8);
+    const int blocks = (int)std::min<long long>((chunks + kThreads - 1) / kThreads, 4096);
+    MOE_LAUNCH(k_a_f16, dim3(blocks), dim3(kThreads), 0, s, (const uint16_t *)w.a,
+               (const uint32_t *)w.a_max, T * top_k, I, w.a16);
+    a = w.a16;
+  }
   MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
-             dim3(kThreads), 0, s, (const uint16_t *)w.a, (const int32_t *)nullptr, w.a_max, offsets,
+             dim3(kThreads), 0, s, a, (const int32_t *)nullptr, w.a_max, offsets,
              (const int32_t *)nullptr, top_k, E, ncb, (uint32_t)((size_t)T * top_k * I * 2), d, d,
              I, H, y);
   return MOE_OK;
@@ -1235,6 +1273,8 @@ int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E
 #undef MOE_GEMV_DN
     return MOE_OK;
   }
+  if (gate_up_msub(T, top_k, E) == 8)
+    return launch_down<8, FMT>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
   return launch_down<4, FMT>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
 }
 
