@@ -152,6 +152,26 @@ __device__ __forceinline__ float gelu_tanh(float g) {
 __device__ __forceinline__ void mfma_acc(f32x4 &acc, const f16x8 &a, const f16x8 &b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The same without the two wait states, for an MFMA whose operands no VALU
+// op has written in the two instructions before it (the caller pins that
+// order with scheduling barriers).
+__device__ __forceinline__ void mfma_acc_nw(f32x4 &acc, const f16x8 &a, const f16x8 &b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Zeroes the accumulators in the accumulation registers, then waits the two
+// wait states after those writes, so that any MFMA may read them next.
+template <int Q, int NW>
+__device__ __forceinline__ void mfma_acc_zero(f32x4 (&acc)[Q][NW]) {
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      acc[q][i] = f32x4{0, 0, 0, 0};
+      asm volatile("" : "+a"(acc[q][i]));
+    }
+  asm volatile("s_nop 1" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 __device__ __forceinline__ void mfma_acc_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -399,10 +419,14 @@ __device__ __forceinline__ void gemm_run(
   };
 
   f32x4 acc[Q][NW];
+  if constexpr (MSUB == 8) {
+    mfma_acc_zero(acc);
+  } else {
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
+    for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
+      for (int i = 0; i < NW; ++i) acc[q][i] = f32x4{0, 0, 0, 0};
+  }
 
   // One K unit: 4 steps of 32.  The weights of step j + 1 are dequantised
   // while the MFMAs of step j run (two register sets), and scheduling-group
@@ -450,7 +474,11 @@ __device__ __forceinline__ void gemm_run(
           };
 #pragma unroll
           for (int q = 0; q < Q; ++q) {
-            mfma_acc(acc[q][i], a[q], b[st & 1]);
+            // the tile's first MFMA reads b just completed by a VALU op; the
+            // later ones follow a dequant step writing the next tile's
+            // registers, or an LDS read (waited for by counter)
+            if (kSpread && q > 0) mfma_acc_nw(acc[q][i], a[q], b[st & 1]);
+            else mfma_acc(acc[q][i], a[q], b[st & 1]);
             if (i == NW - 1 && j < 3)
               a[q] = __builtin_bit_cast(
                   f16x8, *(const u32x4 *)(abuf + lds_chunk(r, 4 * g + j + 1) * 8 + q * kBM * kUnitK));
