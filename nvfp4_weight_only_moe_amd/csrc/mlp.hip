@@ -28,8 +28,9 @@
 //       buffer loads straight into MFMA operand registers.
 //     - tiled mode (prefill): 16*MSUB rows per tile staged in LDS per K unit
 //       and shared by the 4 waves, weights streamed once per tile; 64-row
-//       tiles, and for gate/up 128-row tiles once buckets average 384 rows
-//       (accumulators held in place in the accumulation registers).
+//       tiles, or 128-row tiles once buckets average 192 rows (their
+//       accumulators held in place in the accumulation registers; down then
+//       reads A converted once to row-scaled f16).
 //    Gate/up epilogue: GELU-tanh gating, A rounded to bf16 (row-major
 //    [P][I] in sorted-row order), per-row max|A| by atomicMax on the float
 //    bits (an integer max: order-independent).  Down rescales A to f16 by that maximum's power
@@ -69,15 +70,15 @@ int choose_msub(int T, int top_k, int E) {
   return 4;
 }
 
-// rows per gate/up block in tiled mode: 128 (MSUB = 8) once buckets hold 384
-// rows or more on average (measured crossover: equal at 256 rows, 8% faster
-// at 512, 13% at 1024; slower below), else 64
+// rows per expert-GEMM block in tiled mode: 128 (MSUB = 8) once buckets hold
+// 192 rows or more on average (measured with Zipf routing: 4% slower at 128
+// rows, 4% faster at 256, 9% at 512, 15% at 1024), else 64
 int gate_up_msub(int T, int top_k, int E) {
   const int m = choose_msub(T, top_k, E);
   if (m == 1) return 1;
   const long long P = (long long)T * top_k;
   const long long buckets = P < E ? P : E;
-  return P / buckets >= 384 ? 8 : m;
+  return P / buckets >= 192 ? 8 : m;
 }
 
 // Few rows per expert (decode): the GEMV-mode kernels.  Otherwise tiled mode.
@@ -279,13 +280,14 @@ __device__ __forceinline__ int lds_chunk(int m, int c) { return m * 16 + (c ^ (m
 // activation buffers of that pipeline: kGemmLdsBufs - 1 units in flight.
 constexpr int kGemmWeightSets = 3;
 constexpr int kGemmLdsBufs = 3;
-// 128-row gate/up blocks (MSUB = 8, for buckets of many rows): each wave
-// keeps 8 row groups x 2 gate + 2 up row tiles = 128 accumulators, which
-// fill the accumulation registers (mfma_acc), so each dequantised weight
-// fragment feeds 8 MFMAs instead of 4 -- half the dequant VALU work per
-// MFMA.  The other 128 registers of a wave at two waves per SIMD then hold
-// one activation fragment set, two weight sets and a two-buffer LDS ring
-// (64 KB: two workgroups per CU).
+// 128-row blocks (MSUB = 8, for buckets of many rows): each wave keeps 8 row
+// groups x 4 weight row tiles (gate/up: 2 gate + 2 up; down: 4) = 128
+// accumulators, which fill the accumulation registers (mfma_acc), so each
+// dequantised weight fragment feeds 8 MFMAs instead of 4 -- half the dequant
+// VALU work per MFMA.  The other 128 registers of a wave at two waves per
+// SIMD then hold one activation fragment set and two weight sets; the
+// activations come through a two-buffer LDS ring (64 KB: two workgroups per
+// CU) filled by direct loads, for down from a copy of A converted to f16.
 template <int MSUB>
 constexpr int gemm_weight_sets() { return MSUB == 8 ? 2 : kGemmWeightSets; }
 

@@ -187,7 +187,7 @@ def _expert_mlp_check(fmt_gu, fmt_d, T, k, E, H, I, seed):
 
 
 # GEMV mode with 8- and 16-row tiles (split and unsplit K) and the GEMM with
-# 64- and (T = 1600: 400 rows per expert) 128-row gate/up blocks, with
+# 64- and (T = 1600: 400 rows per expert) 128-row blocks, with
 # partial K units (H, I odd multiples of 64)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,k,E,H,I", [(1, 2, 8, 128, 64), (16, 2, 8, 128, 64),

@@ -466,7 +466,7 @@ def test_expert_mlp_gemm_every_row_group():
 
 
 def test_expert_mlp_gemm_128_row_blocks():
-    # buckets of 384 rows or more on average take the gate/up kernel with
+    # buckets of 192 rows or more on average take the expert GEMMs with
     # 128-row blocks (accumulators in the accumulation registers): bucket
     # sizes whose last block holds 1, 17..32, 33..64 and 65..128 rows (each
     # count of 16-row groups that kernel specialises on), a full block, and
@@ -475,7 +475,7 @@ def test_expert_mlp_gemm_128_row_blocks():
     sizes = [1, 20, 50, 100, 128, 300, 700, 1773]
     k, E, H, I = 1, 8, 192, 64
     T = sum(sizes)
-    assert T * k // min(T * k, E) >= 384
+    assert T * k // min(T * k, E) >= 192
     c = S.small_case(2025, T, H, I, E, k)
     rng = np.random.default_rng(12)
     experts = rng.permutation(E)[:len(sizes)]
