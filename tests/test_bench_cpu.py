@@ -35,7 +35,8 @@ def test_stage_lists():
 
 def test_committed_counter_summaries_name_the_dominant_kernels():
     here = os.path.dirname(bench.__file__)
-    for wl, T in (("moe_layer_decode_T64", 64), ("moe_layer_prefill_T2048_zipf1.2", 2048)):
+    for wl, T in (("moe_layer_decode_T64", 64), ("moe_layer_prefill_T2048_zipf1.2", 2048),
+                  ("moe_layer_prefill_T16384_zipf1.2_outliers", 16384)):
         path = os.path.join(here, "profiles", f"hbm_traffic__{wl}.txt")
         rec = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
         assert rec["kernel"].strip() == bench.gate_up_kernel_name(T, 8, 128)
