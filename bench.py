@@ -216,7 +216,7 @@ def expert_bytes_per_expert(H, I, fmt="nvfp4"):
 
 def gate_up_kernel_name(T, K, E, fmt="nvfp4"):
     """The kernel nvfp4_expert_gate_up launches for this shape (the dispatch
-    rule of the library: few rows per expert -> GEMV mode; 192 or more ->
+    rule of the library: few rows per expert -> GEMV mode; 128 or more ->
     128-row GEMM blocks)."""
     P = T * K
     avg = P // max(1, min(P, E))
@@ -224,7 +224,7 @@ def gate_up_kernel_name(T, K, E, fmt="nvfp4"):
     if avg < 24:
         rows = 8 if P <= 4 * E else 16
         return f"k_expert_gemv<{rows}, 2, true, 4, {f}, 1>"   # ..., prefetch depth 1
-    return f"k_expert_gemm<{8 if avg >= 192 else 4}, 2, true, {f}>"
+    return f"k_expert_gemm<{8 if avg >= 128 else 4}, 2, true, {f}>"
 
 
 def profiled_traffic(workload, kernel):

@@ -71,14 +71,18 @@ int choose_msub(int T, int top_k, int E) {
 }
 
 // rows per expert-GEMM block in tiled mode: 128 (MSUB = 8) once buckets hold
-// 192 rows or more on average (measured with Zipf routing: 4% slower at 128
-// rows, 4% faster at 256, 9% at 512, 15% at 1024), else 64
+// 128 rows or more on average, else 64.  Measured against 64-row blocks at
+// 2048 tokens (128 rows per expert on average): gate/up 198 -> 176 us with
+// Zipf routing, 199 -> 179 us with uniform routing; 4-15% faster from 256
+// rows up.  (Before the gate/up blocks were spread over the XCDs by cost,
+// the crossover lay near 192 rows.)
+constexpr int kMsub8From = 128;
 int gate_up_msub(int T, int top_k, int E) {
   const int m = choose_msub(T, top_k, E);
   if (m == 1) return 1;
   const long long P = (long long)T * top_k;
   const long long buckets = P < E ? P : E;
-  return P / buckets >= 192 ? 8 : m;
+  return P / buckets >= kMsub8From ? 8 : m;
 }
 
 // Few rows per expert (decode): the GEMV-mode kernels.  Otherwise tiled mode.
@@ -204,10 +208,11 @@ __device__ __forceinline__ void mfma_acc_drain() {
 // itself, moved accumulators between register files or spilled them.
 //
 // Order of the workgroups: a 1-D grid, a multiple of the 8 XCDs.  Hardware
-// hands workgroup b to XCD b % 8; b is mapped to the logical index
-// (b % 8) * (grid / 8) + b / 8 so that each XCD walks one contiguous range of
-// the logical order: expert, then groups of kRowGroup row blocks, and in a
-// group column block, then row block.  The row blocks that reuse a column
+// hands workgroup b to XCD b % 8; each XCD walks one contiguous range of the
+// logical order (expert, then groups of kRowGroup row blocks, and in a group
+// column block, then row block), workgroup b taking block b / 8 of XCD
+// b % 8's range.  Down cuts the order into ranges of equal block counts,
+// gate/up into ranges of about equal cost (find_block).  The row blocks that reuse a column
 // block's weights run side by side on one XCD and hit its L2 instead of HBM,
 // and so do the column blocks that reuse a group's activations.
 constexpr int kUnitK = 128;
@@ -217,11 +222,32 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // Row blocks per group of the block order (below).
 constexpr int kRowGroup = 8;
 
-// Logical block `L` of the block order: expert e holds ceil(M_e / bm) * ncb
-// consecutive blocks (row block m0 / bm, column block cb).  Lane l takes
-// experts PER*l .. PER*l + PER - 1; one DPP prefix sum over the lanes
-// (scalar results).  False past the last block.
-__device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int ncb, int L,
+// 16-row groups multiplied for a block of `rows` rows (the kernel's
+// dispatch below)
+__device__ __forceinline__ int block_groups(int rows, int msub) {
+  if (msub == 8) return rows > 64 ? 8 : rows > 32 ? 4 : rows > 16 ? 2 : 1;
+  return rows > 48 ? 4 : rows > 32 ? 3 : rows > 16 ? 2 : 1;
+}
+
+// Cost of a block in the balanced split: kBlockCost + its 16-row groups (a
+// block's weight stream, dequantisation and epilogue set-up do not depend on
+// its rows).  Measured at 2048 tokens with Zipf routing, gate/up: 4 -> 185
+// us, 6 -> 184, 8 -> 181 (equal-count ranges: 211).
+constexpr int kBlockCost = 8;
+
+// The block of this workgroup: expert e, row offset m0 in its bucket, column
+// block cb; false when the workgroup has none.  Expert e holds
+// ceil(M_e / bm) * ncb consecutive blocks of the block order (lane l takes
+// experts PER*l .. PER*l + PER - 1; DPP prefix sums over the lanes, scalar
+// results).  Workgroup b runs on XCD x = b % 8 as its j = b / 8-th
+// workgroup and takes block j of XCD x's range of the order.
+// BALANCED = false: 8 ranges of gridDim.x / 8 blocks.  BALANCED = true: the
+// ranges hold about equal cost (kBlockCost + 16-row groups per block), each
+// at most gridDim.x / 8 blocks long; used where blocks with few rows are
+// common beside full ones (the Zipf tail beside the head experts), whose
+// count-equal ranges differ in work by up to a third.
+template <bool BALANCED>
+__device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int msub, int ncb,
                            int grp, int &e, int &m0, int &cb) {
   constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
   const int lane = threadIdx.x & 63;
@@ -230,15 +256,57 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
 #pragma unroll
   for (int i = 0; i <= PER; ++i)
     off[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ro, (uint32_t)(PER * lane + i) * 4u, 0, 0);
-  int nblk[PER], sum = 0;
+  int nblk[PER], sum = 0, cs[PER], csum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    nblk[i] = PER * lane + i < E ? (off[i + 1] - off[i] + bm - 1) / bm : 0;
+    const int n = PER * lane + i < E ? off[i + 1] - off[i] : 0;
+    nblk[i] = (n + bm - 1) / bm;
     sum += nblk[i] * ncb;
+    if (BALANCED) {
+      const int full = n / bm, rem = n - full * bm;
+      cs[i] = ncb * (full * (kBlockCost + msub) + (rem > 0 ? kBlockCost + block_groups(rem, msub) : 0));
+      csum += cs[i];
+    }
   }
   const int incl = wave_incl_scan(sum);
-  if (L >= __builtin_amdgcn_readlane(incl, kWave - 1)) return false;
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
   const int excl = incl - sum;
+  const int cap = (int)gridDim.x / kXcds, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  int L;
+  if (!BALANCED) {
+    L = x * cap + j;
+  } else {
+    // range starts s_1 .. s_7 at the blocks where the cost prefix reaches
+    // y/8 of the total (uniform cost per block inside an expert), clamped so
+    // that every range has at most cap blocks and the later XCDs can still
+    // take the rest
+    const int cincl = wave_incl_scan(csum);
+    const int C = __builtin_amdgcn_readlane(cincl, kWave - 1), cexcl = cincl - csum;
+    int prev = 0, lo = 0, hi = total;
+    for (int y = 1; y < kXcds; ++y) {
+      const int t = (int)((long long)y * C / kXcds);
+      const unsigned long long bal = __ballot(t >= cexcl && t < cincl);
+      int at = total;
+      if (bal) {
+        int cb0 = cexcl, bb0 = excl, r = -1;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          if (r < 0 && t >= cb0 && t < cb0 + cs[i])
+            r = bb0 + (int)((long long)(t - cb0) * (nblk[i] * ncb) / cs[i]);
+          cb0 += cs[i];
+          bb0 += nblk[i] * ncb;
+        }
+        at = __builtin_amdgcn_readlane(r, (int)__builtin_ctzll(bal));
+      }
+      const int sy = max(prev, max(min(at, prev + cap), total - (kXcds - y) * cap));
+      if (y == x) lo = sy;
+      if (y == x + 1) hi = sy;
+      prev = sy;
+    }
+    L = lo + j;
+    if (L >= hi) return false;
+  }
+  if (L >= total) return false;
   const int src = (int)__builtin_ctzll(__ballot(L >= excl && L < incl));
   int ee = 0, rem = 0, nb = 1, base = excl;
 #pragma unroll
@@ -655,10 +723,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int BM = kBM * MSUB;
   __shared__ __attribute__((aligned(16))) uint16_t s_a[gemm_lds_bufs<MSUB, GATED>()][BM * kUnitK];
   __shared__ float s_rowscale[BM];
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   int e, m0, cb;
-  if (!find_block(offsets, E, BM, ncb, L, kRowGroup, e, m0, cb)) return;  // uniform over the workgroup
+  // gate/up: cost-balanced XCD ranges; down (short blocks, whose start-up
+  // latency the balanced split's extra work would add to): equal counts
+  if (!find_block<GATED>(offsets, E, BM, MSUB, ncb, kRowGroup, e, m0, cb)) return;  // uniform
   const int row0 = offsets[e] + m0;
   const int mrows = min(BM, offsets[e + 1] - row0);  // >= 1: a block holds rows
 #define MOE_GEMM_RUN(Q)                                                                          \

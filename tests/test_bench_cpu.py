@@ -22,7 +22,8 @@ def test_gate_up_kernel_follows_the_dispatch_rule():
     assert bench.gate_up_kernel_name(64, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0, 1>"
     assert bench.gate_up_kernel_name(4, 8, 128) == "k_expert_gemv<8, 2, true, 4, 0, 1>"
     assert bench.gate_up_kernel_name(128, 8, 128) == "k_expert_gemv<16, 2, true, 4, 0, 1>"
-    assert bench.gate_up_kernel_name(2048, 8, 128) == "k_expert_gemm<4, 2, true, 0>"
+    assert bench.gate_up_kernel_name(2048, 8, 128) == "k_expert_gemm<8, 2, true, 0>"
+    assert bench.gate_up_kernel_name(2040, 8, 128) == "k_expert_gemm<4, 2, true, 0>"
     assert bench.gate_up_kernel_name(3072, 8, 128) == "k_expert_gemm<8, 2, true, 0>"
     assert bench.gate_up_kernel_name(16384, 8, 128) == "k_expert_gemm<8, 2, true, 0>"
     assert bench.gate_up_kernel_name(64, 8, 128, "aff4") == "k_expert_gemv<8, 2, true, 4, 2, 1>"

@@ -466,7 +466,7 @@ def test_expert_mlp_gemm_every_row_group():
 
 
 def test_expert_mlp_gemm_128_row_blocks():
-    # buckets of 192 rows or more on average take the expert GEMMs with
+    # buckets of 128 rows or more on average take the expert GEMMs with
     # 128-row blocks (accumulators in the accumulation registers): bucket
     # sizes whose last block holds 1, 17..32, 33..64 and 65..128 rows (each
     # count of 16-row groups that kernel specialises on), a full block, and
@@ -475,13 +475,33 @@ def test_expert_mlp_gemm_128_row_blocks():
     sizes = [1, 20, 50, 100, 128, 300, 700, 1773]
     k, E, H, I = 1, 8, 192, 64
     T = sum(sizes)
-    assert T * k // min(T * k, E) >= 192
+    assert T * k // min(T * k, E) >= 128
     c = S.small_case(2025, T, H, I, E, k)
     rng = np.random.default_rng(12)
     experts = rng.permutation(E)[:len(sizes)]
     idx = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in zip(experts, sizes)])
     idx = idx[rng.permutation(T)].reshape(T, k)
     assert sorted(np.bincount(idx.ravel(), minlength=E)[experts]) == sorted(sizes)
+    _check_expert_mlp(c, idx, T, k, E, H, I)
+
+
+@pytest.mark.parametrize("E,sizes", [
+    # 128-row blocks: one expert of 12 blocks beside tails of 1..129 rows and empty experts
+    (16, [1500, 600, 300, 129, 64, 40, 17, 16, 5, 1]),
+    # 64-row blocks: the same skew over more experts, most of them small
+    (64, [900, 300, 65, 48, 33, 20, 17, 9, 3, 2, 1, 1, 1] + [4] * 30),
+])
+def test_expert_mlp_gemm_cost_balanced_split(E, sizes):
+    # the gate/up blocks are spread over the XCDs in ranges of equal cost
+    # (not equal counts): skewed buckets with empty experts, where the ranges
+    # differ most from the count split and some reach their length cap
+    k, H, I = 1, 192, 64
+    T = sum(sizes)
+    c = S.small_case(2026 + E, T, H, I, E, k)
+    rng = np.random.default_rng(E)
+    experts = rng.permutation(E)[:len(sizes)]
+    idx = np.concatenate([np.full(n, e, dtype=np.int32) for e, n in zip(experts, sizes)])
+    idx = idx[rng.permutation(T)].reshape(T, k)
     _check_expert_mlp(c, idx, T, k, E, H, I)
 
 
