@@ -154,7 +154,8 @@ int moe_route(const uint16_t *x, const uint16_t *w_router, const uint16_t *route
  *   expert_offsets  out [E+1] int32   bucket e is sorted_pairs[off[e] .. off[e+1])
  *   sorted_pairs    out [T*top_k] int32 pair ids in sorted order
  *   pair_rank       out [T*top_k] int32 position of pair p in sorted_pairs
- *   workspace       >= moe_bucket_workspace_bytes(T, top_k, E) bytes; its
+ *   workspace       >= moe_bucket_workspace_bytes(T, top_k, E) bytes (the size
+ *                   also holds moe_route_bucket's split router sums); its
  *                   first int32 is the device error word: the number of pairs
  *                   whose id was outside [0, E).  Such pairs are placed after
  *                   every bucket (positions >= off[E]), go to no expert and
@@ -170,15 +171,21 @@ size_t moe_bucket_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
 
 /*
  * moe_route_bucket -- moe_route followed by moe_bucket in one call, with the
- * same arguments as the two calls and the same output bytes (topk_idx,
- * topk_w, topk_w_raw, logits, expert_offsets, sorted_pairs, pair_rank and the
- * workspace error word; logits may be NULL as in moe_route, which then runs
- * as moe_route + moe_bucket).  For decode batches (T <= 64, H <= 4096) the top-k
- * selection and the bucketing run in one kernel after the logits kernel,
- * which saves a launch on the latency-bound decode path: one wave per token
- * over ceil(T/4) workgroups, the last of which to finish does the bucketing
- * (no workgroup waits for another).  Otherwise it issues the two calls.
- *   workspace  >= moe_bucket_workspace_bytes(T, top_k, E) bytes (as moe_bucket);
+ * same arguments as the two calls.  For decode batches (T <= 64, H <= 4096)
+ * the output bytes are those of the two calls (topk_idx, topk_w, topk_w_raw,
+ * logits, expert_offsets, sorted_pairs, pair_rank and the workspace error
+ * word), and the top-k selection and the bucketing run in one kernel after
+ * the logits kernel, which saves a launch on the latency-bound decode path:
+ * one wave per token over ceil(T/4) workgroups, the last of which to finish
+ * does the bucketing (no workgroup waits for another).  For more tokens the
+ * logits are split along the hidden dimension over more workgroups, whose
+ * partial sums (in the workspace) the selection kernel adds in a fixed order:
+ * deterministic, within moe_route's error bar, but they may differ from
+ * moe_route's logits in the last bits, and ids or weights may differ where
+ * two logits are that close; the bucketing is moe_bucket's of the ids chosen.
+ * logits may be NULL as in moe_route.
+ *   workspace  >= moe_bucket_workspace_bytes(T, top_k, E) bytes (as moe_bucket,
+ *              plus the split's partial sums: up to 8 * T * E + 8 * T floats);
  *              word 1 is the call's arrival counter (no initial value needed)
  * Errors: those of moe_route and moe_bucket, checked before any work is
  * queued.
@@ -195,8 +202,9 @@ int moe_route_bucket(const uint16_t *x, const uint16_t *w_router, const uint16_t
  * first stage on the same x: nvfp4_expert_prep(x) when norm_weight is NULL,
  * else nvfp4_expert_prep_rmsnorm(x, norm_weight, norm_eps) (the learned norm
  * of the expert input, "Gemma 4 26B-A4B (MoE) - Core AI", Architecture code
- * sketch).  Same arguments as those calls and the same output bytes,
- * including the expert workspace's f16 rows; queue nvfp4_expert_gate_up and
+ * sketch).  Same arguments as those calls and the same output bytes as
+ * moe_route_bucket followed by the prep call, including the expert
+ * workspace's f16 rows; queue nvfp4_expert_gate_up and
  * nvfp4_expert_down after it.  For decode batches (moe_route_bucket's
  * one-launch path) the selection kernel's waves also write the expert input,
  * one token row each, beside the bucketing: one launch fewer.

@@ -221,16 +221,36 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_scatter(
   scatter_rounds<kBucketThreads>(s_b, n, p0, nb, s_run, s_wcnt, sorted, rank);
 }
 
-size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_off) {
+// Workspace: error word and arrival counter, per-chunk bucket counts and
+// bases, then (for moe_route_bucket with K-split router logits) the router's
+// partial dot products [ks][T][E] and partial sums of squares [ks][T].
+size_t bucket_ws_layout(int T, int top_k, int E, size_t *cnt_off, size_t *base_off,
+                        size_t *route_off = nullptr) {
   const size_t P = (size_t)T * top_k;
   const size_t nchunks = (P + kChunk - 1) / kChunk;
   const size_t nb = (size_t)E + 1;
   *cnt_off = 256;
   *base_off = *cnt_off + moe_align_up(nchunks * nb * 4, 256);
-  return *base_off + moe_align_up(nchunks * nb * 4, 256);
+  const size_t ro = *base_off + moe_align_up(nchunks * nb * 4, 256);
+  if (route_off) *route_off = ro;
+  const size_t ks = (size_t)route_split_ks(T, E);
+  return ro + (ks > 0 ? moe_align_up(ks * T * E * 4, 256) + moe_align_up(ks * T * 4, 256) : 0);
 }
 
 }  // namespace
+}  // namespace moe
+
+namespace moe {
+// The K-split router's partial buffers in a moe_bucket workspace (valid when
+// route_split_ks(T, E) > 0).
+__attribute__((visibility("hidden"))) void route_partials(void *workspace, int T, int top_k, int E,
+                                                          float **part, float **pss) {
+  size_t a, b, ro;
+  bucket_ws_layout(T, top_k, E, &a, &b, &ro);
+  const int ks = route_split_ks(T, E);
+  *part = (float *)((char *)workspace + ro);
+  *pss = (float *)((char *)workspace + ro + moe_align_up((size_t)ks * T * E * 4, 256));
+}
 }  // namespace moe
 
 namespace moe {

@@ -187,12 +187,17 @@ constexpr int kWideExp16Below = 2048;
 // expert (EXP >= E) of its 64 tokens, writes their logits into LDS (over the
 // weight staging area, free after the K loop) instead of memory, and its
 // waves then select for the tokens from there.
-template <int EXP, bool SELECT>
+// SPLIT (K-split, moe_route_bucket): workgroup z of gridDim.z takes K chunks
+// [z n / Z, (z + 1) n / Z) and writes its raw dot products into part[z][t][e]
+// and (expert block 0) the token's sum of squares over them into pss[z][t];
+// k_route_select_split finishes the logits.
+template <int EXP, bool SELECT, bool SPLIT = false>
 __global__ __launch_bounds__(256) void k_route_logits_wide(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ scale, const float *__restrict__ bias, int T, int H, int E,
     float eps, float *__restrict__ logits, const uint16_t *__restrict__ pes, int K,
-    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw) {
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ topk_w_raw,
+    float *__restrict__ part, float *__restrict__ pss) {
   __shared__ __attribute__((aligned(16))) uint16_t s_xh[kWideTok * kWideLd];
   __shared__ __attribute__((aligned(16))) uint16_t s_xl[kWideTok * kWideLd];
   constexpr int NF = EXP / 16;  // 16-expert MFMA column tiles per wave
@@ -252,8 +257,13 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
   f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0, 0, 0, 0};
-  load(0);
-  for (int kc = 0; kc < H; kc += kWideKC) {
+  const int nchunks = (H + kWideKC - 1) / kWideKC;
+  const int cb = SPLIT ? (int)(blockIdx.z * nchunks / gridDim.z) : 0;
+  const int ce = SPLIT ? (int)((blockIdx.z + 1) * nchunks / gridDim.z) : nchunks;
+  // the chunk past ce (the last prefetch) reads zeros, or the next slice's
+  // first chunk, which is never stored
+  load(cb * kWideKC);
+  for (int kc = cb * kWideKC; kc < ce * kWideKC; kc += kWideKC) {
     store();
     __syncthreads();
     load(kc + kWideKC);  // next chunk in flight during the MFMAs
@@ -280,6 +290,20 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
     if ((tid & 15) == 0) s_ss[srow + 16 * h] = v;
   }
   __syncthreads();
+  if (SPLIT) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int e = e0 + f * 16 + r;
+      if (e >= E) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + wave * 16 + 4 * g + j;
+        if (t < T) part[((size_t)blockIdx.z * T + t) * E + e] = acc[f][j];
+      }
+    }
+    if (blockIdx.x == 0 && tid < kWideTok && t0 + tid < T) pss[(size_t)blockIdx.z * T + t0 + tid] = s_ss[tid];
+    return;
+  }
   const float hs = 1.0f / sqrtf((float)H);
   static_assert(!SELECT || EXP * kWideLd * 2 >= kWideTok * EXP * 4, "LDS logits fit the W area");
   float *s_logit = reinterpret_cast<float *>(s_w);  // SELECT: [kWideTok][E]
@@ -302,6 +326,37 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
       select_token_n<(EXP + kWave - 1) / kWave, true>(s_logit + m * E, pes, t0 + m, E, K,
                                                       topk_idx, topk_w, topk_w_raw);
   }
+}
+
+// The K-split router's end: one wave per token adds the ks partial dot
+// products and sums of squares in slice order, scales them as the unsplit
+// kernel does, writes the logits (when asked) and selects from them.
+template <int NPER>
+__global__ __launch_bounds__(256) void k_route_select_split(
+    const float *__restrict__ part, const float *__restrict__ pss, int ks,
+    const float *__restrict__ bias, int T, int H, int E, float eps, float *__restrict__ logits,
+    const uint16_t *__restrict__ pes, int K, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, float *__restrict__ topk_w_raw) {
+  __shared__ float s_row[4][NPER * kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t < T) {
+    float ss = 0.0f;
+    for (int z = 0; z < ks; ++z) ss += pss[(size_t)z * T + t];
+    const float f = 1.0f / sqrtf(ss / (float)H + eps) * (1.0f / sqrtf((float)H));
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + i * kWave;
+      if (e >= E) break;
+      float a = 0.0f;
+      for (int z = 0; z < ks; ++z) a += part[((size_t)z * T + t) * E + e];
+      const float v = a * f + (bias ? bias[e] : 0.0f);
+      if (logits) logits[(size_t)t * E + e] = v;
+      s_row[wave][e] = v;
+    }
+  }
+  __syncthreads();
+  if (t < T) select_token_n<NPER, true>(s_row[wave], pes, t, E, K, topk_idx, topk_w, topk_w_raw);
 }
 
 __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ logits,
@@ -343,7 +398,7 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
 #define MOE_ALL(EXP)                                                                            \
   MOE_LAUNCH((k_route_logits_wide<EXP, true>), grid, dim3(256), 0, s, x, w_router, router_scale, \
              logit_bias, T, H, E, eps, (float *)nullptr, per_expert_scale, top_k, topk_idx,       \
-             topk_w, topk_w_raw)
+             topk_w, topk_w_raw, (float *)nullptr, (float *)nullptr)
     if (E <= 64) MOE_ALL(64);
     else if (E <= 128) MOE_ALL(128);
     else MOE_ALL(256);
@@ -369,11 +424,11 @@ extern "C" int moe_route(const uint16_t *x, const uint16_t *w_router, const uint
     if (T < kWideExp16Below)
       MOE_LAUNCH((k_route_logits_wide<16, false>), dim3(E / 16, (T + kWideTok - 1) / kWideTok),
                  dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits,
-                 no_pes, 0, no_idx, no_w, no_w);
+                 no_pes, 0, no_idx, no_w, no_w, no_w, no_w);
     else
       MOE_LAUNCH((k_route_logits_wide<32, false>), dim3((E + 31) / 32, (T + kWideTok - 1) / kWideTok),
                  dim3(256), 0, s, x, w_router, router_scale, logit_bias, T, H, E, eps, logits,
-                 no_pes, 0, no_idx, no_w, no_w);
+                 no_pes, 0, no_idx, no_w, no_w, no_w, no_w);
   }
   MOE_LAUNCH(k_route_select, dim3((T + 3) / 4), dim3(256), 0, s, logits, per_expert_scale,
                      T, E, top_k, topk_idx, topk_w, topk_w_raw);
@@ -403,6 +458,39 @@ int route_bucket_checks(const uint16_t *x, const uint16_t *w_router, const uint1
 bool fused_route(int T, int H, int top_k, const float *logits) {
   const int nv = (H + 511) / 512;
   return logits && T > 0 && T <= kFusedMaxT && nv <= kFewMaxV && T * top_k <= 4096;
+}
+
+// moe_route for many tokens with the logits split along K into ks slices,
+// their partial sums in the moe_bucket workspace (arguments validated by the
+// caller; ks <= route_split_ks(T, E), so the workspace holds them)
+int route_split(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
+                 const uint16_t *per_expert_scale, const float *logit_bias, int32_t T, int32_t H,
+                 int32_t E, int32_t top_k, float eps, int32_t *topk_idx, float *topk_w,
+                 float *topk_w_raw, float *logits, int exp, int ks, void *workspace,
+                 hipStream_t s) {
+  float *part, *pss;
+  route_partials(workspace, T, top_k, E, &part, &pss);
+  const uint16_t *no_pes = nullptr;
+  int32_t *no_idx = nullptr;
+  float *no_w = nullptr;
+#define MOE_SPLIT(EXP)                                                                         \
+  MOE_LAUNCH((k_route_logits_wide<EXP, false, true>),                                          \
+             dim3((E + EXP - 1) / EXP, (T + kWideTok - 1) / kWideTok, ks), dim3(256), 0, s, x,   \
+             w_router, router_scale, logit_bias, T, H, E, eps, no_w, no_pes, 0, no_idx, no_w,   \
+             no_w, part, pss)
+  if (exp == 128) MOE_SPLIT(128);
+  else if (exp == 64) MOE_SPLIT(64);
+  else MOE_SPLIT(32);
+#undef MOE_SPLIT
+  if (E <= 2 * kWave)
+    MOE_LAUNCH(k_route_select_split<2>, dim3((T + 3) / 4), dim3(256), 0, s, (const float *)part,
+               (const float *)pss, ks, logit_bias, T, H, E, eps, logits, per_expert_scale, top_k,
+               topk_idx, topk_w, topk_w_raw);
+  else
+    MOE_LAUNCH(k_route_select_split<MOE_MAX_EXPERTS / kWave>, dim3((T + 3) / 4), dim3(256), 0, s,
+               (const float *)part, (const float *)pss, ks, logit_bias, T, H, E, eps, logits,
+               per_expert_scale, top_k, topk_idx, topk_w, topk_w_raw);
+  return MOE_OK;
 }
 
 int route_bucket_fused(const uint16_t *x, const uint16_t *w_router, const uint16_t *router_scale,
@@ -445,7 +533,14 @@ extern "C" int moe_route_bucket(const uint16_t *x, const uint16_t *w_router,
   if (st != MOE_OK) return st;
   if (!fused_route(T, H, top_k, logits)) {
     // T == 0 included: the offsets are all zero, as moe_bucket writes them
-    if (T > 0) {
+    int exp, ks;
+    route_split_cfg(T, E, &exp, &ks);
+    ks = min(ks, (H + kWideKC - 1) / kWideKC);
+    if (ks > 0) {
+      st = route_split(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k, eps,
+                       topk_idx, topk_w, topk_w_raw, logits, exp, ks, workspace, (hipStream_t)stream);
+      if (st != MOE_OK) return st;
+    } else if (T > 0) {
       st = moe_route(x, w_router, router_scale, per_expert_scale, logit_bias, T, H, E, top_k,
                      eps, topk_idx, topk_w, topk_w_raw, logits, stream);
       if (st != MOE_OK) return st;

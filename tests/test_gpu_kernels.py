@@ -323,7 +323,9 @@ def test_invalid_ids_contribute_nothing_through_the_combine():
 def test_route_bucket_matches_oracle_and_separate_calls(T, H, E, k):
     """moe_route_bucket: the routing against the oracle (the same bar as
     moe_route), the bucketing bit-exact against the oracle's bucketing of the
-    experts it chose, and every output byte equal to moe_route + moe_bucket."""
+    experts it chose, and for T <= 64 every output byte equal to moe_route +
+    moe_bucket (more tokens take the K-split logits: moe_route's ids outside
+    near-ties, and the bucketing equal to moe_bucket of its own ids)."""
     router = S.router_params(E % 7, h=H, e=E, zipf=(T == 17))
     x = S.activations(93, T, h=H)
     wr, sc, pes, bias = W.router_to_device(router)
@@ -343,9 +345,13 @@ def test_route_bucket_matches_oracle_and_separate_calls(T, H, E, k):
     moe.moe_route_bucket(xd, wr, sc, pes, bias, k, 1e-6, a["idx"], a["w"], a["w_raw"], a["lg"],
                          a["off"], a["sp"], a["pr"], a["ws"])
     moe.moe_route(xd, wr, sc, pes, bias, k, 1e-6, b["idx"], b["w"], b["w_raw"], b["lg"])
+    split = T > 64
+    if split:
+        b_idx = b["idx"].clone()
+        b["idx"].copy_(a["idx"])
     moe.moe_bucket(b["idx"], E, b["off"], b["sp"], b["pr"], b["ws"])
     torch.cuda.synchronize()
-    for n in ("idx", "w", "w_raw", "lg", "off", "sp", "pr"):
+    for n in ("off", "sp", "pr") if split else ("idx", "w", "w_raw", "lg", "off", "sp", "pr"):
         assert torch.equal(a[n].view(torch.int32), b[n].view(torch.int32)), n
     assert int(a["ws"][:4].view(torch.int32)[0]) == 0
     idx = a["idx"].cpu().numpy()
@@ -361,6 +367,52 @@ def test_route_bucket_matches_oracle_and_separate_calls(T, H, E, k):
         differ = check_route(idx, a["w"].cpu().numpy(), a["w_raw"].cpu().numpy(), ref,
                              r["per_expert_scale"])
         assert len(differ) <= max(1, T // 200)
+        if split:
+            same = np.array([set(u) == set(v) for u, v in zip(idx.tolist(), b_idx.cpu().numpy().tolist())])
+            assert np.all(same | ref["near_tie"])
+
+
+@pytest.mark.parametrize("T,H,E,k", [(65, 2816, 128, 8), (2048, 2816, 128, 8), (4096, 2816, 128, 8),
+                                     (16384, 2816, 128, 8), (700, 4160, 32, 4), (5000, 192, 16, 3),
+                                     (300, 2816, 256, 16)])
+def test_route_bucket_split_logits(T, H, E, k):
+    """The K-split router logits of moe_route_bucket (up to 8 slices of H,
+    64 x 32 or 64 x 128 tiles; H = 4160 ends in half a chunk, H = 192 has
+    two chunks for more slices asked, E = 256 selects from 4 experts per
+    lane): logits within 2e-7 of the oracle with and without a logits buffer,
+    the ids and weights against the oracle, and equal results whether or
+    not the logits are written out."""
+    router = S.router_params(T % 5, h=H, e=E, zipf=(T == 2048 or T == 16384))
+    x = S.activations(97, T, h=H, outliers=(T == 16384))
+    wr, sc, pes, bias = W.router_to_device(router)
+    wsb = moe.moe_bucket_workspace_bytes(T, k, E)
+    res = []
+    for with_logits in (True, False):
+        o = dict(idx=torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+                 w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                 w_raw=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                 lg=torch.empty((T, E), dtype=torch.float32, device="cuda") if with_logits else None,
+                 off=torch.empty((E + 1,), dtype=torch.int32, device="cuda"),
+                 sp=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+                 pr=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+                 ws=torch.full((wsb,), 0x55, dtype=torch.uint8, device="cuda"))
+        moe.moe_route_bucket(_bits(x), wr, sc, pes, bias, k, 1e-6, o["idx"], o["w"], o["w_raw"],
+                             o["lg"], o["off"], o["sp"], o["pr"], o["ws"])
+        torch.cuda.synchronize()
+        res.append(o)
+    for n in ("idx", "w", "w_raw", "off", "sp", "pr"):
+        assert torch.equal(res[0][n], res[1][n]), n
+    r = router_f64(router)
+    ref = M.route(F.bf16_bits_to_f64(x), r["w_router"], r["scale"], r["per_expert_scale"], k,
+                  r["bias"])
+    assert np.max(np.abs(res[0]["lg"].cpu().numpy() - ref["logits"])) <= 2e-7
+    idx = res[0]["idx"].cpu().numpy()
+    differ = check_route(idx, res[0]["w"].cpu().numpy(), res[0]["w_raw"].cpu().numpy(), ref,
+                         r["per_expert_scale"])
+    assert len(differ) <= max(1, T // 200)
+    ref_b = M.bucket(idx, E)
+    assert np.array_equal(res[0]["off"].cpu().numpy(), ref_b["offsets"])
+    assert np.array_equal(res[0]["sp"].cpu().numpy(), ref_b["sorted_pairs"])
 
 
 @pytest.mark.parametrize("T,H,E,k,I", [(0, 2816, 128, 8, 704), (1, 2816, 128, 8, 704),
