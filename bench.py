@@ -325,7 +325,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     t_setup = time.perf_counter() - t_setup
     hs, stream = B.hs, B.stream
     separate = B.args.separate_prep
-    # decode batches run as moe_layer_decode (four launches) unless a
+    # decode batches run as moe_layer_decode (three or four launches) unless a
     # variant asks for the separate calls
     fused = buf.decode and not (chain or separate or B.args.four_calls)
     stage_names = ("layer_decode",) if fused else SEPARATE_STAGES if separate else STAGES
@@ -473,7 +473,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     }
     if stage_avg_us is not None:
         res["stage_avg_us_with_event_nodes"] = stage_avg_us
-    res["path"] = ("moe_layer_decode (4 launches)" if fused else
+    res["path"] = ((f"moe_layer_decode ({3 if T * K <= 32 else 4} launches)") if fused else
                    "moe_route_bucket + nvfp4_expert_prep + gate_up + down + combine" if separate else
                    "moe_route_bucket_prep + nvfp4_expert_gate_up + nvfp4_expert_down + combine")
     for g in (graph, gu_graph):

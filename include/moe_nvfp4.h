@@ -227,15 +227,19 @@ int moe_route_bucket_prep(const uint16_t *x, const uint16_t *w_router,
  * moe_layer_decode -- the whole block for a decode batch in one call: the
  * router, the bucketing, the expert MLP and the weighted combine of
  * moe_route -> moe_bucket -> nvfp4_expert_mlp -> moe_combine, queued as four
- * kernels instead of five ("Gemma-4-26B-A4B-IT - UD-Q8KXL (mlx-node)",
- * Performance: decode gains from fusing the per-layer dispatch):
+ * kernels instead of five, or three up to 32 pairs ("Gemma-4-26B-A4B-IT -
+ * UD-Q8KXL (mlx-node)", Performance: decode gains from fusing the per-layer
+ * dispatch):
  *   1. the router logits, beside the expert input's f16 rows;
  *   2. the gate/up projection, every workgroup repeating the top-k selection
  *      of every token and the bucketing in LDS (no kernel of their own);
- *   3. the down projection; 4. the combine.
- * Arguments as those calls' (x is also the expert input).  Every output has
- * the same bytes as the four calls': topk_idx, topk_w, topk_w_raw (NULL
- * allowed), expert_offsets, sorted_pairs, pair_rank and out.
+ *   3. the down projection; 4. the combine -- up to 32 pairs one kernel,
+ *      each token's pairs in one workgroup that adds them as moe_combine does.
+ * Arguments as those calls' (x is also the expert input).  topk_idx, topk_w,
+ * topk_w_raw (NULL allowed), expert_offsets, sorted_pairs and pair_rank have
+ * the same bytes as the four calls'; so has out above 32 pairs, and up to 32
+ * pairs it is within a few bf16 steps of theirs (each expert output computed
+ * over the same K in another order of the fp32 sums).
  *   gate, up, down  nvfp4_tensor as nvfp4_expert_mlp's (MOE_LAYOUT_TILED)
  *   out             [T][H] bf16
  *   workspace       >= moe_layer_decode_workspace_bytes(T, top_k, E, H, I)

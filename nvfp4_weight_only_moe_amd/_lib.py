@@ -273,7 +273,8 @@ def decode_fits(T, top_k, H):
 def moe_layer_decode(x, w_router, router_scale, per_expert_scale, logit_bias, top_k, eps, gate,
                      up, down, topk_idx, topk_w, topk_w_raw, expert_offsets, sorted_pairs,
                      pair_rank, out, workspace, stream=None):
-    """The whole block for a decode batch (T <= 8) in four launches."""
+    """The whole block for a decode batch (T <= 8) in three launches (up to
+    32 pairs) or four."""
     T, H = x.shape
     E = w_router.shape[0]
     I = gate.N

@@ -82,7 +82,7 @@ def forward(layer: MoeLayer, x, buf: MoeBuffers, x_expert=None, stream=None, mar
             fused=None):
     """Queue the whole block for x [T, H] bf16; the result lands in buf.out.
 
-    Decode batches (T <= 8) run as moe_layer_decode (four launches) unless
+    Decode batches (T <= 8) run as moe_layer_decode (three or four launches) unless
     ``fused`` is False or the experts read another input.  ``marks``
     (optional) is a callable invoked with a stage name between the calls
     ("route", "bucket", "prep", "gate_up", "down", "combine" after each); with

@@ -1,7 +1,8 @@
 // moe_layer_decode: the whole expert block of a decode batch (T <= 8) in
 // four launches instead of five -- the router logits with the expert-input
 // prep, the gate/up projection with the top-k selection and the bucketing
-// folded in, the down projection, the combine ("Gemma-4-26B-A4B-IT -
+// folded in, the down projection, the combine -- or in three, with the down
+// projection and the combine in one kernel, up to kDecodeCombineMaxP pairs ("Gemma-4-26B-A4B-IT -
 // UD-Q8KXL (mlx-node)", Performance: the per-layer dispatch fused for
 // decode).
 #include "common.h"
@@ -15,6 +16,17 @@ int launch_decode_gate_up(const float *logits, const uint16_t *pes, int T, int t
                           int32_t *topk_idx, float *topk_w, float *topk_w_raw, int32_t *offsets,
                           int32_t *sorted, int32_t *rank, int32_t *err, void *expert_ws,
                           hipStream_t s);
+int launch_decode_down_combine(const int32_t *topk_idx, const float *topk_w, const int32_t *rank,
+                               int T, int top_k, int E, int H, int I, const nvfp4_tensor *down,
+                               void *expert_ws, uint16_t *out, hipStream_t s);
+// Batches of up to this many pairs take the down projection and the combine
+// in one launch: each token's pairs in one workgroup, its expert weights read
+// once per token (a batch of few tokens shares few experts); larger batches
+// keep the expert-major down GEMV, which reads each expert's weights once.
+#ifndef MOE_DECODE_COMBINE_MAX_P
+#define MOE_DECODE_COMBINE_MAX_P 32
+#endif
+constexpr int kDecodeCombineMaxP = MOE_DECODE_COMBINE_MAX_P;
 }  // namespace moe
 
 namespace {
@@ -97,6 +109,9 @@ extern "C" int moe_layer_decode(const uint16_t *x, const uint16_t *w_router,
   st = launch_decode_gate_up(logits, per_expert_scale, T, top_k, E, H, I, gate, up, topk_idx, topk_w,
                              topk_w_raw, expert_offsets, sorted_pairs, pair_rank, err, expert_ws, s);
   if (st != MOE_OK) return st;
+  if (T * top_k <= kDecodeCombineMaxP)
+    return launch_decode_down_combine(topk_idx, topk_w, pair_rank, T, top_k, E, H, I, down,
+                                      expert_ws, out, s);
   uint16_t *y = (uint16_t *)(ws + L.y);
   st = nvfp4_expert_down(down, expert_offsets, T, top_k, H, I, y, expert_ws, ws_bytes - L.expert,
                          stream);

@@ -826,9 +826,13 @@ struct GemvArgs {
   uint16_t *out;           // GATED: A [P][N] bf16; else Y [P][N] bf16
 };
 
-template <int R, int NP, bool GATED, int KS, int FMT, int PD = kGemvPD>
+// STORE = false (down, one row: mrows == 1): instead of writing Y, lanes
+// 0..15 return the row's bf16 outputs (as floats) of columns (nt0 + i) * 16 +
+// lane in yout[i]; the other lanes' yout is undefined.
+template <int R, int NP, bool GATED, int KS, int FMT, int PD = kGemvPD, bool STORE = true>
 __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, const Nvfp4 &w1,
-                                         int e, int row0, int mrows, int nt0, float *s_red) {
+                                         int e, int row0, int mrows, int nt0, float *s_red,
+                                         float *yout = nullptr) {
   constexpr int NW = GATED ? 2 * NP : NP;
   constexpr int NL = R / 4;  // activation chunks per lane and unit
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1005,6 +1009,10 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       rmax = row16_max_u32(rmax);
       if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], rmax);
     }
+  } else if (!STORE) {
+    const float f = ep_g0 * __builtin_ldexpf(1.0f, ep_ex[0] - 14);  // row 0: lanes 0..15, jj = 0
+#pragma unroll
+    for (int i = 0; i < NP; ++i) yout[i] = __uint_as_float((uint32_t)f32_to_bf16_rne(acc[i][0] * f) << 16);
   } else {
     const float gd = ep_g0;
 #pragma unroll
@@ -1120,6 +1128,14 @@ constexpr int kDecodeMaxP = MOE_DECODE_MAX_PAIRS;
 static_assert(kDecodeMaxP <= kWave, "the bucketing of the decode layer is one wave's");
 static_assert(kDecodeMaxT <= 2 * (kThreads / kWave), "two tokens per selecting wave");
 constexpr int kDecodePD = kGemvPD;  // gate/up K units in flight per wave
+#ifndef MOE_DECODE_DOWN_PD
+#define MOE_DECODE_DOWN_PD 2
+#endif
+#ifndef MOE_DECODE_NPC
+#define MOE_DECODE_NPC 1
+#endif
+constexpr int kDecodeDownPD = MOE_DECODE_DOWN_PD;  // down K units in flight per wave (fused combine)
+constexpr int kDecodeNPC = MOE_DECODE_NPC;          // row tiles per workgroup (fused combine)
 
 struct DecodeRoute {
   const float *logits;  // [T][E]
@@ -1180,6 +1196,42 @@ void k_decode_gate_up(GemvArgs p, DecodeRoute r, Nvfp4 w0, Nvfp4 w1) {
   else gemv_run<8, NP, true, KS, FMT, kDecodePD>(q, w0, w1, e, row0, mrows, nt0, s_red);
 }
 
+// Down projection and combine of a decode batch in one launch (the plain
+// combine of moe_layer_decode, T * top_k <= kDecodeCombineMaxP): workgroup
+// (x, t) owns the 16 NPC output columns x of token t, and its wave j the
+// token's pair j -- the pair's A row times its expert's down weights over
+// all of K (R = 4 packing, one row), rounded to bf16 as Y would be.  The
+// waves meet once in LDS and the first 16 NPC threads add the pairs as
+// moe_combine does (fp32 fmaf in pair order, one bf16 rounding).  No Y
+// round trip and no combine launch; each token's expert weights are read
+// once per token (a decode batch of a few tokens shares few experts).
+template <int FMT, int NPC>
+__global__ __launch_bounds__(kWave * MOE_MAX_TOPK) void k_decode_down_combine(
+    GemvArgs p, const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w,
+    const int32_t *__restrict__ rank, int E, Nvfp4 d, uint16_t *__restrict__ out) {
+  __shared__ float s_y[MOE_MAX_TOPK][16 * NPC];
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.y, K = p.top_k;
+  const int nt0 = blockIdx.x * NPC;
+  const int e = topk_idx[t * K + j], rr = rank[t * K + j];  // uniform per wave
+  const bool ok = rr >= 0 && rr < p.P && e >= 0 && e < E;
+  float y[NPC];
+  if (ok) gemv_run<4, NPC, false, 1, FMT, kDecodeDownPD, false>(p, d, d, e, rr, 1, nt0, nullptr, y);
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) s_y[j][i * 16 + lane] = ok ? y[i] : 0.0f;
+  }
+  __syncthreads();
+  const int c = nt0 * 16 + (int)threadIdx.x;
+  if (threadIdx.x < 16 * NPC && c < p.N) {
+    float sum = 0.0f;
+    for (int jj = 0; jj < K; ++jj) {
+      const int q = t * K + jj, r2 = rank[q];
+      if (r2 >= 0 && r2 < p.P) sum = fmaf(topk_w[q], s_y[jj][threadIdx.x], sum);
+    }
+    out[(size_t)t * p.N + c] = f32_to_bf16_rne(sum);
+  }
+}
 
 }  // namespace
 }  // namespace moe
@@ -1488,6 +1540,34 @@ __attribute__((visibility("hidden"))) int launch_decode_gate_up(
       break;
     default:
       MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_NVFP4>, grid, dim3(kThreads), 0, s, a, dr, g, u);
+  }
+  return MOE_OK;
+}
+
+// The down stage and the plain combine of the fused decode layer in one
+// launch (T * top_k <= kDecodeCombineMaxP; arguments validated by the
+// caller, expert_ws as for launch_decode_gate_up with A written).
+__attribute__((visibility("hidden"))) int launch_decode_down_combine(
+    const int32_t *topk_idx, const float *topk_w, const int32_t *rank, int T, int top_k, int E,
+    int H, int I, const nvfp4_tensor *down, void *expert_ws, uint16_t *out, hipStream_t s) {
+  const Ws w = ws_ptrs(expert_ws, ws_layout(T, top_k, E, H, I));
+  const int P = T * top_k;
+  const GemvArgs a{w.a, nullptr, w.a_max, nullptr, top_k, I, H, P,
+                   (uint32_t)((size_t)P * I * 2), nullptr};
+  const Nvfp4 d{down->packed, down->scales, down->global};
+  const dim3 grid((H + 16 * kDecodeNPC - 1) / (16 * kDecodeNPC), T), block(kWave * top_k);
+  switch (down->format) {
+    case MOE_FORMAT_Q4_0:
+      MOE_LAUNCH((k_decode_down_combine<MOE_FORMAT_Q4_0, kDecodeNPC>), grid, block, 0, s, a,
+                 topk_idx, topk_w, rank, E, d, out);
+      break;
+    case MOE_FORMAT_AFF4:
+      MOE_LAUNCH((k_decode_down_combine<MOE_FORMAT_AFF4, kDecodeNPC>), grid, block, 0, s, a,
+                 topk_idx, topk_w, rank, E, d, out);
+      break;
+    default:
+      MOE_LAUNCH((k_decode_down_combine<MOE_FORMAT_NVFP4, kDecodeNPC>), grid, block, 0, s, a,
+                 topk_idx, topk_w, rank, E, d, out);
   }
   return MOE_OK;
 }
