@@ -366,7 +366,7 @@ inline void route_split_cfg(int T, int E, int *exp, int *ks) {
     return;
   }
   const long long k = (1024 + tiles - 1) / tiles;
-  *ks = k > 8 ? 8 : (int)k;
+  *ks = k > 8 ? 8 : (int)k;  // at most the selection kernel's kRouteMaxKs
 }
 inline int route_split_ks(int T, int E) {
   int exp, ks;

@@ -331,6 +331,7 @@ __global__ __launch_bounds__(256) void k_route_logits_wide(
 // The K-split router's end: one wave per token adds the ks partial dot
 // products and sums of squares in slice order, scales them as the unsplit
 // kernel does, writes the logits (when asked) and selects from them.
+constexpr int kRouteMaxKs = 8;  // route_split_cfg's most slices
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route_select_split(
     const float *__restrict__ part, const float *__restrict__ pss, int ks,
@@ -341,15 +342,30 @@ __global__ __launch_bounds__(256) void k_route_select_split(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t < T) {
+    // every partial load issued before the first add (ks <= kRouteMaxKs)
+    float pz[kRouteMaxKs], vz[NPER][kRouteMaxKs];
+#pragma unroll
+    for (int z = 0; z < kRouteMaxKs; ++z) {
+      pz[z] = z < ks ? pss[(size_t)z * T + t] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const int e = lane + i * kWave;
+        vz[i][z] = (z < ks && e < E) ? part[((size_t)z * T + t) * E + e] : 0.0f;
+      }
+    }
     float ss = 0.0f;
-    for (int z = 0; z < ks; ++z) ss += pss[(size_t)z * T + t];
+#pragma unroll
+    for (int z = 0; z < kRouteMaxKs; ++z)
+      if (z < ks) ss += pz[z];
     const float f = 1.0f / sqrtf(ss / (float)H + eps) * (1.0f / sqrtf((float)H));
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       const int e = lane + i * kWave;
       if (e >= E) break;
       float a = 0.0f;
-      for (int z = 0; z < ks; ++z) a += part[((size_t)z * T + t) * E + e];
+#pragma unroll
+      for (int z = 0; z < kRouteMaxKs; ++z)
+        if (z < ks) a += vz[i][z];
       const float v = a * f + (bias ? bias[e] : 0.0f);
       if (logits) logits[(size_t)t * E + e] = v;
       s_row[wave][e] = v;
