@@ -667,7 +667,18 @@ __device__ __forceinline__ void gemm_run(
   if (!wave_on) return;  // no barrier follows
   if constexpr (MSUB == 8) mfma_acc_drain();
 
-  // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile
+  // ---- epilogue: lane holds rows 16q + 4g + jj, column r of each row tile.
+  // The block's output rows go through a buffer resource: rows past the
+  // block and columns past N get offsets outside it (the hardware drops those
+  // stores), so no store sits under a branch and each takes one 32-bit
+  // offset (a row's, plus its column's).
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (size_t)row0 * N, (uint32_t)((size_t)mrows * N * 2));
+  uint32_t coff[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int n = (nt0 + i) * 16 + r;
+    coff[i] = n < N ? (uint32_t)n * 2 : 0x40000000u;  // plus a row offset or kOOB: no wrap
+  }
   if (GATED) {
     const float gg = FMT == MOE_FORMAT_NVFP4 ? w0.global[e] : 1.0f;
     const float gu = FMT == MOE_FORMAT_NVFP4 ? w1.global[e] : 1.0f;
@@ -678,12 +689,13 @@ __device__ __forceinline__ void gemm_run(
         const int m = q * kBM + 4 * g + jj;
         const bool ok = m < mrows;
         const float f = s_rowscale[m];
+        const uint32_t roff = ok ? (uint32_t)(m * N) * 2 : kOOB;
         uint32_t rmax = 0;  // max |A| of the row (f32 bits)
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const float G = acc[q][i][jj] * (gg * f), U = acc[q][NP + i][jj] * (gu * f);
           const uint16_t ab = f32_to_bf16_rne(gelu_tanh(G) * U);
-          if (ok) out[(size_t)(row0 + m) * N + (nt0 + i) * 16 + r] = ab;
+          __builtin_amdgcn_raw_buffer_store_b16(ab, ro, roff + coff[i], 0, 0);
           rmax = max(rmax, ok ? bf16_abs_bits(ab) : 0u);
         }
         rmax = row16_max_u32(rmax);
@@ -697,14 +709,11 @@ __device__ __forceinline__ void gemm_run(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int m = q * kBM + 4 * g + jj;
-        if (m < mrows) {
-          const float f = gd * s_rowscale[m];
+        const float f = gd * s_rowscale[m];  // 0 past the block's rows
+        const uint32_t roff = m < mrows ? (uint32_t)(m * N) * 2 : kOOB;
 #pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            const int n = (nt0 + i) * 16 + r;
-            if (n < N) out[(size_t)(row0 + m) * N + n] = f32_to_bf16_rne(acc[q][i][jj] * f);
-          }
-        }
+        for (int i = 0; i < NP; ++i)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[q][i][jj] * f), ro, roff + coff[i], 0, 0);
       }
     }
   }
