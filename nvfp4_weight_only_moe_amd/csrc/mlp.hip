@@ -77,12 +77,14 @@ int choose_msub(int T, int top_k, int E) {
 // rows up.  (Before the gate/up blocks were spread over the XCDs by cost,
 // the crossover lay near 192 rows.)
 constexpr int kMsub8From = 128;
-int gate_up_msub(int T, int top_k, int E) {
+// (and the expert intermediate I fits the row conversion of the down
+// blocks, k_a_f16: at most 4096)
+int gate_up_msub(int T, int top_k, int E, int I) {
   const int m = choose_msub(T, top_k, E);
   if (m == 1) return 1;
   const long long P = (long long)T * top_k;
   const long long buckets = P < E ? P : E;
-  return P / buckets >= kMsub8From ? 8 : m;
+  return P / buckets >= kMsub8From && I <= 4096 ? 8 : m;
 }
 
 // Few rows per expert (decode): the GEMV-mode kernels.  Otherwise tiled mode.
@@ -111,7 +113,7 @@ WsLayout ws_layout(int T, int top_k, int E, int H, int I) {
   L.a = L.x16 + moe_align_up((size_t)T * H * 2, 256);
   L.a16 = L.a + moe_align_up(P * (size_t)I * 2, 256);
   // 128-row down blocks read A converted to f16 (a copy beside A)
-  L.total = L.a16 + (gate_up_msub(T, top_k, E) == 8 ? moe_align_up(P * (size_t)I * 2, 256) : 0);
+  L.total = L.a16 + (gate_up_msub(T, top_k, E, I) == 8 ? moe_align_up(P * (size_t)I * 2, 256) : 0);
   if (L.total < 256) L.total = 256;  // never empty, so T = 0 still gets a valid pointer
   return L;
 }
@@ -698,8 +700,12 @@ __device__ __forceinline__ void gemm_run(
           __builtin_amdgcn_raw_buffer_store_b16(ab, ro, roff + coff[i], 0, 0);
           rmax = max(rmax, ok ? bf16_abs_bits(ab) : 0u);
         }
-        rmax = row16_max_u32(rmax);
-        if (r == 0 && ok) atomicMax(&a_max[row0 + m], rmax);
+        // the row maxima of A: 128-row blocks leave them to k_a_f16, which
+        // reads every row of A anyway
+        if constexpr (MSUB != 8) {
+          rmax = row16_max_u32(rmax);
+          if (r == 0 && ok) atomicMax(&a_max[row0 + m], rmax);
+        }
       }
     }
   } else {
@@ -756,28 +762,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #undef MOE_GEMM_RUN
 }
 
-// For the 128-row down blocks: A [P][I] bf16 -> f16 times its row's power of
-// two 2^(14 - exponent of max|A|) (exact, as the 64-row kernel converts it
-// while staging), once per element instead of once per column block, so
-// that the down kernel stages A into LDS with direct loads.
+// For the 128-row down blocks: the row maxima of A (a_max, which the 128-row
+// gate/up blocks do not compute) and A [P][I] bf16 -> f16 times its row's
+// power of two 2^(14 - exponent of max|A|) (exact, as the 64-row kernel
+// converts it while staging), once per element instead of once per column
+// block, so that the down kernel stages A into LDS with direct loads.  One
+// wave per row, which it holds in registers (NCH 16-byte chunks per lane):
+// the row's maximum, then its conversion.
+template <int NCH>
 __global__ __launch_bounds__(kThreads) void k_a_f16(const uint16_t *__restrict__ a,
-                                                    const uint32_t *__restrict__ a_max, int P,
+                                                    uint32_t *__restrict__ a_max, int P,
                                                     int I, uint16_t *__restrict__ a16) {
-  const int per_row = I / 8;  // 16-byte chunks per row
-  const size_t n = (size_t)P * per_row;
-  for (size_t c = (size_t)blockIdx.x * kThreads + threadIdx.x; c < n;
-       c += (size_t)gridDim.x * kThreads) {
-    const int row = (int)(c / per_row);
-    const float f = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(a_max[row])));
-    const u32x4 v = *(const u32x4 *)(a + c * 8);
-    u32x4 o;
+  const int lane = threadIdx.x & 63;
+  const int per_row = I / 8;  // 16-byte chunks per row, at most 64 NCH
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= P) return;
+  const uint16_t *ar = a + (size_t)row * I;
+  u32x4 v[NCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16 lo = (f16)(__uint_as_float(v[i] << 16) * f);
-      const f16 hi = (f16)(__uint_as_float(v[i] & 0xFFFF0000u) * f);
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + k * kWave;
+    v[k] = c < per_row ? *(const u32x4 *)(ar + c * 8) : u32x4{0, 0, 0, 0};
+  }
+  uint32_t mx = 0;  // max |A| of the row (f32 bits; NaN counts as 0)
+#pragma unroll
+  for (int k = 0; k < NCH; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mx = max(mx, max(bf16_abs_bits((uint16_t)v[k][i]), bf16_abs_bits((uint16_t)(v[k][i] >> 16))));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  if (lane == 0) a_max[row] = mx;
+  const float f = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(mx)));
+  {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = lane + k * kWave;
+      if (c >= per_row) break;
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16 lo = (f16)(__uint_as_float(v[k][i] << 16) * f);
+        const f16 hi = (f16)(__uint_as_float(v[k][i] & 0xFFFF0000u) * f);
+        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *(u32x4 *)(a16 + (size_t)row * I + c * 8) = o;
     }
-    *(u32x4 *)(a16 + c * 8) = o;
   }
 }
 
@@ -1323,10 +1354,13 @@ int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nv
   const int ncb = (H + 64 * kGemmDownNP - 1) / (64 * kGemmDownNP);
   const uint16_t *a = w.a;
   if (MSUB == 8) {
-    const long long chunks = (long long)T * top_k * (I / 8);
-    const int blocks = (int)std::min<long long>((chunks + kThreads - 1) / kThreads, 4096);
-    MOE_LAUNCH(k_a_f16, dim3(blocks), dim3(kThreads), 0, s, (const uint16_t *)w.a,
-               (const uint32_t *)w.a_max, T * top_k, I, w.a16);
+    const dim3 grid((T * top_k + 3) / 4);
+    if (I <= 8 * 64 * 2)
+      MOE_LAUNCH(k_a_f16<2>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
+    else if (I <= 8 * 64 * 4)
+      MOE_LAUNCH(k_a_f16<4>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
+    else  // I <= 4096 (gate_up_msub)
+      MOE_LAUNCH(k_a_f16<8>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
     a = w.a16;
   }
   MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
@@ -1400,7 +1434,7 @@ int gate_up_fmt(const Ws &w, const int32_t *expert_offsets, const int32_t *sorte
                  expert_offsets, E, g, u);
     return MOE_OK;
   }
-  if (gate_up_msub(T, top_k, E) == 8)
+  if (gate_up_msub(T, top_k, E, I) == 8)
     return launch_gate_up<8, FMT>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
   return launch_gate_up<4, FMT>(w, expert_offsets, sorted_pairs, T, top_k, E, g, u, H, I, s);
 }
@@ -1432,7 +1466,7 @@ int down_fmt(const Ws &w, const int32_t *expert_offsets, int T, int top_k, int E
 #undef MOE_GEMV_DN
     return MOE_OK;
   }
-  if (gate_up_msub(T, top_k, E) == 8)
+  if (gate_up_msub(T, top_k, E, I) == 8)
     return launch_down<8, FMT>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
   return launch_down<4, FMT>(w, expert_offsets, T, top_k, E, d, H, I, y_sorted, s);
 }
