@@ -767,22 +767,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // power of two 2^(14 - exponent of max|A|) (exact, as the 64-row kernel
 // converts it while staging), once per element instead of once per column
 // block, so that the down kernel stages A into LDS with direct loads.  One
-// wave per row, which it holds in registers (NCH 16-byte chunks per lane):
-// the row's maximum, then its conversion.
+// half-wave per row, which it holds in registers (NCH 16-byte chunks per
+// lane): the row's maximum, then its conversion.
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void k_a_f16(const uint16_t *__restrict__ a,
                                                     uint32_t *__restrict__ a_max, int P,
                                                     int I, uint16_t *__restrict__ a16) {
-  const int lane = threadIdx.x & 63;
-  const int per_row = I / 8;  // 16-byte chunks per row, at most 64 NCH
-  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (row >= P) return;
-  const uint16_t *ar = a + (size_t)row * I;
+  constexpr int L = kWave / 2;  // lanes per row
+  const int lane = threadIdx.x & (L - 1);
+  const int per_row = I / 8;  // 16-byte chunks per row, at most L NCH
+  const int row = blockIdx.x * (kThreads / L) + (int)(threadIdx.x / L);
+  const bool on = row < P;  // both halves of a wave stay for the shuffles
+  const uint16_t *ar = a + (size_t)(on ? row : 0) * I;
   u32x4 v[NCH];
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
-    const int c = lane + k * kWave;
-    v[k] = c < per_row ? *(const u32x4 *)(ar + c * 8) : u32x4{0, 0, 0, 0};
+    const int c = lane + k * L;
+    v[k] = (on && c < per_row) ? *(const u32x4 *)(ar + c * 8) : u32x4{0, 0, 0, 0};
   }
   uint32_t mx = 0;  // max |A| of the row (f32 bits; NaN counts as 0)
 #pragma unroll
@@ -791,13 +792,14 @@ __global__ __launch_bounds__(kThreads) void k_a_f16(const uint16_t *__restrict__
     for (int i = 0; i < 4; ++i)
       mx = max(mx, max(bf16_abs_bits((uint16_t)v[k][i]), bf16_abs_bits((uint16_t)(v[k][i] >> 16))));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  for (int o = L / 2; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  if (!on) return;
   if (lane == 0) a_max[row] = mx;
   const float f = __builtin_ldexpf(1.0f, 14 - row_exponent(__uint_as_float(mx)));
   {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const int c = lane + k * kWave;
+      const int c = lane + k * L;
       if (c >= per_row) break;
       u32x4 o;
 #pragma unroll
@@ -1354,13 +1356,13 @@ int launch_down(const Ws &w, const int32_t *offsets, int T, int top_k, int E, Nv
   const int ncb = (H + 64 * kGemmDownNP - 1) / (64 * kGemmDownNP);
   const uint16_t *a = w.a;
   if (MSUB == 8) {
-    const dim3 grid((T * top_k + 3) / 4);
-    if (I <= 8 * 64 * 2)
-      MOE_LAUNCH(k_a_f16<2>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
-    else if (I <= 8 * 64 * 4)
-      MOE_LAUNCH(k_a_f16<4>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
-    else  // I <= 4096 (gate_up_msub)
+    const dim3 grid((T * top_k + 7) / 8);  // 8 rows per workgroup
+    if (I <= 8 * 32 * 3)
+      MOE_LAUNCH(k_a_f16<3>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
+    else if (I <= 8 * 32 * 8)
       MOE_LAUNCH(k_a_f16<8>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
+    else  // I <= 4096 (gate_up_msub)
+      MOE_LAUNCH(k_a_f16<16>, grid, dim3(kThreads), 0, s, (const uint16_t *)w.a, w.a_max, T * top_k, I, w.a16);
     a = w.a16;
   }
   MOE_LAUNCH((k_expert_gemm<MSUB, kGemmDownNP, false, FMT>), gemm_grid(T * top_k, E, kBM * MSUB, ncb),
