@@ -20,10 +20,13 @@ Without --workload every one of them is measured: the JSON line is workload
 1's, and detail.workloads holds each workload's own figures (T = 1 and T = 8
 for workload 3).
 
-Timing: W warm-up steps, then K steps captured in one HIP graph on one stream
-and replayed once.  ms_per_step is the GPU time of that replay from HIP events
-recorded on the same stream around the graph launch, divided by K (the host
-wall clock around launch and synchronisation is reported beside it).  The
+Timing: W warm-up steps, then K steps captured in one HIP graph on one stream.
+The graph is launched twice back to back; ms_per_step is the GPU time of the
+second replay from HIP events recorded on the same stream before and after it,
+divided by K, so the host's launch of the graph overlaps the first replay as
+it overlaps the previous step in a serving loop.  The first replay's time
+(launched onto an idle stream, the GPU waiting for the graph's packets) and
+the host wall clock per replay are reported beside it.  The
 dominant kernel (the gate/up projection) is timed by HIP events around
 back-to-back launches of its stage call on the same stream.  Consecutive steps
 of a single-layer workload read different, byte-identical copies of the expert
@@ -186,17 +189,25 @@ class HipRuntime:
         return self.instantiate(g)
 
     def timed_replay(self, exe, stream, sync):
-        """GPU milliseconds of one replay of `exe` (events on `stream` around
-        the launch) and the host wall-clock milliseconds of launch + sync."""
-        a, b = self.event(), self.event()
+        """GPU milliseconds of one replay of `exe` in steady state, and of a
+        replay launched onto an idle stream, plus the host wall-clock
+        milliseconds per replay.  Two replays are queued back to back with
+        events before, between and after them: the second one's GPU time
+        (between the middle and the last event) excludes the host-side launch
+        of the graph, which overlaps the first replay's execution, as it
+        overlaps the previous step's in a serving loop; the first one's
+        includes it (the GPU waits for the graph's packets)."""
+        a, b, c = self.event(), self.event(), self.event()
         sync()
         t0 = time.perf_counter()
         self.record(a, stream)
         self.launch(exe, stream)
         self.record(b, stream)
+        self.launch(exe, stream)
+        self.record(c, stream)
         sync()
-        wall = (time.perf_counter() - t0) * 1e3
-        return self.elapsed(a, b), wall
+        wall = (time.perf_counter() - t0) * 1e3 / 2
+        return self.elapsed(b, c), wall, self.elapsed(a, b)
 
 
 # scale bytes per 32 weights: two E4M3 codes (NVFP4), one fp16 d (q4_0), fp16 s and b (aff4)
@@ -393,7 +404,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     graph = hip.instantiate(hip.capture(hs, lambda: [queue_step(p) for p in plan]))
     hip.launch(graph, hs)                       # one untimed replay
     torch.cuda.synchronize()
-    gpu_ms, wall_ms = hip.timed_replay(graph, hs, torch.cuda.synchronize)
+    gpu_ms, wall_ms, cold_ms = hip.timed_replay(graph, hs, torch.cuda.synchronize)
     ms_per_step = gpu_ms / steps
 
     # ---- the dominant kernel alone: the gate/up stage call R times back to
@@ -410,7 +421,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
         gu_seq = [gu_calls[i % len(gu_calls)] for i in range(reps_gu)]
         gu_graph = hip.instantiate(hip.capture(hs, lambda: [c() for c in gu_seq]))
         hip.launch(gu_graph, hs)                # warm
-        gu_ms, _ = hip.timed_replay(gu_graph, hs, torch.cuda.synchronize)
+        gu_ms, _, _ = hip.timed_replay(gu_graph, hs, torch.cuda.synchronize)
         gu_us = 1e3 * gu_ms / reps_gu
 
     stage_avg_us = None
@@ -454,6 +465,7 @@ def run_workload(B, workload, T, steps, warmup, stages=False, chain=False, name=
     res = {
         "workload": name, "tokens": T, "layers": n_layers, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "ms_per_step_wall": wall_ms / steps,
+        "ms_per_step_launch_on_idle_stream": cold_ms / steps,
         "tokens_per_s": T / step_s,
         "active_experts": U_total,
         "expert_weight_GBps": per_exp * U_total / step_s / 1e9,
@@ -576,7 +588,7 @@ def main(argv=None):
         "config": {"workload": head["workload"], "tokens": head["tokens"], "hidden": B.H,
                    "experts": B.E, "top_k": B.K, "moe_intermediate": B.I,
                    "layers": head["layers"], "weight_replicas": head["weight_replicas"],
-                   "timing": "hip_graph (one stream); GPU time by HIP events around the replay"},
+                   "timing": "hip_graph (one stream); GPU time by HIP events around the second of two back-to-back replays"},
         "detail": {"headline": public(head),
                    "workloads": {r["workload"]: public(r) for _, r in results[1:]}},
         "roofline": rl,

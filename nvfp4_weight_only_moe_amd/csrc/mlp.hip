@@ -243,11 +243,14 @@ constexpr int kBlockCost = 8;
 // experts PER*l .. PER*l + PER - 1; DPP prefix sums over the lanes, scalar
 // results).  Workgroup b runs on XCD x = b % 8 as its j = b / 8-th
 // workgroup and takes block j of XCD x's range of the order.
-// BALANCED = false: 8 ranges of gridDim.x / 8 blocks.  BALANCED = true: the
-// ranges hold about equal cost (kBlockCost + 16-row groups per block), each
-// at most gridDim.x / 8 blocks long; used where blocks with few rows are
-// common beside full ones (the Zipf tail beside the head experts), whose
-// count-equal ranges differ in work by up to a third.
+// BALANCED = false: 8 ranges of ceil(blocks / 8) blocks (the real block
+// count: the grid is sized for the most blocks any routing can give, and
+// ranges of gridDim.x / 8 left the last XCD with a few blocks or none).
+// BALANCED = true: the ranges hold about equal cost (kBlockCost + 16-row
+// groups per block), each at most gridDim.x / 8 blocks long; used where
+// blocks with few rows are common beside full ones (the Zipf tail beside
+// the head experts), whose count-equal ranges differ in work by up to a
+// third.
 template <bool BALANCED>
 __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, int msub, int ncb,
                            int grp, int &e, int &m0, int &cb) {
@@ -274,9 +277,11 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
   const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
   const int excl = incl - sum;
   const int cap = (int)gridDim.x / kXcds, x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  int L;
+  int lo, hi;
   if (!BALANCED) {
-    L = x * cap + j;
+    const int len = (total + kXcds - 1) / kXcds;
+    lo = min(total, x * len);
+    hi = min(total, lo + len);
   } else {
     // range starts s_1 .. s_7 at the blocks where the cost prefix reaches
     // y/8 of the total (uniform cost per block inside an expert), clamped so
@@ -284,7 +289,9 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
     // take the rest
     const int cincl = wave_incl_scan(csum);
     const int C = __builtin_amdgcn_readlane(cincl, kWave - 1), cexcl = cincl - csum;
-    int prev = 0, lo = 0, hi = total;
+    int prev = 0;
+    lo = 0;
+    hi = total;
     for (int y = 1; y < kXcds; ++y) {
       const int t = (int)((long long)y * C / kXcds);
       const unsigned long long bal = __ballot(t >= cexcl && t < cincl);
@@ -305,10 +312,9 @@ __device__ bool find_block(const int32_t *__restrict__ offsets, int E, int bm, i
       if (y == x + 1) hi = sy;
       prev = sy;
     }
-    L = lo + j;
-    if (L >= hi) return false;
   }
-  if (L >= total) return false;
+  if (lo + j >= hi) return false;  // uniform
+  const int L = lo + j;
   const int src = (int)__builtin_ctzll(__ballot(L >= excl && L < incl));
   int ee = 0, rem = 0, nb = 1, base = excl;
 #pragma unroll
