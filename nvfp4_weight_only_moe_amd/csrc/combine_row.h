@@ -50,7 +50,9 @@ __device__ __forceinline__ TokenPairs token_pairs(const float *__restrict__ w,
 
 // The fp32 sums of columns c .. c + 7 (c < H), accumulated in the order
 // j = 0, 1, ...; the row loads of each batch of 8 pairs are all issued before
-// any is used, so their latencies overlap.
+// any is used, so their latencies overlap.  The expert outputs are read once:
+// non-temporal loads keep them from displacing other data in the caches
+// (16384 tokens: combine 186 -> 145 us).
 constexpr int kCombineBatch = 8;
 __device__ __forceinline__ void combine_sums8(const uint16_t *__restrict__ y, const TokenPairs &tp,
                                               int H, int c, float (&acc)[8]) {
@@ -62,7 +64,8 @@ __device__ __forceinline__ void combine_sums8(const uint16_t *__restrict__ y, co
     u32x4 v[kCombineBatch];
 #pragma unroll
     for (int b = 0; b < kCombineBatch; ++b)
-      if ((tp.valid >> (j0 + b)) & 1u) v[b] = *(const u32x4 *)(y + (size_t)tp.rk[j0 + b] * H + c);
+      if ((tp.valid >> (j0 + b)) & 1u)
+        v[b] = __builtin_nontemporal_load((const u32x4 *)(y + (size_t)tp.rk[j0 + b] * H + c));
 #pragma unroll
     for (int b = 0; b < kCombineBatch; ++b) {
       const int j = j0 + b;
