@@ -418,6 +418,7 @@ def test_route_bucket_split_logits(T, H, E, k):
 @pytest.mark.parametrize("T,H,E,k,I", [(0, 2816, 128, 8, 704), (1, 2816, 128, 8, 704),
                                        (5, 2816, 128, 8, 704), (64, 2816, 128, 8, 704),
                                        (65, 2816, 128, 8, 704), (300, 2816, 128, 8, 704),
+                                       (1024, 2816, 128, 8, 704), (1100, 4160, 32, 4, 64),
                                        (9, 192, 16, 3, 64), (64, 4096, 256, 16, 128),
                                        (30, 4160, 32, 4, 64)])
 @pytest.mark.parametrize("norm", [False, True])
@@ -425,7 +426,9 @@ def test_route_bucket_prep_equals_separate_calls(T, H, E, k, I, norm):
     """moe_route_bucket_prep: every output byte, the whole expert workspace
     included (filled with garbage first, so that the clearing of the row
     maxima is checked), equal to moe_route_bucket followed by
-    nvfp4_expert_prep (or nvfp4_expert_prep_rmsnorm)."""
+    nvfp4_expert_prep (or nvfp4_expert_prep_rmsnorm); T = 1024 and 1100 have
+    more than 4096 pairs (the chunked bucketing), and H = 4160 rows are
+    longer than a wave of the prep keeps in registers."""
     router = S.router_params(3, h=H, e=E)
     x = S.activations(94, T, h=H)
     x[:min(T, 2)] = S.f32_to_bf16_bits(S.bf16_bits_to_f32(x[:min(T, 2)]) * np.float32(3e4))
