@@ -1051,8 +1051,10 @@ __device__ __forceinline__ void gemv_run(const GemvArgs &p, const Nvfp4 &w0, con
       for (int i = 0; i < NP; ++i) {
         const float G = acc[i][jj] * (gg * f), U = acc[NP + i][jj] * (gu * f);
         const uint16_t ab = f32_to_bf16_rne(gelu_tanh(G) * U);
-        if (ok) p.out[(size_t)(row0 + mr) * N + (nt0 + i) * 16 + r] = ab;
-        rmax = max(rmax, ok ? bf16_abs_bits(ab) : 0u);
+        // columns past N: a last column group of 3 row-tile pairs when N % 48 != 0
+        const bool cok = ok && (nt0 + i) * 16 < N;
+        if (cok) p.out[(size_t)(row0 + mr) * N + (nt0 + i) * 16 + r] = ab;
+        rmax = max(rmax, cok ? bf16_abs_bits(ab) : 0u);
       }
       rmax = row16_max_u32(rmax);
       if (r == 0 && ok) atomicMax(&p.a_max[row0 + mr], rmax);
@@ -1176,6 +1178,12 @@ constexpr int kDecodeMaxP = MOE_DECODE_MAX_PAIRS;
 static_assert(kDecodeMaxP <= kWave, "the bucketing of the decode layer is one wave's");
 static_assert(kDecodeMaxT <= 2 * (kThreads / kWave), "two tokens per selecting wave");
 constexpr int kDecodePD = kGemvPD;  // gate/up K units in flight per wave
+// gate/up row-tile pairs per wave: 2, or 3 once the grid of 2 would hold
+// kDecodeNP3From workgroups or more (most of the 1024 that four per CU keep
+// resident at once; 3 pairs per wave keep every tile of a T = 8 batch in one
+// round).  Measured, 30-layer sweep at T = 8 1676 -> 1564-1586 us, T = 4 step
+// 37.5 -> 36.8 us; at T = 1 (176 workgroups) 3 pairs ran the sweep 673 -> 693 us.
+constexpr int kDecodeNP3From = 512;
 #ifndef MOE_DECODE_DOWN_PD
 #define MOE_DECODE_DOWN_PD 2
 #endif
@@ -1194,10 +1202,10 @@ struct DecodeRoute {
   int32_t *offsets, *sorted, *rank, *err;  // [E+1], [P], [P], [1]
 };
 
-template <int FMT>
+template <int FMT, int NP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_gate_up(GemvArgs p, DecodeRoute r, Nvfp4 w0, Nvfp4 w1) {
-  constexpr int NP = kGateNP, NW = 2 * NP, KS = 4;
+  constexpr int NW = 2 * NP, KS = 4;
   __shared__ __attribute__((aligned(16))) float s_red[KS * 64 * NW * 4];
   __shared__ int32_t s_idx[kDecodeMaxP], s_sorted[kDecodeMaxP], s_rank[kDecodeMaxP];
   __shared__ float s_w[kDecodeMaxP], s_wr[kDecodeMaxP];
@@ -1581,17 +1589,18 @@ __attribute__((visibility("hidden"))) int launch_decode_gate_up(
                    (uint32_t)((size_t)T * H * 2), w.a};
   const DecodeRoute dr{logits, pes, T, E, topk_idx, topk_w, topk_w_raw, offsets, sorted, rank, err};
   const Nvfp4 g{gate->packed, gate->scales, gate->global}, u{up->packed, up->scales, up->global};
-  const dim3 grid((I + 16 * kGateNP - 1) / (16 * kGateNP), P < E ? P : E);
+  const int tiles = P < E ? P : E;  // at most one 8-row tile per pair
+  const bool np3 = (long long)((I + 31) / 32) * tiles >= kDecodeNP3From;
+  const dim3 grid(np3 ? (I + 47) / 48 : (I + 31) / 32, tiles);
+#define MOE_DECODE_GU(F)                                                                        \
+  if (np3) MOE_LAUNCH((k_decode_gate_up<F, 3>), grid, dim3(kThreads), 0, s, a, dr, g, u);        \
+  else MOE_LAUNCH((k_decode_gate_up<F, 2>), grid, dim3(kThreads), 0, s, a, dr, g, u)
   switch (gate->format) {
-    case MOE_FORMAT_Q4_0:
-      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_Q4_0>, grid, dim3(kThreads), 0, s, a, dr, g, u);
-      break;
-    case MOE_FORMAT_AFF4:
-      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_AFF4>, grid, dim3(kThreads), 0, s, a, dr, g, u);
-      break;
-    default:
-      MOE_LAUNCH(k_decode_gate_up<MOE_FORMAT_NVFP4>, grid, dim3(kThreads), 0, s, a, dr, g, u);
+    case MOE_FORMAT_Q4_0: MOE_DECODE_GU(MOE_FORMAT_Q4_0); break;
+    case MOE_FORMAT_AFF4: MOE_DECODE_GU(MOE_FORMAT_AFF4); break;
+    default: MOE_DECODE_GU(MOE_FORMAT_NVFP4);
   }
+#undef MOE_DECODE_GU
   return MOE_OK;
 }
 
