@@ -1226,26 +1226,48 @@ void k_decode_gate_up(GemvArgs p, DecodeRoute r, Nvfp4 w0, Nvfp4 w1) {
                                                    s_w, s_wr);
   }
   __syncthreads();
-  bucket_one_wave(s_idx, P, r.E, s_off, s_sorted, s_rank, &s_err, s_cnt);
-  __syncthreads();
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int i = tid; i < P; i += kThreads) {
-      r.topk_idx[i] = s_idx[i];
-      r.topk_w[i] = s_w[i];
-      if (r.topk_w_raw) r.topk_w_raw[i] = s_wr[i];
-      r.sorted[i] = s_sorted[i];
-      r.rank[i] = s_rank[i];
+  // One token (uniform): its K selected experts are distinct, so tile y is the
+  // y-th smallest selected id, one row at sorted position y -- every
+  // workgroup but (0, 0), which writes the routing outputs, skips the
+  // bucketing and the tile search.
+  const bool one = r.T == 1 && (blockIdx.x | blockIdx.y) != 0;
+  if (!one) {
+    bucket_one_wave(s_idx, P, r.E, s_off, s_sorted, s_rank, &s_err, s_cnt);
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      for (int i = tid; i < P; i += kThreads) {
+        r.topk_idx[i] = s_idx[i];
+        r.topk_w[i] = s_w[i];
+        if (r.topk_w_raw) r.topk_w_raw[i] = s_wr[i];
+        r.sorted[i] = s_sorted[i];
+        r.rank[i] = s_rank[i];
+      }
+      for (int i = tid; i <= r.E; i += kThreads) r.offsets[i] = s_off[i];
+      if (tid == 0) *r.err = s_err;
     }
-    for (int i = tid; i <= r.E; i += kThreads) r.offsets[i] = s_off[i];
-    if (tid == 0) *r.err = s_err;
   }
   const int nt0 = blockIdx.x * NP;
   if (nt0 * 16 >= p.N) return;  // uniform: past the last column
-  int off[kTilePer + 1];
-#pragma unroll
-  for (int i = 0; i <= kTilePer; ++i) off[i] = s_off[min(kTilePer * lane + i, r.E)];
   int e, row0, mrows;
-  if (!find_tile_from(off, r.E, 8, blockIdx.y, e, row0, mrows)) return;  // uniform
+  if (one) {
+    const int id = lane < K ? s_idx[lane] : 0;
+    int below = 0;  // selected ids smaller than this lane's
+    for (int jj = 0; jj < K; ++jj) below += s_idx[jj] < id;
+    const unsigned long long hit = __ballot(lane < K && below == (int)blockIdx.y);
+    if (!hit) return;  // uniform: no tile y
+    const int src = (int)__builtin_ctzll(hit);
+    e = __builtin_amdgcn_readlane(id, src);
+    row0 = (int)blockIdx.y;
+    mrows = 1;
+    // the pair at sorted position row0 (pair src of token 0), written by
+    // every wave before it reads it in the GEMV
+    if (lane == 0) s_sorted[row0] = src;
+  } else {
+    int off[kTilePer + 1];
+#pragma unroll
+    for (int i = 0; i <= kTilePer; ++i) off[i] = s_off[min(kTilePer * lane + i, r.E)];
+    if (!find_tile_from(off, r.E, 8, blockIdx.y, e, row0, mrows)) return;  // uniform
+  }
   GemvArgs q = p;
   q.sorted_pairs = s_sorted;
   if (mrows <= 4) gemv_run<4, NP, true, KS, FMT, kDecodePD>(q, w0, w1, e, row0, mrows, nt0, s_red);
