@@ -140,6 +140,20 @@ def test_layer_decode_int4_formats(fmt_gu, fmt_d):
     assert np.max(row_rel(got, ref)) <= REL_FROB_TOL
 
 
+@pytest.mark.parametrize("fmt", ["q4_0", "aff4"])
+def test_layer_decode_int4_model_shape(fmt):
+    """The int4 formats through moe_layer_decode at the model's shape, where
+    from 4 tokens on the gate/up kernel takes three row-tile pairs per wave
+    (15 column groups of 48, the last one partly past I = 704): every routing
+    byte and the output equal to the four calls (T = 8), within a bf16 step
+    (T = 4: down and combine in one kernel)."""
+    key = f"int4_{fmt}"
+    if key not in _L:
+        _L[key] = W.build_int4_layer(fmt, 0)
+    for T in (4, 8):
+        _both(_L[key], S.activations(50 + T, T))
+
+
 @pytest.mark.parametrize("T", [2, 8])
 def test_layer_decode_deterministic_and_graph_replay(layer0, T):
     x = W.to_device_bf16(S.activations(40, T))
